@@ -1,0 +1,182 @@
+"""Python handle on the CPU oracle (``oracle.c``), for tests and measurement only.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module. It marshals arrays into the C oracle
+and back; it computes nothing of the method itself.
+
+Thetas are dicts as produced by ``linear_02_amd.inputs.theta``: W0, U, V bf16
+tensors, s an fp32 tensor or None, plus d_in, d_out, r. Results are float64
+numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "oracle.c")
+LIBRARY = os.path.join(HERE, "liboracle.so")
+# Plain IEEE double arithmetic: no contraction into fused multiply-adds, no fast-math.
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-D_GNU_SOURCE",
+          "-fPIC", "-shared"]
+
+
+def build(source: str = SOURCE, out: str = LIBRARY) -> str:
+    """Compile ``source`` into the shared library ``out`` with gcc."""
+    cmd = ["gcc", *CFLAGS, "-o", out, source, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+class _Theta(ctypes.Structure):
+    _fields_ = [("W0", ctypes.c_void_p), ("s", ctypes.c_void_p), ("U", ctypes.c_void_p),
+                ("V", ctypes.c_void_p), ("d_in", ctypes.c_int64), ("d_out", ctypes.c_int64),
+                ("r", ctypes.c_int64)]
+
+
+def _bits(t) -> np.ndarray:
+    """bf16 tensor (or uint16 array of bf16 patterns) -> contiguous uint16 array."""
+    if isinstance(t, np.ndarray):
+        assert t.dtype == np.uint16
+        return np.ascontiguousarray(t)
+    import torch
+    assert t.dtype == torch.bfloat16, t.dtype
+    return np.ascontiguousarray(t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def _f32(t) -> np.ndarray | None:
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return np.ascontiguousarray(t, dtype=np.float32)
+    return np.ascontiguousarray(t.detach().cpu().float().numpy())
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes wrapper around one compiled oracle library."""
+
+    def __init__(self, path: str = LIBRARY):
+        if path == LIBRARY and not os.path.exists(path):
+            build()
+        self.path = path
+        lib = ctypes.CDLL(path)
+        P = ctypes.POINTER
+        lib.orc_linear.argtypes = [P(_Theta), ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+        lib.orc_linear.restype = ctypes.c_int
+        lib.orc_qkv.argtypes = [P(_Theta)] * 3 + [ctypes.c_int64] + [ctypes.c_void_p] * 3
+        lib.orc_qkv.restype = ctypes.c_int
+        lib.orc_mlp.argtypes = [P(_Theta)] * 3 + [ctypes.c_int64] + [ctypes.c_void_p] * 4
+        lib.orc_mlp.restype = ctypes.c_int
+        lib.orc_weff.argtypes = [P(_Theta), ctypes.c_void_p, ctypes.c_void_p]
+        lib.orc_weff.restype = ctypes.c_int
+        lib.orc_rel_frob.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.orc_rel_frob.restype = ctypes.c_double
+        lib.orc_gelu_tanh.argtypes = [ctypes.c_double]
+        lib.orc_gelu_tanh.restype = ctypes.c_double
+        lib.orc_bf16_rne.argtypes = [ctypes.c_double]
+        lib.orc_bf16_rne.restype = ctypes.c_uint16
+        lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
+        lib.orc_bf16_value.restype = ctypes.c_double
+        self.lib = lib
+
+    # -- marshalling ----------------------------------------------------------------
+    @staticmethod
+    def _theta(th: dict):
+        keep = dict(W0=_bits(th["W0"]), s=_f32(th.get("s")))
+        r = int(th["r"])
+        keep["U"] = _bits(th["U"]) if r > 0 else None
+        keep["V"] = _bits(th["V"]) if r > 0 else None
+        d_in, d_out = int(th["d_in"]), int(th["d_out"])
+        assert keep["W0"].size == d_out * d_in
+        if keep["s"] is not None:
+            assert keep["s"].size == d_out
+        if r > 0:
+            assert keep["U"].size == d_out * r and keep["V"].size == d_in * r
+        st = _Theta(_ptr(keep["W0"]), _ptr(keep["s"]), _ptr(keep["U"]), _ptr(keep["V"]),
+                    d_in, d_out, r)
+        return st, keep
+
+    # -- operations -----------------------------------------------------------------
+    def linear(self, th: dict, x) -> tuple[np.ndarray, np.ndarray]:
+        """(y, bound), both float64 [T][d_out]."""
+        st, keep = self._theta(th)
+        xb = _bits(x).reshape(-1, int(th["d_in"]))
+        T = xb.shape[0]
+        y = np.empty((T, int(th["d_out"])), np.float64)
+        b = np.empty_like(y)
+        rc = self.lib.orc_linear(ctypes.byref(st), T, _ptr(xb), _ptr(y), _ptr(b))
+        assert rc == 0
+        return y, b
+
+    def qkv(self, q: dict, k: dict, v: dict, x) -> tuple[np.ndarray, np.ndarray]:
+        """(y, bound) float64 [T][dq+dk+dv], columns Q | K | V."""
+        sq, kq = self._theta(q)
+        sk, kk = self._theta(k)
+        sv, kv = self._theta(v)
+        xb = _bits(x).reshape(-1, int(q["d_in"]))
+        T = xb.shape[0]
+        width = int(q["d_out"]) + int(k["d_out"]) + int(v["d_out"])
+        y = np.empty((T, width), np.float64)
+        b = np.empty_like(y)
+        rc = self.lib.orc_qkv(ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(sv), T,
+                              _ptr(xb), _ptr(y), _ptr(b))
+        assert rc == 0
+        return y, b
+
+    def mlp(self, gate: dict, up: dict, down: dict, x):
+        """(y, bound, h_bits): y, bound float64 [T][d_model]; h_bits uint16 [T][d_ff]."""
+        sg, kg = self._theta(gate)
+        su, ku = self._theta(up)
+        sd, kd = self._theta(down)
+        xb = _bits(x).reshape(-1, int(gate["d_in"]))
+        T = xb.shape[0]
+        y = np.empty((T, int(down["d_out"])), np.float64)
+        b = np.empty_like(y)
+        h = np.empty((T, int(gate["d_out"])), np.uint16)
+        rc = self.lib.orc_mlp(ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), T,
+                              _ptr(xb), _ptr(y), _ptr(b), _ptr(h))
+        assert rc == 0
+        return y, b, h
+
+    def weff(self, th: dict) -> tuple[np.ndarray, np.ndarray]:
+        """(W_eff, bound) float64 [d_out][d_in]."""
+        st, keep = self._theta(th)
+        w = np.empty((int(th["d_out"]), int(th["d_in"])), np.float64)
+        b = np.empty_like(w)
+        rc = self.lib.orc_weff(ctypes.byref(st), _ptr(w), _ptr(b))
+        assert rc == 0
+        return w, b
+
+    def rel_frob(self, W, R) -> float:
+        W = np.ascontiguousarray(W, dtype=np.float64)
+        R = np.ascontiguousarray(R, dtype=np.float64)
+        assert W.size == R.size
+        return float(self.lib.orc_rel_frob(W.size, _ptr(W), _ptr(R)))
+
+    def gelu(self, z: float) -> float:
+        return float(self.lib.orc_gelu_tanh(float(z)))
+
+    def bf16_rne(self, v: float) -> int:
+        return int(self.lib.orc_bf16_rne(float(v)))
+
+    def bf16_value(self, bits: int) -> float:
+        return float(self.lib.orc_bf16_value(int(bits)))
+
+
+_DEFAULT: Oracle | None = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``oracle.c`` next to this file (built on first use)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle()
+    return _DEFAULT

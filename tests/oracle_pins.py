@@ -1,0 +1,429 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each ``pin_*`` takes an oracle handle and raises AssertionError when the oracle
+disagrees with something the pages or the mathematics fix:
+
+* a worked example computed by hand (tests/golden/linear_worked_example.txt);
+* the bfloat16 round-to-nearest-even table worked out from the format
+  definition (tests/golden/bf16_rne_cases.txt) and torch's float32 -> bf16 cast;
+* the passthrough point (U = V = 0, s = 1 gives y = W0 x) against numpy's
+  float64 matmul and exact integer matmul ("Serve and generate with weightless",
+  fast path on NVIDIA: at the passthrough point every reconstructed weight is
+  the original);
+* exact rational brute force on tiny integer problems, evaluated through the
+  materialized weight W_eff = diag(s) W0 + U V^T (the pages state that the
+  reconstruction paths and the precompute-outside path are math-identical);
+* closed forms and invariants: unit-vector inputs, rank-1 factors, linearity,
+  the role of s, rank splitting, relative Frobenius error closed forms, GELU
+  identities and its sigmoid form evaluated in 50-digit decimal arithmetic.
+
+The same pins run against deliberately broken copies of the oracle
+(test_oracle_mutants.py) to show that each plausible mistake fails one of them.
+"""
+from __future__ import annotations
+
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from linear_02_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# -- helpers ------------------------------------------------------------------------------
+
+def _bf16(a) -> torch.Tensor:
+    return torch.as_tensor(np.asarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+def _theta(W0, s, U, V) -> dict:
+    W0 = _bf16(W0)
+    d_out, d_in = W0.shape
+    U = _bf16(U).reshape(d_out, -1)
+    V = _bf16(V).reshape(d_in, -1)
+    r = U.shape[1]
+    return dict(W0=W0, s=None if s is None else torch.as_tensor(np.asarray(s, np.float32)),
+                U=U, V=V, d_in=d_in, d_out=d_out, r=r)
+
+
+def _f64(t) -> np.ndarray:
+    return t.double().numpy() if isinstance(t, torch.Tensor) else np.asarray(t, np.float64)
+
+
+def _s_vec(th) -> np.ndarray:
+    return np.ones(th["d_out"]) if th["s"] is None else _f64(th["s"])
+
+
+def _frac(a) -> list:
+    """float64 array -> nested lists of exact Fractions."""
+    a = np.asarray(a, np.float64)
+    return [[Fraction(float(v)) for v in row] for row in a.reshape(a.shape[0], -1)]
+
+
+def _exact_weff(th) -> list:
+    """W_eff = diag(s) W0 + U V^T in exact rational arithmetic."""
+    W0, U, V = _frac(_f64(th["W0"])), _frac(_f64(th["U"])), _frac(_f64(th["V"]))
+    s = [Fraction(float(v)) for v in _s_vec(th)]
+    d_out, d_in, r = th["d_out"], th["d_in"], th["r"]
+    return [[s[o] * W0[o][i] + sum((U[o][k] * V[i][k] for k in range(r)), Fraction(0))
+             for i in range(d_in)] for o in range(d_out)]
+
+
+def _exact_apply(W, x) -> list:
+    """y[t][o] = sum_i W[o][i] x[t][i] in exact rationals."""
+    X = _frac(x)
+    return [[sum((W[o][i] * X[t][i] for i in range(len(X[t]))), Fraction(0))
+             for o in range(len(W))] for t in range(len(X))]
+
+
+def _read_blocks(path) -> dict:
+    out = {}
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        key, rest = line.split(None, 1)
+        rows = [[float(v) for v in part.split()] for part in rest.split("|")]
+        out[key] = rows
+    return out
+
+
+def _rand_int_theta(gen, d_in, d_out, r, s_values=(0.5, 1.0, 2.0, -1.0)):
+    W0 = inputs.int_tensor(gen, (d_out, d_in), -2, 2)
+    U = inputs.int_tensor(gen, (d_out, r), -1, 1)
+    V = inputs.int_tensor(gen, (d_in, r), -1, 1)
+    s = inputs.choice_tensor(gen, (d_out,), s_values)
+    return dict(W0=W0, s=s, U=U, V=V, d_in=d_in, d_out=d_out, r=r)
+
+
+# -- pins ---------------------------------------------------------------------------------
+
+def pin_worked_example(orc):
+    g = _read_blocks(os.path.join(GOLDEN, "linear_worked_example.txt"))
+    th = _theta(g["W0"], g["s"][0], g["U"], g["V"])
+    x = _bf16(g["x"])
+    y, b = orc.linear(th, x)
+    assert np.array_equal(y, np.array(g["y"])), (y, g["y"])
+    assert np.array_equal(b, np.array(g["bound"])), (b, g["bound"])
+    w, _ = orc.weff(th)
+    assert np.array_equal(w, np.array(g["W_eff"])), w
+
+
+def pin_bf16_rne_table(orc):
+    for line in open(os.path.join(GOLDEN, "bf16_rne_cases.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        val, bits = line.split()[:2]
+        v = float.fromhex(val)
+        got = orc.bf16_rne(v)
+        assert got == int(bits, 16), (val, hex(got), bits)
+        if got & 0x7F80 != 0x7F80:   # finite: the pattern decodes back to the rounded value
+            assert abs(orc.bf16_value(got) - v) <= abs(v) * 2.0 ** -8 + 2.0 ** -134
+
+
+def pin_bf16_rne_matches_torch(orc):
+    """float32 inputs (normals, subnormals, near-ties) against torch's RNE cast."""
+    gen = torch.Generator().manual_seed(11)
+    a = torch.randn(4000, generator=gen) * torch.exp2(torch.randint(-140, 120, (4000,), generator=gen).float())
+    # exact ties: bf16 values plus half a quantum
+    base = torch.randn(1000, generator=gen).to(torch.bfloat16).float()
+    bits = base.view(torch.int32)
+    ties = (bits + 0x8000).view(torch.float32)
+    vals = torch.cat([a, ties, torch.tensor([0.0, -0.0, 1e-45, -1e-45, 3.0e38, -3.0e38])])
+    vals = vals[torch.isfinite(vals)]
+    want = vals.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for v, w in zip(vals.tolist(), want.tolist()):
+        assert orc.bf16_rne(v) == w, (v.hex(), hex(orc.bf16_rne(v)), hex(w))
+
+
+def pin_passthrough_integer_exact(orc):
+    """U = V = 0, s = 1: y equals the exact integer product W0 x."""
+    gen = torch.Generator().manual_seed(1)
+    d_in, d_out, r, T = 40, 23, 3, 3
+    W0 = inputs.int_tensor(gen, (d_out, d_in), -8, 8)
+    x = inputs.int_tensor(gen, (T, d_in), -4, 4)
+    for s in (None, torch.ones(d_out)):
+        th = dict(W0=W0, s=s, U=torch.zeros(d_out, r, dtype=torch.bfloat16),
+                  V=torch.zeros(d_in, r, dtype=torch.bfloat16), d_in=d_in, d_out=d_out, r=r)
+        y, _ = orc.linear(th, x)
+        want = x.to(torch.int64).numpy() @ W0.to(torch.int64).numpy().T
+        assert np.array_equal(y, want.astype(np.float64))
+        w, _ = orc.weff(th)
+        assert np.array_equal(w, W0.double().numpy())
+        assert orc.rel_frob(W0.double().numpy(), w) == 0.0
+
+
+def pin_passthrough_random_matmul(orc):
+    """r = 0, s = 1 on random bf16 data: y equals numpy's float64 x @ W0^T."""
+    gen = torch.Generator().manual_seed(2)
+    d_in, d_out, T = 96, 70, 4
+    th = inputs.theta(gen, d_in, d_out, 0)
+    th["s"] = None
+    x = inputs.activations(gen, T, d_in)
+    y, b = orc.linear(th, x)
+    want = _f64(x) @ _f64(th["W0"]).T
+    assert np.max(np.abs(y - want) / b) < 1e-13
+
+
+def pin_bruteforce_exact(orc):
+    """Tiny integer problems: every output equals exact rational W_eff x."""
+    for seed, (d_in, d_out, r, T) in enumerate([(5, 3, 1, 1), (8, 11, 2, 2), (16, 24, 4, 3),
+                                                (7, 13, 3, 2), (12, 5, 4, 3)]):
+        gen = torch.Generator().manual_seed(100 + seed)
+        th = _rand_int_theta(gen, d_in, d_out, r)
+        x = inputs.int_tensor(gen, (T, d_in), -2, 2)
+        y, b = orc.linear(th, x)
+        want = _exact_apply(_exact_weff(th), _f64(x))
+        for t in range(T):
+            for o in range(d_out):
+                assert Fraction(float(y[t, o])) == want[t][o], (seed, t, o, y[t, o], want[t][o])
+                assert abs(y[t, o]) <= b[t, o]
+        w, _ = orc.weff(th)
+        ew = _exact_weff(th)
+        assert all(Fraction(float(w[o, i])) == ew[o][i] for o in range(d_out) for i in range(d_in))
+
+
+def pin_qkv_bruteforce(orc):
+    """Q/K/V fusion on tiny integer problems: columns Q | K | V of exact products."""
+    gen = torch.Generator().manual_seed(7)
+    d_in, T = 9, 2
+    ths = [_rand_int_theta(gen, d_in, n, r) for n, r in ((6, 2), (3, 1), (4, 3))]
+    x = inputs.int_tensor(gen, (T, d_in), -2, 2)
+    y, b = orc.qkv(*ths, x)
+    cols = []
+    for th in ths:
+        e = _exact_apply(_exact_weff(th), _f64(x))
+        cols.append(np.array([[float(v) for v in row] for row in e]))
+    assert np.array_equal(y, np.concatenate(cols, axis=1))
+    for c, th in enumerate(ths):
+        yc, bc = orc.linear(th, x)
+        lo = sum(t["d_out"] for t in ths[:c])
+        assert np.array_equal(b[:, lo:lo + th["d_out"]], bc)
+
+
+def pin_unit_vectors(orc):
+    """x = e_i picks column i of the effective weight: s[o] W0[o,i] + sum_k U[o,k] V[i,k]."""
+    gen = torch.Generator().manual_seed(3)
+    d_in, d_out, r = 13, 9, 5
+    th = inputs.theta(gen, d_in, d_out, r)
+    x = torch.eye(d_in, dtype=torch.bfloat16)
+    y, b = orc.linear(th, x)          # y[i, o]
+    W0, U, V, s = _f64(th["W0"]), _f64(th["U"]), _f64(th["V"]), _s_vec(th)
+    for i in range(d_in):
+        for o in range(d_out):
+            col = s[o] * W0[o, i] + sum(U[o, k] * V[i, k] for k in range(r))
+            assert abs(y[i, o] - col) <= 1e-15 * b[i, o], (i, o)
+
+
+def pin_rank1_closed_form(orc):
+    """W0 = 0, r = 1: y = u (v . x), with numpy's dot for v . x."""
+    gen = torch.Generator().manual_seed(4)
+    d_in, d_out, T = 33, 17, 3
+    th = inputs.theta(gen, d_in, d_out, 1)
+    th["W0"] = torch.zeros(d_out, d_in, dtype=torch.bfloat16)
+    x = inputs.activations(gen, T, d_in)
+    y, b = orc.linear(th, x)
+    u, v = _f64(th["U"])[:, 0], _f64(th["V"])[:, 0]
+    want = np.outer(_f64(x) @ v, u)
+    assert np.max(np.abs(y - want)) <= 1e-14 * np.max(b)
+
+
+def pin_linearity(orc):
+    """y(x1 + x2) = y(x1) + y(x2); y(2x) = 2 y(x) bit for bit."""
+    gen = torch.Generator().manual_seed(5)
+    d_in, d_out, r, T = 48, 31, 4, 3
+    th = inputs.theta(gen, d_in, d_out, r)
+    x1 = inputs.int_tensor(gen, (T, d_in), -3, 3)
+    x2 = inputs.int_tensor(gen, (T, d_in), -3, 3)
+    y1, b1 = orc.linear(th, x1)
+    y2, b2 = orc.linear(th, x2)
+    y12, _ = orc.linear(th, (x1.float() + x2.float()).to(torch.bfloat16))
+    assert np.max(np.abs(y12 - (y1 + y2)) / (b1 + b2)) < 1e-14
+    xr = inputs.activations(gen, T, d_in)
+    yr, _ = orc.linear(th, xr)
+    y2r, _ = orc.linear(th, (xr.float() * 2).to(torch.bfloat16))
+    assert np.array_equal(y2r, 2 * yr)
+
+
+def pin_s_role(orc):
+    """s scales only the W0 term: with s = 0 the output is the low-rank term
+    U (V^T x) alone (numpy matmuls), and y(s) - y(0) = s * (W0 x)."""
+    gen = torch.Generator().manual_seed(6)
+    d_in, d_out, r, T = 40, 27, 6, 2
+    th = inputs.theta(gen, d_in, d_out, r)
+    x = inputs.activations(gen, T, d_in)
+    y, b = orc.linear(th, x)
+    th0 = dict(th, s=torch.zeros(d_out))
+    y0, _ = orc.linear(th0, x)
+    X, U, V, W0, s = _f64(x), _f64(th["U"]), _f64(th["V"]), _f64(th["W0"]), _s_vec(th)
+    low = (X @ V) @ U.T
+    assert np.max(np.abs(y0 - low)) <= 1e-14 * np.max(b)
+    assert np.max(np.abs((y - y0) - s[None, :] * (X @ W0.T))) <= 1e-13 * np.max(b)
+    # a negative scale flips only the W0 term
+    thn = dict(th, s=-th["s"])
+    yn, bn = orc.linear(thn, x)
+    assert np.max(np.abs((yn - y0) + (y - y0))) <= 1e-13 * np.max(b)
+    assert np.array_equal(bn, b)
+
+
+def pin_rank_split(orc):
+    """Splitting the rank r = r1 + r2 adds the two low-rank deltas."""
+    gen = torch.Generator().manual_seed(8)
+    d_in, d_out, r, r1, T = 36, 20, 7, 3, 2
+    th = inputs.theta(gen, d_in, d_out, r)
+    x = inputs.activations(gen, T, d_in)
+    y, b = orc.linear(th, x)
+    tha = dict(th, U=th["U"][:, :r1].contiguous(), V=th["V"][:, :r1].contiguous(), r=r1)
+    thb = dict(th, U=th["U"][:, r1:].contiguous(), V=th["V"][:, r1:].contiguous(), r=r - r1)
+    th0 = dict(th, U=th["U"][:, :0].contiguous(), V=th["V"][:, :0].contiguous(), r=0)
+    ya, _ = orc.linear(tha, x)
+    yb, _ = orc.linear(thb, x)
+    y0, _ = orc.linear(th0, x)
+    assert np.max(np.abs(y - (ya + yb - y0)) / b) < 1e-13
+
+
+def pin_weff_forms(orc):
+    """The materialized weight equals numpy's diag(s) W0 + U V^T, and the
+    projection equals the dense product x W_eff^T (numpy matmul)."""
+    gen = torch.Generator().manual_seed(9)
+    d_in, d_out, r, T = 64, 40, 8, 5
+    th = inputs.theta(gen, d_in, d_out, r)
+    W0, U, V, s = _f64(th["W0"]), _f64(th["U"]), _f64(th["V"]), _s_vec(th)
+    w, bw = orc.weff(th)
+    want = np.diag(s) @ W0 + U @ V.T
+    assert np.max(np.abs(w - want) / np.maximum(bw, 1e-300)) < 1e-15
+    assert np.all(bw >= np.abs(w))
+    x = inputs.activations(gen, T, d_in)
+    y, b = orc.linear(th, x)
+    assert np.max(np.abs(y - _f64(x) @ w.T) / b) < 1e-13
+
+
+def pin_rel_frob_closed_forms(orc):
+    gen = np.random.default_rng(10)
+    W = gen.standard_normal((17, 23))
+    assert orc.rel_frob(W, W) == 0.0
+    for eps in (1e-3, -0.25, 2.0):
+        got = orc.rel_frob(W, (1 + eps) * W)
+        assert abs(got - abs(eps)) <= 1e-14 * max(1.0, abs(eps))
+    u, v = gen.standard_normal(17), gen.standard_normal(23)
+    got = orc.rel_frob(W, W + np.outer(u, v))
+    want = np.linalg.norm(u) * np.linalg.norm(v) / np.linalg.norm(W)
+    assert abs(got - want) <= 1e-13 * want
+    Z = np.zeros((3, 4))
+    assert orc.rel_frob(Z, Z) == 0.0
+    assert orc.rel_frob(Z, Z + 1) == float("inf")
+
+
+def _gelu_sigmoid_decimal(z: float) -> Decimal:
+    """tanh-GELU through its sigmoid form 0.5 (1 + tanh a) = 1 / (1 + e^(-2a)),
+    in 50-digit decimal arithmetic, with sqrt(2/pi) from a 60-digit pi."""
+    getcontext().prec = 60
+    pi = Decimal("3.14159265358979323846264338327950288419716939937510582097494")
+    zd = Decimal(z)
+    a = (Decimal(2) / pi).sqrt() * (zd + Decimal("0.044715") * zd ** 3)
+    return zd / (1 + (-2 * a).exp())
+
+
+def pin_gelu(orc):
+    assert orc.gelu(0.0) == 0.0
+    for z in (-7.5, -3.0, -1.0, -0.3, 0.1, 0.5, 1.0, 2.0, 4.25, 8.0):
+        want = float(_gelu_sigmoid_decimal(z))
+        assert abs(orc.gelu(z) - want) <= 4e-16 * max(1.0, abs(want)), (z, orc.gelu(z), want)
+        # odd part: gelu(z) - gelu(-z) = z
+        assert abs(orc.gelu(z) - orc.gelu(-z) - z) <= 4e-15 * abs(z)
+    for z in (10.0, 11.0, 64.0, 250.0):
+        assert orc.gelu(z) == z and orc.gelu(-z) == 0.0
+
+
+def pin_mlp_exact_integer(orc):
+    """Integer gate/up outputs with |g| >= 10, where tanh-GELU is exactly the
+    identity (g >= 10) or exactly 0 (g <= -10) in double precision, so h and y
+    are exact and can be brute-forced in rationals."""
+    gen = torch.Generator().manual_seed(12)
+    d, ff, T = 6, 10, 2
+    x = inputs.int_tensor(gen, (T, d), 1, 2)               # positive entries
+    rows = []
+    while len(rows) < ff:                                   # gate rows with |g| >= 10 for every token
+        w = inputs.int_tensor(gen, (d,), -3, 3).float()
+        g = x.float() @ w
+        if torch.all(g.abs() >= 10):
+            rows.append(w)
+    Wg = torch.stack(rows).to(torch.bfloat16)
+    Wu = inputs.int_tensor(gen, (ff, d), -1, 1)
+    Wd = inputs.int_tensor(gen, (d, ff), -1, 1)
+    zero = lambda n, r: torch.zeros(n, r, dtype=torch.bfloat16)
+    gate = dict(W0=Wg, s=None, U=zero(ff, 1), V=zero(d, 1), d_in=d, d_out=ff, r=1)
+    up = dict(W0=Wu, s=torch.ones(ff), U=zero(ff, 1), V=zero(d, 1), d_in=d, d_out=ff, r=1)
+    down = _rand_int_theta(gen, ff, d, 2, s_values=(1.0, 2.0))
+    down["W0"] = Wd
+    y, b, hb = orc.mlp(gate, up, down, x)
+    X = x.double().numpy()
+    g = X @ Wg.double().numpy().T
+    u = X @ Wu.double().numpy().T
+    h = np.where(g > 0, g, 0.0) * u
+    assert np.max(np.abs(h)) <= 256                         # exact in bf16
+    assert np.array_equal(np.array([[orc.bf16_value(v) for v in row] for row in hb]), h)
+    want = _exact_apply(_exact_weff(down), h)
+    for t in range(T):
+        for o in range(d):
+            assert Fraction(float(y[t, o])) == want[t][o]
+
+
+def pin_mlp_zero_gate(orc):
+    """A zero gate gives gelu(0) = 0, so h = 0 and y = 0 exactly."""
+    gen = torch.Generator().manual_seed(13)
+    d, ff, r, T = 16, 24, 3, 3
+    gate = inputs.theta(gen, d, ff, r)
+    gate["W0"] = torch.zeros(ff, d, dtype=torch.bfloat16)
+    gate["U"] = torch.zeros(ff, r, dtype=torch.bfloat16)
+    up, down = inputs.theta(gen, d, ff, r), inputs.theta(gen, ff, d, r)
+    x = inputs.activations(gen, T, d)
+    y, b, hb = orc.mlp(gate, up, down, x)
+    assert np.all(y == 0.0) and np.all(b == 0.0) and np.all((hb & 0x7FFF) == 0)
+
+
+def pin_mlp_h_is_rounded_gelu_product(orc):
+    """h is the bf16 value nearest gelu(g) * u, with gelu through the decimal
+    sigmoid form and g, u from numpy matmuls of the materialized weights."""
+    gen = torch.Generator().manual_seed(14)
+    d, ff, r, T = 24, 20, 4, 2
+    gate, up, down = (inputs.theta(gen, d, ff, r), inputs.theta(gen, d, ff, r),
+                      inputs.theta(gen, ff, d, r))
+    x = inputs.activations(gen, T, d)
+    y, b, hb = orc.mlp(gate, up, down, x)
+    X = _f64(x)
+
+    def dense(th):
+        return np.diag(_s_vec(th)) @ _f64(th["W0"]) + _f64(th["U"]) @ _f64(th["V"]).T
+    g, u = X @ dense(gate).T, X @ dense(up).T
+    for t in range(T):
+        for j in range(ff):
+            hv = float(_gelu_sigmoid_decimal(float(g[t, j]))) * u[t, j]
+            got = orc.bf16_value(int(hb[t, j]))
+            assert abs(got - hv) <= abs(hv) * 2.0 ** -8 * 1.0001 + 1e-30, (t, j, got, hv)
+    hd = np.array([[orc.bf16_value(int(v)) for v in row] for row in hb])
+    assert np.max(np.abs(y - hd @ dense(down).T) / b) < 1e-13
+
+
+PINS = [pin_worked_example, pin_bf16_rne_table, pin_bf16_rne_matches_torch,
+        pin_passthrough_integer_exact, pin_passthrough_random_matmul, pin_bruteforce_exact,
+        pin_qkv_bruteforce, pin_unit_vectors, pin_rank1_closed_form, pin_linearity, pin_s_role,
+        pin_rank_split, pin_weff_forms, pin_rel_frob_closed_forms, pin_gelu,
+        pin_mlp_exact_integer, pin_mlp_zero_gate, pin_mlp_h_is_rounded_gelu_product]
+
+
+def report(lib_path: str) -> None:
+    """Run every pin against the oracle library at ``lib_path``; print one line per pin."""
+    from oracle.oracle import Oracle
+    orc = Oracle(lib_path)
+    for pin in PINS:
+        try:
+            pin(orc)
+            print("PASS", pin.__name__, flush=True)
+        except AssertionError:
+            print("FAIL", pin.__name__, flush=True)
