@@ -1,0 +1,176 @@
+/*
+ * wl.h: C ABI of the fused reconstruct-and-project linear for AMD MI355X (gfx950).
+ *
+ * The operation ("In-kernel reconstruction" page, introduction: the
+ * reconstruction formula and its per-element expansion):
+ *
+ *     y[t,o] = s[o] * sum_i W0[o,i] * x[t,i]  +  sum_k U[o,k] * sum_i V[i,k] * x[t,i]
+ *
+ * i.e. y = s (.) (W0 x) + U (V^T x), computed without ever forming the dense
+ * weight diag(s) W0 + U V^T in memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.    Every tensor pointer is a DEVICE pointer on the current HIP device.
+ *            The caller allocates and owns every buffer, including the
+ *            workspace; the library never allocates or frees memory and keeps
+ *            no per-call state (its only global state is a per-device cache of
+ *            the compute-unit count and the regime switch below).
+ * Layout.    All tensors are row-major and contiguous:
+ *              W0 bf16 [d_out][d_in]   s fp32 [d_out]
+ *              U  bf16 [d_out][r]      V bf16 [d_in][r]
+ *              x  bf16 [T][d_in]       y bf16 [T][d_out]
+ *            (the index roles of the per-element expansion; the GEMM form on
+ *            the same page, "The GEMM path", multiplies x by W0 transposed, by
+ *            V, and the result by U transposed).
+ * Alignment. W0, U, V, x, y and W_eff must be 16-byte aligned, s 4-byte
+ *            aligned, the workspace 256-byte aligned. d_in must be a multiple
+ *            of 8 (rows are read in 16-byte pieces).
+ * Limits.    0 <= r <= 64; d_in, d_out >= 1; T >= 0 (T == 0 is a no-op that
+ *            returns WL_OK, and x, y may then be NULL). Sizes are int32 and
+ *            every tensor must hold fewer than 2^31 elements.
+ * Numerics.  Products accumulate in fp32; the epilogue s[o]*m + U[o,:].vtx is
+ *            fp32; y is rounded once to bf16, round-to-nearest-even ("In-kernel
+ *            reconstruction", "The custom-op path": every implementation
+ *            accumulates in float32 and casts back to the output dtype). The
+ *            matrix-core regime feeds vtx = V^T x to the matrix cores as a bf16
+ *            head plus a bf16 remainder. Results are deterministic from run to
+ *            run (no floating-point atomics) but not bit-exact against other
+ *            summation orders ("Serve and generate with weightless", "Set the
+ *            fast path on NVIDIA": parity is logit parity, not bit equality).
+ * Streams.   Every call only enqueues work on `hip_stream` (a hipStream_t;
+ *            NULL = the default stream) and returns; errors that happen on the
+ *            device surface at the caller's next synchronization.
+ * Workspace. Operations that take `ws` need at least wl_workspace_bytes(...)
+ *            bytes. The workspace must be zero-filled before its first use;
+ *            every call leaves it in a state fit for the next call (its counter
+ *            region is zero again when the call's stream work completes).
+ *            Calls that can run at the same time (different streams) must not
+ *            share a workspace.
+ * Errors.    Every argument is checked on the host before anything is
+ *            enqueued; a fused operation checks all of its thetas first, so an
+ *            invalid argument never leaves a partial launch.
+ *              WL_ERR_INVALID_ARG  null or misaligned pointer, bad size or
+ *                                  shape mismatch, output overlapping an input
+ *                                  or the workspace
+ *              WL_ERR_UNSUPPORTED  r > 64
+ *              WL_ERR_WORKSPACE    ws_bytes below the required size
+ *              WL_ERR_HIP          a kernel launch failed
+ *            No call aborts, throws or prints (set the environment variable
+ *            WL_LOG to log the regime chosen and every failure to stderr).
+ *            wl_last_error() describes the last failure on the calling thread.
+ * Devices.   One device per call; nothing here shards across GPUs ("Serve and
+ *            generate with weightless", "Supported encodings and devices": the
+ *            pages' implementation runs on a single device as well).
+ */
+#ifndef WL_H
+#define WL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WL_ABI_VERSION 1
+
+typedef enum {
+    WL_OK = 0,
+    WL_ERR_INVALID_ARG = 1,
+    WL_ERR_UNSUPPORTED = 2,
+    WL_ERR_HIP = 3,
+    WL_ERR_WORKSPACE = 4
+} wl_status;
+
+/* One projection's theta bundle ("Serve and generate with weightless",
+ * introduction: a shared block W0 per band of layers, a per-row scale s and a
+ * low-rank delta U, V of rank r). Several thetas may point at the same W0
+ * (band sharing). The library only reads through these pointers. */
+typedef struct {
+    const void  *W0;   /* bf16 [d_out][d_in]                                   */
+    const float *s;    /* fp32 [d_out]; NULL means every s[o] is 1              */
+    const void  *U;    /* bf16 [d_out][r]; ignored (may be NULL) when r == 0    */
+    const void  *V;    /* bf16 [d_in][r];  ignored (may be NULL) when r == 0    */
+    int32_t d_in, d_out, r;
+} wl_theta;
+
+/* Operation codes for wl_workspace_bytes. */
+enum { WL_OP_LINEAR = 0, WL_OP_QKV = 1, WL_OP_MLP = 2 };
+
+/* Bytes of workspace `op` needs for these thetas at T tokens:
+ *   WL_OP_LINEAR: th[0]                      (n_th == 1)
+ *   WL_OP_QKV:    th[0..2] = Q, K, V         (n_th == 3)
+ *   WL_OP_MLP:    th[0..2] = gate, up, down  (n_th == 3)
+ * Returns 0 for invalid arguments (the matching call then fails with the
+ * specific status). The value is a multiple of 256 and grows with T. */
+size_t wl_workspace_bytes(int32_t op, const wl_theta *const *th, int32_t n_th, int32_t T);
+
+/* The reconstruct-and-project linear ("In-kernel reconstruction",
+ * introduction: reconstruction formula and per-element expansion).
+ *   th    one theta bundle
+ *   x     bf16 [T][th->d_in]
+ *   y     bf16 [T][th->d_out] (written; must not overlap any input)
+ *   T     tokens (rows of x)
+ *   ws    workspace, ws_bytes >= wl_workspace_bytes(WL_OP_LINEAR, &th, 1, T)
+ * With th->r == 0 and th->s == NULL this is the dense product y = x W0^T: the
+ * comparator of the precompute-outside path ("Serve and generate with
+ * weightless", "Set the fast path on NVIDIA") when W0 is a materialized W_eff. */
+wl_status wl_linear(const wl_theta *th, const void *x, void *y, int32_t T,
+                    void *ws, size_t ws_bytes, void *hip_stream);
+
+/* Q/K/V fusion ("In-kernel reconstruction", "Q/K/V fusion"): the three
+ * attention projections that read the same x, computed in one pass over the
+ * concatenated W0 rows, each child with its own V^T x (a block-diagonal U).
+ *   q, k, v   thetas with equal d_in; ranks, scales and d_out may differ
+ *   x         bf16 [T][d_in]
+ *   y_qkv     bf16 [T][q->d_out + k->d_out + v->d_out], columns Q | K | V
+ *   ws        ws_bytes >= wl_workspace_bytes(WL_OP_QKV, {q, k, v}, 3, T)
+ * Each child's columns equal wl_linear of that child to within rounding. */
+wl_status wl_qkv_fused(const wl_theta *q, const wl_theta *k, const wl_theta *v,
+                       const void *x, void *y_qkv, int32_t T,
+                       void *ws, size_t ws_bytes, void *hip_stream);
+
+/* Fused MLP ("In-kernel reconstruction", "The custom-op path": the fused MLP
+ * op runs gate, up, the activation and down as one operation):
+ *   g = linear(gate, x), u = linear(up, x)       (fp32, not rounded)
+ *   h = bf16_rne(gelu_tanh(g) * u)               (rounded once to bf16)
+ *   y = linear(down, h)
+ * with gelu_tanh(z) = 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+ * Shapes: gate.d_in == up.d_in (= d_model), gate.d_out == up.d_out ==
+ * down.d_in (= d_ff); x bf16 [T][d_model], y bf16 [T][down.d_out].
+ * h lives in the workspace:
+ *   ws_bytes >= wl_workspace_bytes(WL_OP_MLP, {gate, up, down}, 3, T). */
+wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta *down,
+                       const void *x, void *y, int32_t T,
+                       void *ws, size_t ws_bytes, void *hip_stream);
+
+/* The effective weight of the precompute-outside path ("Serve and generate
+ * with weightless", "Set the fast path on NVIDIA"):
+ *   W_eff[o,i] = bf16_rne( s[o] * W0[o,i] + sum_k U[o,k] * V[i,k] )
+ * W_eff: bf16 [th->d_out][th->d_in], written; must not overlap any input.
+ * Needs no workspace. */
+wl_status wl_materialize_weff(const wl_theta *th, void *W_eff, void *hip_stream);
+
+/* Kernel regime for the projection calls: 0 chooses by token count (the
+ * default), 1 forces the wave-per-row GEMV wherever its LDS staging fits, 2
+ * forces the matrix-core GEMM. Results agree within rounding in every regime;
+ * the switch exists for tests and measurements. Process-wide; returns the
+ * previous value, or -1 (and changes nothing) for any other argument. */
+int32_t wl_set_regime(int32_t regime);
+
+/* Static description of a status code. */
+const char *wl_status_str(wl_status status);
+
+/* Message describing the last non-WL_OK return on the calling thread ("" after
+ * a success). The pointer stays valid until the thread's next library call. */
+const char *wl_last_error(void);
+
+/* WL_ABI_VERSION of the built library. */
+int32_t wl_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WL_H */

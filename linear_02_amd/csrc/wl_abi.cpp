@@ -1,0 +1,442 @@
+// Host side of the C ABI declared in include/wl.h: argument checks, workspace
+// layout, regime choice (wave-per-row GEMV for a few tokens, matrix-core GEMM
+// above that) and kernel launches. Nothing here computes any part of the
+// projection; every arithmetic step runs in the HIP kernels.
+#include "wl.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "wl_kernels.h"
+
+namespace {
+
+thread_local std::string g_error;
+std::atomic<int> g_regime{0};   // 0 auto, 1 GEMV, 2 matrix-core GEMM
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+wl_status fail(wl_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    if (getenv("WL_LOG")) fprintf(stderr, "wl: %s\n", buf);
+    return st;
+}
+
+wl_status ok() {
+    g_error.clear();
+    return WL_OK;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+struct Range {
+    const void *p;
+    size_t bytes;
+};
+
+bool overlaps(Range a, Range b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+const int64_t kMaxElems = (int64_t)1 << 31;
+
+wl_status check_theta(const wl_theta *th, const char *name) {
+    if (!th) return fail(WL_ERR_INVALID_ARG, "%s: theta is NULL", name);
+    if (th->d_in < 1 || th->d_out < 1)
+        return fail(WL_ERR_INVALID_ARG, "%s: d_in=%d d_out=%d must be >= 1", name, th->d_in, th->d_out);
+    if (th->d_in % 8)
+        return fail(WL_ERR_INVALID_ARG, "%s: d_in=%d is not a multiple of 8", name, th->d_in);
+    if (th->r < 0) return fail(WL_ERR_INVALID_ARG, "%s: r=%d is negative", name, th->r);
+    if (th->r > wl::kMaxRank)
+        return fail(WL_ERR_UNSUPPORTED, "%s: r=%d exceeds the supported maximum %d", name, th->r, wl::kMaxRank);
+    if ((int64_t)th->d_in * th->d_out >= kMaxElems)
+        return fail(WL_ERR_INVALID_ARG, "%s: W0 has 2^31 or more elements", name);
+    if (!th->W0) return fail(WL_ERR_INVALID_ARG, "%s: W0 is NULL", name);
+    if (!aligned(th->W0, 16)) return fail(WL_ERR_INVALID_ARG, "%s: W0 is not 16-byte aligned", name);
+    if (th->s && !aligned(th->s, 4)) return fail(WL_ERR_INVALID_ARG, "%s: s is not 4-byte aligned", name);
+    if (th->r > 0) {
+        if (!th->U || !th->V) return fail(WL_ERR_INVALID_ARG, "%s: r=%d but U or V is NULL", name, th->r);
+        if (!aligned(th->U, 16) || !aligned(th->V, 16))
+            return fail(WL_ERR_INVALID_ARG, "%s: U or V is not 16-byte aligned", name);
+    }
+    return WL_OK;
+}
+
+void theta_ranges(const wl_theta *th, Range *out /* 4 */) {
+    out[0] = {th->W0, (size_t)th->d_out * th->d_in * 2};
+    out[1] = {th->s, th->s ? (size_t)th->d_out * 4 : 0};
+    out[2] = {th->r > 0 ? th->U : nullptr, (size_t)th->d_out * th->r * 2};
+    out[3] = {th->r > 0 ? th->V : nullptr, (size_t)th->d_in * th->r * 2};
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout. One layout function serves both wl_workspace_bytes and the
+// calls, so the two always agree.
+//
+//   [0, counters)     uint32 arrival counters of the V^T x reduction; zero on
+//                     entry, zero again when the call's work has finished
+//   vtx[c]            fp32 [T][r_c] per child with r_c > 0
+//   partial           fp32 slice partials of V^T x (when the input axis is sliced)
+//   h                 bf16 [T][d_ff] (MLP only)
+
+struct VtxPlan {
+    int n_slices = 1, slice_len = 0, n_tb = 0;
+};
+
+VtxPlan vtx_plan(int d_in, int T) {
+    VtxPlan p;
+    p.n_tb = (T + wl::kVtxTok - 1) / wl::kVtxTok;
+    int len;
+    if (T <= 64) {
+        // Few tokens: cut the input axis finely so the reduction spreads over many CUs.
+        len = (d_in + 31) / 32;
+        len = (len + 7) / 8 * 8;
+        if (len < 64) len = 64;
+    } else {
+        len = wl::kVtxMaxSlice;
+    }
+    if (len > wl::kVtxMaxSlice) len = wl::kVtxMaxSlice;
+    if (len > d_in) len = d_in;
+    p.slice_len = len;
+    p.n_slices = (d_in + len - 1) / len;
+    return p;
+}
+
+struct Layout {
+    size_t counters = 0;
+    size_t vtx[4] = {0, 0, 0, 0};   // offsets
+    size_t partial = 0;
+    size_t h = 0;
+    size_t total = 0;
+};
+
+// thetas: children of one vtx phase (n <= 3) sharing input width d_in; extra
+// vtx slots appended for the MLP's down projection.
+Layout layout(int op, const wl_theta *const *th, int T) {
+    Layout L;
+    size_t off = 0;
+    int n_ch = op == WL_OP_LINEAR ? 1 : op == WL_OP_QKV ? 3 : 2;
+    int d_in = th[0]->d_in;
+    VtxPlan vp = vtx_plan(d_in, T);
+    size_t n_counters = (size_t)vp.n_tb * n_ch;
+    size_t part_elems = vp.n_slices > 1 ? (size_t)vp.n_tb * n_ch * vp.n_slices * wl::kVtxTok * wl::kMaxRank : 0;
+    if (op == WL_OP_MLP) {
+        VtxPlan vd = vtx_plan(th[2]->d_in, T);
+        if ((size_t)vd.n_tb > n_counters) n_counters = vd.n_tb;
+        size_t pd = vd.n_slices > 1 ? (size_t)vd.n_tb * vd.n_slices * wl::kVtxTok * wl::kMaxRank : 0;
+        if (pd > part_elems) part_elems = pd;
+    }
+    L.counters = 0;
+    off = round_up(n_counters * 4, kAlign);
+    const int n_v = op == WL_OP_MLP ? 3 : n_ch;
+    for (int c = 0; c < n_v; ++c) {
+        L.vtx[c] = off;
+        off = round_up(off + (size_t)T * th[c]->r * 4, kAlign);
+    }
+    L.partial = off;
+    off = round_up(off + part_elems * 4, kAlign);
+    if (op == WL_OP_MLP) {
+        L.h = off;
+        off = round_up(off + (size_t)T * th[0]->d_out * 2, kAlign);
+    }
+    L.total = off;
+    return L;
+}
+
+wl::Child make_child(const wl_theta *th, char *ws, size_t vtx_off, int col0) {
+    wl::Child c;
+    c.W0 = static_cast<const uint16_t *>(th->W0);
+    c.s = th->s;
+    c.U = static_cast<const uint16_t *>(th->U);
+    c.V = static_cast<const uint16_t *>(th->V);
+    c.vtx = th->r > 0 ? reinterpret_cast<const float *>(ws + vtx_off) : nullptr;
+    c.r = th->r;
+    c.d_out = th->d_out;
+    c.col0 = col0;
+    return c;
+}
+
+// V^T x for the children with r > 0 (all sharing input x of width d_in).
+wl_status run_vtx(const wl_theta *const *th, int n, const size_t *vtx_off, const Layout &L, char *ws,
+                  const void *x, int d_in, int T, hipStream_t stream) {
+    wl::VtxJob job{};
+    job.x = static_cast<const uint16_t *>(x);
+    job.d_in = d_in;
+    job.T = T;
+    for (int c = 0; c < n; ++c) {
+        if (th[c]->r == 0) continue;
+        job.V[job.n_ch] = static_cast<const uint16_t *>(th[c]->V);
+        job.vtx[job.n_ch] = reinterpret_cast<float *>(ws + vtx_off[c]);
+        job.r[job.n_ch] = th[c]->r;
+        ++job.n_ch;
+    }
+    if (job.n_ch == 0) return WL_OK;
+    const VtxPlan vp = vtx_plan(d_in, T);
+    job.n_slices = vp.n_slices;
+    job.slice_len = vp.slice_len;
+    job.partial = reinterpret_cast<float *>(ws + L.partial);
+    job.counter = reinterpret_cast<uint32_t *>(ws + L.counters);
+    const hipError_t e = wl::launch_vtx(job, stream);
+    if (e != hipSuccess) return fail(WL_ERR_HIP, "V^T x launch failed: %s", hipGetErrorString(e));
+    return WL_OK;
+}
+
+bool use_gemv(int T, int d_in) {
+    const int regime = g_regime.load(std::memory_order_relaxed);
+    if (d_in > wl::kGemvMaxStaged) return false;
+    if (regime == 1) return true;
+    if (regime == 2) return false;
+    return T <= 8;
+}
+
+// One projection over shared input x: children side by side in y (ldy = total width),
+// or the gate/up pair (pair = true, y = h).
+wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, const void *x, void *y, int ldy,
+                   hipStream_t stream) {
+    hipError_t e;
+    const bool gemv = use_gemv(T, d_in);
+    if (getenv("WL_LOG"))
+        fprintf(stderr, "wl: proj n_ch=%d pair=%d d_in=%d T=%d -> %s\n", n_ch, (int)pair, d_in, T,
+                gemv ? "gemv" : "mfma");
+    if (gemv) {
+        wl::Gemv g{};
+        for (int c = 0; c < n_ch; ++c) g.ch[c] = ch[c];
+        g.n_ch = n_ch;
+        g.pair = pair;
+        g.d_in = d_in;
+        g.rows = 0;
+        if (pair)
+            g.rows = ch[0].d_out;
+        else
+            for (int c = 0; c < n_ch; ++c) g.rows += ch[c].d_out;
+        g.ldy = ldy;
+        g.T = T;
+        g.x = static_cast<const uint16_t *>(x);
+        g.y = static_cast<uint16_t *>(y);
+        e = wl::launch_gemv(g, cu_count(), stream);
+    } else {
+        wl::Gemm g{};
+        for (int c = 0; c < n_ch; ++c) g.ch[c] = ch[c];
+        g.n_ch = n_ch;
+        g.pair = pair;
+        g.d_in = d_in;
+        g.ldy = ldy;
+        g.T = T;
+        g.x = static_cast<const uint16_t *>(x);
+        g.y = static_cast<uint16_t *>(y);
+        e = wl::launch_gemm(g, stream);
+    }
+    if (e != hipSuccess) return fail(WL_ERR_HIP, "projection launch failed: %s", hipGetErrorString(e));
+    return WL_OK;
+}
+
+wl_status check_io(const void *x, const void *y, int T, int d_in, int ldy) {
+    if (T < 0) return fail(WL_ERR_INVALID_ARG, "T=%d is negative", T);
+    if (T == 0) return WL_OK;
+    if (!x || !y) return fail(WL_ERR_INVALID_ARG, "x or y is NULL");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(WL_ERR_INVALID_ARG, "x or y is not 16-byte aligned");
+    if ((int64_t)T * d_in >= kMaxElems || (int64_t)T * ldy >= kMaxElems)
+        return fail(WL_ERR_INVALID_ARG, "x or y has 2^31 or more elements");
+    return WL_OK;
+}
+
+wl_status check_ws(size_t need, const void *ws, size_t ws_bytes) {
+    if (ws_bytes < need)
+        return fail(WL_ERR_WORKSPACE, "workspace of %zu bytes is below the required %zu", ws_bytes, need);
+    if (need > 0 && !ws) return fail(WL_ERR_INVALID_ARG, "workspace is NULL");
+    if (ws && !aligned(ws, kAlign)) return fail(WL_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    return WL_OK;
+}
+
+// y must not overlap x, the workspace or any theta tensor.
+wl_status check_overlap(Range y, const Range *in, int n) {
+    for (int j = 0; j < n; ++j)
+        if (overlaps(y, in[j])) return fail(WL_ERR_INVALID_ARG, "output overlaps an input or the workspace");
+    return WL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t wl_abi_version(void) { return WL_ABI_VERSION; }
+
+const char *wl_status_str(wl_status st) {
+    switch (st) {
+        case WL_OK: return "ok";
+        case WL_ERR_INVALID_ARG: return "invalid argument";
+        case WL_ERR_UNSUPPORTED: return "unsupported";
+        case WL_ERR_HIP: return "HIP error";
+        case WL_ERR_WORKSPACE: return "workspace too small";
+    }
+    return "unknown status";
+}
+
+const char *wl_last_error(void) { return g_error.c_str(); }
+
+int32_t wl_set_regime(int32_t regime) {
+    if (regime < 0 || regime > 2) return -1;
+    return g_regime.exchange(regime);
+}
+
+size_t wl_workspace_bytes(int32_t op, const wl_theta *const *th, int32_t n_th, int32_t T) {
+    if (!th || T < 0) return 0;
+    if (op == WL_OP_LINEAR) {
+        if (n_th != 1 || check_theta(th[0], "theta") != WL_OK) return 0;
+    } else if (op == WL_OP_QKV || op == WL_OP_MLP) {
+        if (n_th != 3) return 0;
+        for (int c = 0; c < 3; ++c)
+            if (check_theta(th[c], "theta") != WL_OK) return 0;
+    } else {
+        return 0;
+    }
+    return layout(op, th, T).total;
+}
+
+wl_status wl_linear(const wl_theta *th, const void *x, void *y, int32_t T, void *ws, size_t ws_bytes,
+                    void *hip_stream) {
+    wl_status st = check_theta(th, "theta");
+    if (st != WL_OK) return st;
+    if ((st = check_io(x, y, T, th->d_in, th->d_out)) != WL_OK) return st;
+    if (T == 0) return ok();
+    const wl_theta *ths[1] = {th};
+    const Layout L = layout(WL_OP_LINEAR, ths, T);
+    if ((st = check_ws(L.total, ws, ws_bytes)) != WL_OK) return st;
+    Range in[6];
+    theta_ranges(th, in);
+    in[4] = {x, (size_t)T * th->d_in * 2};
+    in[5] = {ws, ws_bytes};
+    if ((st = check_overlap({y, (size_t)T * th->d_out * 2}, in, 6)) != WL_OK) return st;
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    char *w = static_cast<char *>(ws);
+    if ((st = run_vtx(ths, 1, L.vtx, L, w, x, th->d_in, T, stream)) != WL_OK) return st;
+    const wl::Child ch = make_child(th, w, L.vtx[0], 0);
+    if ((st = run_proj(&ch, 1, false, th->d_in, T, x, y, th->d_out, stream)) != WL_OK) return st;
+    return ok();
+}
+
+wl_status wl_qkv_fused(const wl_theta *q, const wl_theta *k, const wl_theta *v, const void *x, void *y_qkv,
+                       int32_t T, void *ws, size_t ws_bytes, void *hip_stream) {
+    const wl_theta *ths[3] = {q, k, v};
+    const char *names[3] = {"q", "k", "v"};
+    wl_status st;
+    for (int c = 0; c < 3; ++c)
+        if ((st = check_theta(ths[c], names[c])) != WL_OK) return st;
+    if (k->d_in != q->d_in || v->d_in != q->d_in)
+        return fail(WL_ERR_INVALID_ARG, "q, k, v must share d_in (%d, %d, %d)", q->d_in, k->d_in, v->d_in);
+    const int64_t width = (int64_t)q->d_out + k->d_out + v->d_out;
+    if (width >= kMaxElems) return fail(WL_ERR_INVALID_ARG, "q, k, v outputs are too wide");
+    if ((st = check_io(x, y_qkv, T, q->d_in, (int)width)) != WL_OK) return st;
+    if (T == 0) return ok();
+    const Layout L = layout(WL_OP_QKV, ths, T);
+    if ((st = check_ws(L.total, ws, ws_bytes)) != WL_OK) return st;
+    Range in[14];
+    for (int c = 0; c < 3; ++c) theta_ranges(ths[c], in + 4 * c);
+    in[12] = {x, (size_t)T * q->d_in * 2};
+    in[13] = {ws, ws_bytes};
+    if ((st = check_overlap({y_qkv, (size_t)T * width * 2}, in, 14)) != WL_OK) return st;
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    char *w = static_cast<char *>(ws);
+    if ((st = run_vtx(ths, 3, L.vtx, L, w, x, q->d_in, T, stream)) != WL_OK) return st;
+    wl::Child ch[3];
+    int col0 = 0;
+    for (int c = 0; c < 3; ++c) {
+        ch[c] = make_child(ths[c], w, L.vtx[c], col0);
+        col0 += ths[c]->d_out;
+    }
+    if ((st = run_proj(ch, 3, false, q->d_in, T, x, y_qkv, (int)width, stream)) != WL_OK) return st;
+    return ok();
+}
+
+wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta *down, const void *x, void *y,
+                       int32_t T, void *ws, size_t ws_bytes, void *hip_stream) {
+    const wl_theta *ths[3] = {gate, up, down};
+    const char *names[3] = {"gate", "up", "down"};
+    wl_status st;
+    for (int c = 0; c < 3; ++c)
+        if ((st = check_theta(ths[c], names[c])) != WL_OK) return st;
+    if (up->d_in != gate->d_in || up->d_out != gate->d_out || down->d_in != gate->d_out)
+        return fail(WL_ERR_INVALID_ARG,
+                    "MLP shapes disagree: gate %dx%d, up %dx%d, down %dx%d (need gate == up, down.d_in == d_ff)",
+                    gate->d_out, gate->d_in, up->d_out, up->d_in, down->d_out, down->d_in);
+    if ((st = check_io(x, y, T, gate->d_in, down->d_out)) != WL_OK) return st;
+    if ((int64_t)T * gate->d_out >= kMaxElems) return fail(WL_ERR_INVALID_ARG, "h has 2^31 or more elements");
+    if (T == 0) return ok();
+    const Layout L = layout(WL_OP_MLP, ths, T);
+    if ((st = check_ws(L.total, ws, ws_bytes)) != WL_OK) return st;
+    Range in[14];
+    for (int c = 0; c < 3; ++c) theta_ranges(ths[c], in + 4 * c);
+    in[12] = {x, (size_t)T * gate->d_in * 2};
+    in[13] = {ws, ws_bytes};
+    if ((st = check_overlap({y, (size_t)T * down->d_out * 2}, in, 14)) != WL_OK) return st;
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    char *w = static_cast<char *>(ws);
+    void *h = w + L.h;
+    const int d_ff = gate->d_out;
+    // gate/up -> h = bf16(gelu_tanh(g) * u)
+    if ((st = run_vtx(ths, 2, L.vtx, L, w, x, gate->d_in, T, stream)) != WL_OK) return st;
+    wl::Child gu[2] = {make_child(gate, w, L.vtx[0], 0), make_child(up, w, L.vtx[1], 0)};
+    if ((st = run_proj(gu, 2, true, gate->d_in, T, x, h, d_ff, stream)) != WL_OK) return st;
+    // down over h
+    const wl_theta *dn[1] = {down};
+    const size_t dn_off[1] = {L.vtx[2]};
+    if ((st = run_vtx(dn, 1, dn_off, L, w, h, d_ff, T, stream)) != WL_OK) return st;
+    const wl::Child dc = make_child(down, w, L.vtx[2], 0);
+    if ((st = run_proj(&dc, 1, false, d_ff, T, h, y, down->d_out, stream)) != WL_OK) return st;
+    return ok();
+}
+
+wl_status wl_materialize_weff(const wl_theta *th, void *W_eff, void *hip_stream) {
+    wl_status st = check_theta(th, "theta");
+    if (st != WL_OK) return st;
+    if (!W_eff) return fail(WL_ERR_INVALID_ARG, "W_eff is NULL");
+    if (!aligned(W_eff, 16)) return fail(WL_ERR_INVALID_ARG, "W_eff is not 16-byte aligned");
+    Range in[4];
+    theta_ranges(th, in);
+    if ((st = check_overlap({W_eff, (size_t)th->d_out * th->d_in * 2}, in, 4)) != WL_OK) return st;
+    wl::Weff w{};
+    w.W0 = static_cast<const uint16_t *>(th->W0);
+    w.s = th->s;
+    w.U = static_cast<const uint16_t *>(th->U);
+    w.V = static_cast<const uint16_t *>(th->V);
+    w.W_eff = static_cast<uint16_t *>(W_eff);
+    w.d_in = th->d_in;
+    w.d_out = th->d_out;
+    w.r = th->r;
+    const hipError_t e = wl::launch_weff(w, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(WL_ERR_HIP, "materialize launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

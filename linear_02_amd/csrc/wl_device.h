@@ -1,0 +1,69 @@
+// Device-side helpers of the reconstruct-and-project linear kernels.
+// gfx950 (CDNA4) only: wave64, v_dot2c_f32_bf16, v_cvt_pk_bf16_f32, DPP row
+// broadcasts and the bf16 matrix-core instructions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wl {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// bf16 bit pattern -> fp32. Exact: a bf16 is the upper half of a binary32.
+__device__ __forceinline__ float bf16_f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16 bit pattern, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f_bf16(float v) {
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// acc + dot of two 16-byte pieces (8 bf16 each); products are exact in fp32
+// and are added into the fp32 accumulator.
+__device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float acc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]),
+                                              __builtin_bit_cast(bf16x2, x[j]), acc, false);
+    return acc;
+}
+
+template <int ctrl, int row_mask = 0xF, bool bound_ctrl = true>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, row_mask, 0xF,
+                                                      bound_ctrl));
+}
+
+// Sum over the 64 lanes of a wave. The full sum lands in lane 63; the other
+// lanes hold partial sums. Butterflies inside each 16-lane row (quad swaps,
+// half-row and row mirrors), then the row-15 and lane-31 broadcasts fold rows
+// 0..3 into row 3.
+__device__ __forceinline__ float wave_sum_last(float v) {
+    v += dpp<0xB1>(v);             // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);             // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);            // row_half_mirror
+    v += dpp<0x140>(v);            // row_mirror: every lane holds its row's sum
+    v += dpp<0x142, 0xA, false>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp<0x143, 0xC, false>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// Sum over the 64 lanes, returned in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_last(v)), 63));
+}
+
+// tanh-approximated GELU (Hendrycks & Gimpel, 2016), fp32, device tanhf.
+__device__ __forceinline__ float gelu_tanh(float z) {
+    const float c0 = 0.7978845608028654f;   // sqrt(2 / pi)
+    const float c1 = 0.044715f;
+    return 0.5f * z * (1.0f + tanhf(c0 * (z + c1 * z * z * z)));
+}
+
+}  // namespace wl

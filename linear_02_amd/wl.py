@@ -1,0 +1,202 @@
+"""Python binding of libwl (the C ABI in include/wl.h).
+
+Argument marshalling only: every function here checks tensor dtypes, shapes
+and devices, passes raw device pointers and the current HIP stream to the
+library, and returns the output tensor. All arithmetic runs in the library's
+HIP kernels; there is no fallback of any kind. If libwl.so is missing the
+import fails loudly (build it with ``python -m linear_02_amd.build``).
+
+A theta is a dict with device tensors ``W0`` (bf16 [d_out][d_in]), ``s`` (fp32
+[d_out] or None), ``U`` (bf16 [d_out][r]), ``V`` (bf16 [d_in][r]) and the ints
+``d_in``, ``d_out``, ``r``, as drawn by ``linear_02_amd.inputs.theta`` and
+moved with :func:`theta_to`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwl.so")
+
+OP_LINEAR, OP_QKV, OP_MLP = 0, 1, 2
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error", 4: "workspace too small"}
+
+
+class WlError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Theta(ctypes.Structure):
+    _fields_ = [("W0", ctypes.c_void_p), ("s", ctypes.c_void_p), ("U", ctypes.c_void_p),
+                ("V", ctypes.c_void_p), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("r", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBRARY):
+        raise ImportError(f"{LIBRARY} is not built; run `python -m linear_02_amd.build`")
+    lib = ctypes.CDLL(LIBRARY)
+    P = ctypes.POINTER(Theta)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.wl_workspace_bytes.argtypes = [i32, ctypes.POINTER(P), i32, i32]
+    lib.wl_workspace_bytes.restype = sz
+    lib.wl_linear.argtypes = [P, vp, vp, i32, vp, sz, vp]
+    lib.wl_qkv_fused.argtypes = [P, P, P, vp, vp, i32, vp, sz, vp]
+    lib.wl_mlp_fused.argtypes = [P, P, P, vp, vp, i32, vp, sz, vp]
+    lib.wl_materialize_weff.argtypes = [P, vp, vp]
+    for name in ("wl_linear", "wl_qkv_fused", "wl_mlp_fused", "wl_materialize_weff"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.wl_set_regime.argtypes = [i32]
+    lib.wl_set_regime.restype = i32
+    lib.wl_status_str.argtypes = [ctypes.c_int]
+    lib.wl_status_str.restype = ctypes.c_char_p
+    lib.wl_last_error.argtypes = []
+    lib.wl_last_error.restype = ctypes.c_char_p
+    lib.wl_abi_version.argtypes = []
+    lib.wl_abi_version.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise WlError(status, lib.wl_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def theta_to(th: dict, device) -> dict:
+    """Copy a theta's tensors to ``device`` (contiguous); ints are kept."""
+    out = dict(th)
+    for key in ("W0", "s", "U", "V"):
+        if th.get(key) is not None:
+            out[key] = th[key].to(device).contiguous()
+    return out
+
+
+def make_theta(th: dict) -> Theta:
+    """The C struct of a theta dict (device tensors). The dict keeps them alive."""
+    W0, s, U, V = th["W0"], th.get("s"), th.get("U"), th.get("V")
+    d_in, d_out, r = int(th["d_in"]), int(th["d_out"]), int(th["r"])
+    if W0.dtype != torch.bfloat16 or not W0.is_contiguous() or tuple(W0.shape) != (d_out, d_in):
+        raise ValueError("W0 must be a contiguous bf16 [d_out][d_in] tensor")
+    if s is not None and (s.dtype != torch.float32 or not s.is_contiguous() or s.numel() != d_out):
+        raise ValueError("s must be a contiguous fp32 [d_out] tensor or None")
+    if r > 0:
+        for name, t, rows in (("U", U, d_out), ("V", V, d_in)):
+            if t is None or t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != (rows, r):
+                raise ValueError(f"{name} must be a contiguous bf16 [{rows}][{r}] tensor")
+    return Theta(_ptr(W0), _ptr(s), _ptr(U) if r > 0 else None, _ptr(V) if r > 0 else None, d_in, d_out, r)
+
+
+def workspace_bytes(op: int, thetas: list, T: int) -> int:
+    structs = [make_theta(t) for t in thetas]
+    arr = (ctypes.POINTER(Theta) * len(structs))(*[ctypes.pointer(s) for s in structs])
+    return int(lib.wl_workspace_bytes(op, arr, len(structs), T))
+
+
+class Workspace:
+    """A zero-filled device workspace per (device, stream) that grows on demand.
+
+    Calls on one stream run in order, so they can share one workspace; every call
+    leaves it fit for the next (its counters are zero again)."""
+
+    def __init__(self):
+        self._bufs: dict = {}
+
+    def get(self, device: torch.device, nbytes: int) -> torch.Tensor | None:
+        if nbytes == 0:
+            return None
+        key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+        buf = self._bufs.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            self._bufs[key] = buf
+        return buf
+
+
+WORKSPACE = Workspace()
+
+
+def _io(x: torch.Tensor, d_in: int) -> int:
+    if x.dtype != torch.bfloat16 or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != d_in:
+        raise ValueError(f"x must be a contiguous bf16 [T][{d_in}] tensor")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    return x.shape[0]
+
+
+def wl_linear(th: dict, x: torch.Tensor, y: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """y = s (.) (W0 x) + U (V^T x), bf16 [T][d_out]."""
+    T = _io(x, int(th["d_in"]))
+    st = make_theta(th)
+    if y is None:
+        y = torch.empty(T, int(th["d_out"]), dtype=torch.bfloat16, device=x.device)
+    need = workspace_bytes(OP_LINEAR, [th], T)
+    ws = ws if ws is not None else WORKSPACE.get(x.device, need)
+    _check(lib.wl_linear(ctypes.byref(st), _ptr(x), _ptr(y), T, _ptr(ws),
+                         0 if ws is None else ws.numel() * ws.element_size(), _stream(x.device)))
+    return y
+
+
+def wl_qkv_fused(q: dict, k: dict, v: dict, x: torch.Tensor, y: torch.Tensor | None = None,
+                 ws: torch.Tensor | None = None):
+    """Q | K | V side by side, bf16 [T][dq + dk + dv]."""
+    T = _io(x, int(q["d_in"]))
+    sq, sk, sv = make_theta(q), make_theta(k), make_theta(v)
+    width = int(q["d_out"]) + int(k["d_out"]) + int(v["d_out"])
+    if y is None:
+        y = torch.empty(T, width, dtype=torch.bfloat16, device=x.device)
+    need = workspace_bytes(OP_QKV, [q, k, v], T)
+    ws = ws if ws is not None else WORKSPACE.get(x.device, need)
+    _check(lib.wl_qkv_fused(ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(sv), _ptr(x), _ptr(y), T,
+                            _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(x.device)))
+    return y
+
+
+def wl_mlp_fused(gate: dict, up: dict, down: dict, x: torch.Tensor, y: torch.Tensor | None = None,
+                 ws: torch.Tensor | None = None):
+    """down(bf16(gelu_tanh(gate x) * up x)), bf16 [T][down.d_out]."""
+    T = _io(x, int(gate["d_in"]))
+    sg, su, sd = make_theta(gate), make_theta(up), make_theta(down)
+    if y is None:
+        y = torch.empty(T, int(down["d_out"]), dtype=torch.bfloat16, device=x.device)
+    need = workspace_bytes(OP_MLP, [gate, up, down], T)
+    ws = ws if ws is not None else WORKSPACE.get(x.device, need)
+    _check(lib.wl_mlp_fused(ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), _ptr(x), _ptr(y), T,
+                            _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(x.device)))
+    return y
+
+
+def wl_materialize_weff(th: dict, W_eff: torch.Tensor | None = None):
+    """W_eff = bf16(s (.) W0 + U V^T), bf16 [d_out][d_in]."""
+    st = make_theta(th)
+    dev = th["W0"].device
+    if W_eff is None:
+        W_eff = torch.empty(int(th["d_out"]), int(th["d_in"]), dtype=torch.bfloat16, device=dev)
+    _check(lib.wl_materialize_weff(ctypes.byref(st), _ptr(W_eff), _stream(dev)))
+    return W_eff
+
+
+def set_regime(regime: int) -> int:
+    """0 auto, 1 GEMV, 2 matrix-core GEMM; returns the previous setting."""
+    prev = int(lib.wl_set_regime(regime))
+    if prev < 0:
+        raise ValueError(f"regime {regime} is not 0, 1 or 2")
+    return prev
+
+
+def abi_version() -> int:
+    return int(lib.wl_abi_version())

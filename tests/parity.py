@@ -1,0 +1,44 @@
+"""Acceptance checks of HIP outputs against the CPU oracle.
+
+Floating-point outputs pass when, over the whole output tensor of a call,
+  relL2 = ||y_gpu - y_oracle||_2 / ||y_oracle||_2 <= 2e-3
+and for every element
+  |y_gpu - y_oracle| <= 8e-3 * bound,
+bound being the oracle's magnitude bound |s| sum|W0 x| + sum|U vtx| (for W_eff:
+|s W0| + sum|U V|). One bf16 rounding of the output costs at most 2^-9 relative,
+inside both bars; fp32 accumulation adds orders of magnitude less.
+Integer-valued cases are compared bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+REL_L2 = 2e-3
+ELEM = 8e-3
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+def check(y_gpu: torch.Tensor, y_ref: np.ndarray, bound: np.ndarray, what: str = "") -> dict:
+    yg = to_f64(y_gpu).reshape(y_ref.shape)
+    assert np.all(np.isfinite(yg)), f"{what}: non-finite output"
+    diff = yg - y_ref
+    nref = float(np.linalg.norm(y_ref))
+    ndiff = float(np.linalg.norm(diff))
+    rel = ndiff / nref if nref > 0 else (0.0 if ndiff == 0 else float("inf"))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, np.abs(diff) / bound, np.where(diff == 0, 0.0, np.inf))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    assert rel <= REL_L2, f"{what}: relL2 {rel:.3e} > {REL_L2}"
+    assert worst <= ELEM, f"{what}: max |err|/bound {worst:.3e} > {ELEM} at {np.unravel_index(ratio.argmax(), ratio.shape)}"
+    return dict(rel_l2=rel, max_err_over_bound=worst)
+
+
+def check_exact(y_gpu: torch.Tensor, y_ref: np.ndarray, what: str = "") -> None:
+    yg = to_f64(y_gpu).reshape(y_ref.shape)
+    bad = np.argwhere(yg != y_ref)
+    assert bad.size == 0, (f"{what}: {len(bad)} elements differ; first at {tuple(bad[0])}: "
+                           f"gpu {yg[tuple(bad[0])]} vs oracle {y_ref[tuple(bad[0])]}")

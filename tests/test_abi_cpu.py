@@ -1,0 +1,183 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and
+rejects bad arguments on the host before touching the device.
+
+Pointers below are fake addresses that are never dereferenced: every call here
+fails validation (or is the T == 0 no-op) before anything reaches HIP.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(REPO, "include", "wl.h")
+
+
+@pytest.fixture(scope="module")
+def wl():
+    from linear_02_amd import build
+    if not os.path.exists(build.LIBRARY):
+        build.build()
+    from linear_02_amd import wl as mod
+    return mod
+
+
+def declared_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wl_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(wl):
+    names = declared_functions()
+    assert {"wl_linear", "wl_qkv_fused", "wl_mlp_fused", "wl_materialize_weff",
+            "wl_workspace_bytes"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", wl.LIBRARY], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (wl_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for n in names:
+        getattr(wl.lib, n)
+
+
+def test_abi_version_and_status_strings(wl):
+    assert wl.abi_version() == 1
+    assert wl.lib.wl_status_str(0) == b"ok"
+    assert wl.lib.wl_status_str(4) == b"workspace too small"
+    assert wl.lib.wl_status_str(99) == b"unknown status"
+
+
+A = 0x10000   # fake, 256-byte aligned device addresses
+B = 0x20000000
+C = 0x40000000
+D = 0x60000000
+
+
+def theta(W0=A, s=None, U=B, V=C, d_in=64, d_out=32, r=4):
+    return wl_mod().Theta(W0, s, U, V, d_in, d_out, r)
+
+
+def wl_mod():
+    from linear_02_amd import wl as mod
+    return mod
+
+
+def call_linear(wl, th, x=D, y=D + 0x1000000, T=1, ws=D + 0x2000000, ws_bytes=1 << 30):
+    p = None if th is None else ctypes.byref(th)
+    return wl.lib.wl_linear(p, x, y, T, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(d_in=60), 1),            # not a multiple of 8
+    (dict(d_in=0), 1),
+    (dict(d_out=0), 1),
+    (dict(r=-1), 1),
+    (dict(r=65), 2),               # above the supported rank
+    (dict(W0=None), 1),
+    (dict(W0=A + 8), 1),           # misaligned
+    (dict(U=None), 1),
+    (dict(V=B + 2), 1),
+    (dict(s=A + 2), 1),
+])
+def test_linear_rejects_bad_theta(wl, case, status):
+    assert call_linear(wl, theta(**case)) == status
+    assert wl.lib.wl_last_error() != b""
+
+
+def test_linear_rejects_null_theta_and_io(wl):
+    assert call_linear(wl, None) == 1
+    assert call_linear(wl, theta(), x=None) == 1
+    assert call_linear(wl, theta(), y=None) == 1
+    assert call_linear(wl, theta(), x=D + 4) == 1
+    assert call_linear(wl, theta(), T=-1) == 1
+
+
+def test_r0_needs_no_factors(wl):
+    th = theta(U=None, V=None, r=0)
+    assert call_linear(wl, th, T=0) == 0
+
+
+def test_t0_is_a_noop(wl):
+    assert call_linear(wl, theta(), x=None, y=None, T=0, ws=None, ws_bytes=0) == 0
+    assert wl.lib.wl_last_error() == b""
+
+
+def test_workspace_checks(wl):
+    th = theta()
+    arr = (ctypes.POINTER(wl.Theta) * 1)(ctypes.pointer(th))
+    need = wl.lib.wl_workspace_bytes(0, arr, 1, 1)
+    assert need > 0 and need % 256 == 0
+    assert call_linear(wl, th, ws_bytes=need - 1) == 4
+    assert b"workspace" in wl.lib.wl_last_error()
+    assert call_linear(wl, th, ws=None, ws_bytes=need) == 1
+    assert call_linear(wl, th, ws=D + 0x2000010, ws_bytes=need) == 1   # misaligned
+
+
+def test_workspace_bytes_grows_with_tokens_and_rejects_bad_args(wl):
+    th = theta(d_in=1152, d_out=1152, r=32)
+    arr = (ctypes.POINTER(wl.Theta) * 1)(ctypes.pointer(th))
+    sizes = [wl.lib.wl_workspace_bytes(0, arr, 1, T) for T in (0, 1, 8, 64, 2048)]
+    assert all(s % 256 == 0 for s in sizes)
+    assert sizes == sorted(sizes) and sizes[-1] > sizes[1]
+    assert wl.lib.wl_workspace_bytes(0, arr, 2, 1) == 0      # wrong count
+    assert wl.lib.wl_workspace_bytes(7, arr, 1, 1) == 0      # unknown op
+    assert wl.lib.wl_workspace_bytes(0, arr, 1, -1) == 0
+    bad = theta(d_in=12)
+    arr_bad = (ctypes.POINTER(wl.Theta) * 1)(ctypes.pointer(bad))
+    assert wl.lib.wl_workspace_bytes(0, arr_bad, 1, 1) == 0
+
+
+def test_output_overlap_is_rejected(wl):
+    th = theta()
+    # y on top of x
+    assert call_linear(wl, th, x=D, y=D) == 1
+    # y inside W0 (W0 spans 32*64*2 bytes from A)
+    assert call_linear(wl, th, y=A + 256) == 1
+    # y inside the workspace
+    assert call_linear(wl, th, y=D + 0x2000000 + 4096) == 1
+    assert b"overlap" in wl.lib.wl_last_error()
+
+
+def test_qkv_requires_shared_d_in(wl):
+    q, k = theta(d_in=64), theta(W0=A + 0x100000, d_in=64)
+    v = theta(W0=A + 0x200000, d_in=128)
+    rc = wl.lib.wl_qkv_fused(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), D, D + 0x1000000, 1,
+                             D + 0x2000000, 1 << 30, None)
+    assert rc == 1 and b"d_in" in wl.lib.wl_last_error()
+
+
+def test_mlp_shape_checks(wl):
+    gate = theta(W0=A, d_in=64, d_out=128)
+    up = theta(W0=A + 0x100000, d_in=64, d_out=128)
+    down_bad = theta(W0=A + 0x200000, d_in=64, d_out=64)
+    rc = wl.lib.wl_mlp_fused(ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down_bad), D, D + 0x1000000,
+                             1, D + 0x2000000, 1 << 30, None)
+    assert rc == 1 and b"MLP" in wl.lib.wl_last_error()
+    up_bad = theta(W0=A + 0x100000, d_in=64, d_out=120)
+    down = theta(W0=A + 0x200000, d_in=128, d_out=64)
+    rc = wl.lib.wl_mlp_fused(ctypes.byref(gate), ctypes.byref(up_bad), ctypes.byref(down), D, D + 0x1000000,
+                             1, D + 0x2000000, 1 << 30, None)
+    assert rc == 1
+
+
+def test_weff_checks(wl):
+    th = theta()
+    assert wl.lib.wl_materialize_weff(ctypes.byref(th), None, None) == 1
+    assert wl.lib.wl_materialize_weff(ctypes.byref(th), D + 2, None) == 1
+    assert wl.lib.wl_materialize_weff(ctypes.byref(th), A, None) == 1     # on top of W0
+    assert wl.lib.wl_materialize_weff(ctypes.byref(theta(r=99)), D, None) == 2
+
+
+def test_regime_switch(wl):
+    prev = wl.set_regime(2)
+    try:
+        assert wl.set_regime(1) == 2
+        with pytest.raises(ValueError):
+            wl.set_regime(5)
+    finally:
+        wl.set_regime(prev)
