@@ -14,8 +14,8 @@
  * Memory.    Every tensor pointer is a DEVICE pointer on the current HIP device.
  *            The caller allocates and owns every buffer, including the
  *            workspace; the library never allocates or frees memory and keeps
- *            no per-call state (its only global state is a per-device cache of
- *            the compute-unit count and the regime switch below).
+ *            no per-call state (its only global state is the regime switch
+ *            below).
  * Layout.    All tensors are row-major and contiguous:
  *              W0 bf16 [d_out][d_in]   s fp32 [d_out]
  *              U  bf16 [d_out][r]      V bf16 [d_in][r]
@@ -42,11 +42,9 @@
  *            NULL = the default stream) and returns; errors that happen on the
  *            device surface at the caller's next synchronization.
  * Workspace. Operations that take `ws` need at least wl_workspace_bytes(...)
- *            bytes. The workspace must be zero-filled before its first use;
- *            every call leaves it in a state fit for the next call (its counter
- *            region is zero again when the call's stream work completes).
- *            Calls that can run at the same time (different streams) must not
- *            share a workspace.
+ *            bytes of scratch device memory; its contents on entry do not
+ *            matter. Calls that can run at the same time (different streams)
+ *            must not share a workspace.
  * Errors.    Every argument is checked on the host before anything is
  *            enqueued; a fused operation checks all of its thetas first, so an
  *            invalid argument never leaves a partial launch.
@@ -153,10 +151,12 @@ wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta 
 wl_status wl_materialize_weff(const wl_theta *th, void *W_eff, void *hip_stream);
 
 /* Kernel regime for the projection calls: 0 chooses by token count (the
- * default), 1 forces the wave-per-row GEMV wherever its LDS staging fits, 2
- * forces the matrix-core GEMM. Results agree within rounding in every regime;
- * the switch exists for tests and measurements. Process-wide; returns the
- * previous value, or -1 (and changes nothing) for any other argument. */
+ * default), 1 forces the decode GEMV wherever it applies (V^T x computed by
+ * every workgroup when V is small, else by a separate launch before it), 2
+ * forces the matrix-core GEMM, 3 forces the decode GEMV with V^T x always
+ * computed by a separate launch. Results agree within rounding in every
+ * regime; the switch exists for tests and measurements. Process-wide; returns
+ * the previous value, or -1 (and changes nothing) for any other argument. */
 int32_t wl_set_regime(int32_t regime);
 
 /* Static description of a status code. */

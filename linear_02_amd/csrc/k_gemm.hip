@@ -14,7 +14,8 @@
 //
 // Epilogue: the accumulators are scaled by s[o] (one column per lane in the
 // 32x32 output layout), then the rank-r term runs on the matrix cores as a few
-// extra K steps with A = vtx and B = U. vtx is fp32; it is split into a bf16
+// extra K steps with A = vtx and B = U. vtx (the sum, in slice order, of the
+// V^T x slice partials written by the preceding launch) is fp32; it is split into a bf16
 // head and a bf16 remainder (vtx = hi + lo up to about 2^-16 relative) and both
 // go through the MFMA, so the rank term keeps close to fp32 accuracy. Results
 // are rounded once to bf16. Pair mode (the MLP's gate/up) keeps two
@@ -164,7 +165,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Gemm g) {
                 float hi[8], lo[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float v = (t < g.T && kb + e < r) ? C.vtx[(size_t)t * r + kb + e] : 0.f;
+                    float v = 0.f;
+                    if (t < g.T && kb + e < r)
+                        for (int sl = 0; sl < C.vtx_slices; ++sl)
+                            v += C.vtx[((size_t)sl * g.T + t) * r + kb + e];
                     hi[e] = bf16_f(f_bf16(v));
                     lo[e] = v - hi[e];
                 }

@@ -1,15 +1,13 @@
-// V^T x of the low-rank delta: the inner sum over i of V[i,k] * x[t,i] in the
-// per-element expansion of the reconstruction equation ("In-kernel
-// reconstruction", reconstruction equation). Computed once per call into the
-// workspace; every output row's epilogue then reads it.
+// V^T x of the low-rank delta for the matrix-core regime: the inner sum over i
+// of V[i,k] * x[t,i] in the per-element expansion of the reconstruction formula
+// ("In-kernel reconstruction", introduction).
 //
-// Workgroup (slice, child, token block): the input axis is cut into slices so
-// that decode-sized calls (one token, a few thousand inputs) still spread over
-// many compute units. Each workgroup stages its slice of x in LDS, lets thread
-// (g, k) sum rows g, g+G, ... of the slice for rank index k, folds the G partial
-// sums through LDS and writes them out. The last workgroup of a (child, token
-// block) to arrive adds the slice partials in slice order, so the result is
-// the same whichever workgroup finishes first. No workgroup ever waits.
+// Workgroup (slice, child, token block): the input axis is cut into slices of
+// at most kVtxMaxSlice inputs, so the x slice fits in LDS and calls with few
+// tokens still spread over several compute units. Each workgroup writes the
+// slice's partial sums; the consuming kernel (launched after this one on the
+// same stream) adds the slices in slice order, so the result does not depend
+// on scheduling. There is no cross-workgroup communication inside the kernel.
 #include "wl_device.h"
 #include "wl_kernels.h"
 
@@ -19,23 +17,23 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <int TB>
 __global__ __launch_bounds__(kThreads) void vtx_kernel(VtxJob job) {
-    __shared__ u32x4 xs_raw[kVtxTok * kVtxMaxSlice / 8];
-    __shared__ float red[kThreads][kVtxTok + 1];
-    __shared__ int last;
+    __shared__ u32x4 xs_raw[TB * kVtxMaxSlice / 8];
+    __shared__ float red[kThreads][TB + 1];
 
     const int slice = blockIdx.x, c = blockIdx.y, tb = blockIdx.z;
     const int tid = threadIdx.x;
-    const int t0 = tb * kVtxTok;
-    const int tn = min(kVtxTok, job.T - t0);
+    const int t0 = tb * TB;
+    const int tn = min(TB, job.T - t0);
     const int i0 = slice * job.slice_len;
     const int len = max(0, min(job.d_in - i0, job.slice_len));
     const int nchunk = len >> 3;
 
-    // Stage x[t0 .. t0+kVtxTok)[i0 .. i0+len) as 16-byte pieces; absent tokens are zero.
+    // Stage x[t0 .. t0+TB)[i0 .. i0+len) as 16-byte pieces; absent tokens are zero.
     const u32x4 *xg = reinterpret_cast<const u32x4 *>(job.x);
     const int row_chunks = job.d_in >> 3;
-    for (int idx = tid; idx < kVtxTok * nchunk; idx += kThreads) {
+    for (int idx = tid; idx < TB * nchunk; idx += kThreads) {
         const int t = idx / nchunk, j = idx - t * nchunk;
         xs_raw[t * (kVtxMaxSlice / 8) + j] =
             t < tn ? xg[(size_t)(t0 + t) * row_chunks + (i0 >> 3) + j] : u32x4{0u, 0u, 0u, 0u};
@@ -49,57 +47,52 @@ __global__ __launch_bounds__(kThreads) void vtx_kernel(VtxJob job) {
     const int k = tid & (rp - 1), g = tid / rp, G = kThreads / rp;
     const uint16_t *__restrict__ V = job.V[c];
 
-    float acc[kVtxTok];
+    // Thread (g, k) sums rows g, g+G, ...; the V loads of 16 rows are issued
+    // before any of them is used.
+    float acc[TB];
 #pragma unroll
-    for (int t = 0; t < kVtxTok; ++t) acc[t] = 0.f;
+    for (int t = 0; t < TB; ++t) acc[t] = 0.f;
     if (k < r) {
-        for (int i = g; i < len; i += G) {
-            const float v = bf16_f(V[(size_t)(i0 + i) * r + k]);
+        for (int ib = g; ib < len; ib += 16 * G) {
+            float v[16];
 #pragma unroll
-            for (int t = 0; t < kVtxTok; ++t) acc[t] += v * bf16_f(xs[t * kVtxMaxSlice + i]);
+            for (int u = 0; u < 16; ++u) {
+                const int i = ib + u * G;
+                v[u] = i < len ? bf16_f(V[(size_t)(i0 + i) * r + k]) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int i = min(ib + u * G, len - 1);
+#pragma unroll
+                for (int t = 0; t < TB; ++t) acc[t] += v[u] * bf16_f(xs[t * kVtxMaxSlice + i]);
+            }
         }
     }
 #pragma unroll
-    for (int t = 0; t < kVtxTok; ++t) red[tid][t] = acc[t];
+    for (int t = 0; t < TB; ++t) red[tid][t] = acc[t];
     __syncthreads();
 
-    const bool single = job.n_slices == 1;
-    float *part = job.partial + ((size_t)(tb * job.n_ch + c) * job.n_slices + slice) * kVtxTok * kMaxRank;
+    // partial[c][slice][t][k]
+    float *part = job.partial[c] + (size_t)slice * job.ld_T * r;
     for (int idx = tid; idx < r * tn; idx += kThreads) {
         const int t = idx / r, kk = idx - t * r;
         float sum = 0.f;
         for (int gg = 0; gg < G; ++gg) sum += red[gg * rp + kk][t];
-        if (single)
-            job.vtx[c][(size_t)(t0 + t) * r + kk] = sum;
-        else
-            part[t * kMaxRank + kk] = sum;
+        part[(size_t)(t0 + t) * r + kk] = sum;
     }
-    if (single) return;
-
-    // Publish this slice; the last slice of the (child, token block) adds them all.
-    __threadfence();
-    __syncthreads();
-    uint32_t *cnt = job.counter + tb * job.n_ch + c;
-    if (tid == 0) last = atomicAdd(cnt, 1u) == (uint32_t)(job.n_slices - 1);
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    const float *base = job.partial + (size_t)(tb * job.n_ch + c) * job.n_slices * kVtxTok * kMaxRank;
-    for (int idx = tid; idx < r * tn; idx += kThreads) {
-        const int t = idx / r, kk = idx - t * r;
-        float sum = 0.f;
-        for (int sl = 0; sl < job.n_slices; ++sl)
-            sum += base[((size_t)sl * kVtxTok + t) * kMaxRank + kk];
-        job.vtx[c][(size_t)(t0 + t) * r + kk] = sum;
-    }
-    if (tid == 0) atomicExch(cnt, 0u);
 }
 
 }  // namespace
 
 hipError_t launch_vtx(const VtxJob &job, hipStream_t stream) {
-    const int n_tb = (job.T + kVtxTok - 1) / kVtxTok;
-    hipLaunchKernelGGL(vtx_kernel, dim3(job.n_slices, job.n_ch, n_tb), dim3(kThreads), 0, stream, job);
+    const int tb = job.T >= 8 ? 8 : job.T >= 4 ? 4 : job.T >= 2 ? 2 : 1;
+    const dim3 grid(job.n_slices, job.n_ch, (job.T + tb - 1) / tb);
+    switch (tb) {
+        case 8: hipLaunchKernelGGL(vtx_kernel<8>, grid, dim3(kThreads), 0, stream, job); break;
+        case 4: hipLaunchKernelGGL(vtx_kernel<4>, grid, dim3(kThreads), 0, stream, job); break;
+        case 2: hipLaunchKernelGGL(vtx_kernel<2>, grid, dim3(kThreads), 0, stream, job); break;
+        default: hipLaunchKernelGGL(vtx_kernel<1>, grid, dim3(kThreads), 0, stream, job); break;
+    }
     return hipGetLastError();
 }
 

@@ -18,11 +18,9 @@
 namespace {
 
 thread_local std::string g_error;
-std::atomic<int> g_regime{0};   // 0 auto, 1 GEMV, 2 matrix-core GEMM
+std::atomic<int> g_regime{0};   // 0 auto, 1 GEMV, 2 matrix-core GEMM, 3 GEMV always after a V^T x launch
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_cu_count[kMaxDevices];
 
 wl_status fail(wl_status st, const char *fmt, ...) {
     char buf[512];
@@ -43,17 +41,6 @@ wl_status ok() {
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
-
-// Compute units of the current device (cached per device).
-int cu_count() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-    int n = g_cu_count[dev].load(std::memory_order_relaxed);
-    if (n > 0) return n;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    g_cu_count[dev].store(n, std::memory_order_relaxed);
-    return n;
-}
 
 struct Range {
     const void *p;
@@ -99,70 +86,40 @@ void theta_ranges(const wl_theta *th, Range *out /* 4 */) {
 
 // ---------------------------------------------------------------------------
 // Workspace layout. One layout function serves both wl_workspace_bytes and the
-// calls, so the two always agree.
+// calls, so the two always agree. Both regimes' regions are always reserved,
+// so the size does not depend on the regime switch.
 //
-//   [0, counters)     uint32 arrival counters of the V^T x reduction; zero on
-//                     entry, zero again when the call's work has finished
-//   vtx[c]            fp32 [T][r_c] per child with r_c > 0
-//   partial           fp32 slice partials of V^T x (when the input axis is sliced)
+//   [0, 256)          reserved
+//   gemv_partial      fp32 3 x [kGemvMaxSlices][kGemvMaxTok][kMaxRank] V^T x slices
+//   vtx[c]            matrix-core regime: fp32 [n_slices][T][r_c] V^T x slice
+//                     partials per child (MLP: gate, up, down)
 //   h                 bf16 [T][d_ff] (MLP only)
 
-struct VtxPlan {
-    int n_slices = 1, slice_len = 0, n_tb = 0;
-};
+constexpr size_t kSyncBytes = 256;
 
-VtxPlan vtx_plan(int d_in, int T) {
-    VtxPlan p;
-    p.n_tb = (T + wl::kVtxTok - 1) / wl::kVtxTok;
-    int len;
-    if (T <= 64) {
-        // Few tokens: cut the input axis finely so the reduction spreads over many CUs.
-        len = (d_in + 31) / 32;
-        len = (len + 7) / 8 * 8;
-        if (len < 64) len = 64;
-    } else {
-        len = wl::kVtxMaxSlice;
-    }
-    if (len > wl::kVtxMaxSlice) len = wl::kVtxMaxSlice;
-    if (len > d_in) len = d_in;
-    p.slice_len = len;
-    p.n_slices = (d_in + len - 1) / len;
-    return p;
+int mfma_vtx_slices(int d_in) { return (d_in + wl::kVtxMaxSlice - 1) / wl::kVtxMaxSlice; }
+int mfma_vtx_slice_len(int d_in) {
+    const int n = mfma_vtx_slices(d_in);
+    return ((d_in + n - 1) / n + 7) / 8 * 8;
 }
 
 struct Layout {
-    size_t counters = 0;
-    size_t vtx[4] = {0, 0, 0, 0};   // offsets
-    size_t partial = 0;
+    size_t gemv_partial = 0;
+    size_t vtx[3] = {0, 0, 0};   // offsets
     size_t h = 0;
     size_t total = 0;
 };
 
-// thetas: children of one vtx phase (n <= 3) sharing input width d_in; extra
-// vtx slots appended for the MLP's down projection.
 Layout layout(int op, const wl_theta *const *th, int T) {
     Layout L;
-    size_t off = 0;
-    int n_ch = op == WL_OP_LINEAR ? 1 : op == WL_OP_QKV ? 3 : 2;
-    int d_in = th[0]->d_in;
-    VtxPlan vp = vtx_plan(d_in, T);
-    size_t n_counters = (size_t)vp.n_tb * n_ch;
-    size_t part_elems = vp.n_slices > 1 ? (size_t)vp.n_tb * n_ch * vp.n_slices * wl::kVtxTok * wl::kMaxRank : 0;
-    if (op == WL_OP_MLP) {
-        VtxPlan vd = vtx_plan(th[2]->d_in, T);
-        if ((size_t)vd.n_tb > n_counters) n_counters = vd.n_tb;
-        size_t pd = vd.n_slices > 1 ? (size_t)vd.n_tb * vd.n_slices * wl::kVtxTok * wl::kMaxRank : 0;
-        if (pd > part_elems) part_elems = pd;
-    }
-    L.counters = 0;
-    off = round_up(n_counters * 4, kAlign);
-    const int n_v = op == WL_OP_MLP ? 3 : n_ch;
-    for (int c = 0; c < n_v; ++c) {
+    size_t off = kSyncBytes;
+    L.gemv_partial = off;
+    off = round_up(off + wl::kMaxChildren * wl::kGemvPartialPerChild * 4, kAlign);
+    const int n = op == WL_OP_LINEAR ? 1 : 3;
+    for (int c = 0; c < n; ++c) {
         L.vtx[c] = off;
-        off = round_up(off + (size_t)T * th[c]->r * 4, kAlign);
+        off = round_up(off + (size_t)mfma_vtx_slices(th[c]->d_in) * T * th[c]->r * 4, kAlign);
     }
-    L.partial = off;
-    off = round_up(off + part_elems * 4, kAlign);
     if (op == WL_OP_MLP) {
         L.h = off;
         off = round_up(off + (size_t)T * th[0]->d_out * 2, kAlign);
@@ -178,57 +135,64 @@ wl::Child make_child(const wl_theta *th, char *ws, size_t vtx_off, int col0) {
     c.U = static_cast<const uint16_t *>(th->U);
     c.V = static_cast<const uint16_t *>(th->V);
     c.vtx = th->r > 0 ? reinterpret_cast<const float *>(ws + vtx_off) : nullptr;
+    c.vtx_slices = (th->d_in + mfma_vtx_slice_len(th->d_in) - 1) / mfma_vtx_slice_len(th->d_in);
     c.r = th->r;
     c.d_out = th->d_out;
     c.col0 = col0;
     return c;
 }
 
-// V^T x for the children with r > 0 (all sharing input x of width d_in).
-wl_status run_vtx(const wl_theta *const *th, int n, const size_t *vtx_off, const Layout &L, char *ws,
-                  const void *x, int d_in, int T, hipStream_t stream) {
+// V^T x slice partials for the children with r > 0 (all sharing input x of
+// width d_in): tokens [t0, t0 + T) of x, partial of child c at partial_c(c),
+// laid out [n_slices][ld_T][r_c].
+template <class PartialOf>
+wl_status run_vtx(const wl::Child *ch, int n, PartialOf partial_c, const void *x, int d_in, int t0, int T, int ld_T,
+                  int slice_len, hipStream_t stream) {
     wl::VtxJob job{};
-    job.x = static_cast<const uint16_t *>(x);
+    job.x = static_cast<const uint16_t *>(x) + (size_t)t0 * d_in;
     job.d_in = d_in;
     job.T = T;
+    job.ld_T = ld_T;
     for (int c = 0; c < n; ++c) {
-        if (th[c]->r == 0) continue;
-        job.V[job.n_ch] = static_cast<const uint16_t *>(th[c]->V);
-        job.vtx[job.n_ch] = reinterpret_cast<float *>(ws + vtx_off[c]);
-        job.r[job.n_ch] = th[c]->r;
+        if (ch[c].r == 0) continue;
+        job.V[job.n_ch] = ch[c].V;
+        job.partial[job.n_ch] = partial_c(c);
+        job.r[job.n_ch] = ch[c].r;
         ++job.n_ch;
     }
     if (job.n_ch == 0) return WL_OK;
-    const VtxPlan vp = vtx_plan(d_in, T);
-    job.n_slices = vp.n_slices;
-    job.slice_len = vp.slice_len;
-    job.partial = reinterpret_cast<float *>(ws + L.partial);
-    job.counter = reinterpret_cast<uint32_t *>(ws + L.counters);
+    job.slice_len = slice_len;
+    job.n_slices = (d_in + slice_len - 1) / slice_len;
     const hipError_t e = wl::launch_vtx(job, stream);
     if (e != hipSuccess) return fail(WL_ERR_HIP, "V^T x launch failed: %s", hipGetErrorString(e));
     return WL_OK;
 }
 
-bool use_gemv(int T, int d_in) {
+// Tokens per decode pass, or 0 when the matrix-core regime is to be used.
+int gemv_tokens(int T, int d_in) {
     const int regime = g_regime.load(std::memory_order_relaxed);
-    if (d_in > wl::kGemvMaxStaged) return false;
-    if (regime == 1) return true;
-    if (regime == 2) return false;
-    return T <= 8;
+    const int tt = wl::gemv_tokens_per_pass(d_in, T);
+    if (tt == 0 || regime == 2) return 0;
+    if (regime == 1 || regime == 3) return tt;
+    return T <= wl::kGemvMaxTok ? tt : 0;
 }
 
-// One projection over shared input x: children side by side in y (ldy = total width),
-// or the gate/up pair (pair = true, y = h).
+// One projection over shared input x: children side by side in y (ldy = total
+// width), or the gate/up pair (pair = true, y = h).
 wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, const void *x, void *y, int ldy,
-                   hipStream_t stream) {
-    hipError_t e;
-    const bool gemv = use_gemv(T, d_in);
+                   char *ws, const Layout &L, const size_t *vtx_off, hipStream_t stream) {
+    hipError_t e = hipSuccess;
+    const int tt = gemv_tokens(T, d_in);
     if (getenv("WL_LOG"))
-        fprintf(stderr, "wl: proj n_ch=%d pair=%d d_in=%d T=%d -> %s\n", n_ch, (int)pair, d_in, T,
-                gemv ? "gemv" : "mfma");
-    if (gemv) {
-        wl::Gemv g{};
-        for (int c = 0; c < n_ch; ++c) g.ch[c] = ch[c];
+        fprintf(stderr, "wl: proj n_ch=%d pair=%d d_in=%d T=%d -> %s (tt=%d)\n", n_ch, (int)pair, d_in, T,
+                tt ? "gemv" : "mfma", tt);
+    if (tt > 0) {
+        wl::GemvF g{};
+        int sum_r = 0;
+        for (int c = 0; c < n_ch; ++c) {
+            g.ch[c] = ch[c];
+            sum_r += ch[c].r;
+        }
         g.n_ch = n_ch;
         g.pair = pair;
         g.d_in = d_in;
@@ -241,8 +205,23 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
         g.T = T;
         g.x = static_cast<const uint16_t *>(x);
         g.y = static_cast<uint16_t *>(y);
-        e = wl::launch_gemv(g, cu_count(), stream);
+        g.partial = reinterpret_cast<float *>(ws + L.gemv_partial);
+        const bool allow_redundant = g_regime.load(std::memory_order_relaxed) != 3;
+        const wl::GemvPlan plan = wl::gemv_plan(g, tt, allow_redundant);
+        auto part = [&](int c) { return g.partial + (size_t)c * wl::kGemvPartialPerChild; };
+        for (int t0 = 0; t0 < T && e == hipSuccess; t0 += tt) {
+            g.t0 = t0;
+            if (plan.vmode == wl::kVtxPartials) {
+                const int n_tok = T - t0 < tt ? T - t0 : tt;
+                wl_status st = run_vtx(ch, n_ch, part, x, d_in, t0, n_tok, tt, plan.slice_len, stream);
+                if (st != WL_OK) return st;
+            }
+            e = wl::launch_gemv(g, plan, tt, stream);
+        }
     } else {
+        auto part = [&](int c) { return reinterpret_cast<float *>(ws + vtx_off[c]); };
+        wl_status st = run_vtx(ch, n_ch, part, x, d_in, 0, T, T, mfma_vtx_slice_len(d_in), stream);
+        if (st != WL_OK) return st;
         wl::Gemm g{};
         for (int c = 0; c < n_ch; ++c) g.ch[c] = ch[c];
         g.n_ch = n_ch;
@@ -303,7 +282,7 @@ const char *wl_status_str(wl_status st) {
 const char *wl_last_error(void) { return g_error.c_str(); }
 
 int32_t wl_set_regime(int32_t regime) {
-    if (regime < 0 || regime > 2) return -1;
+    if (regime < 0 || regime > 3) return -1;
     return g_regime.exchange(regime);
 }
 
@@ -338,9 +317,8 @@ wl_status wl_linear(const wl_theta *th, const void *x, void *y, int32_t T, void 
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     char *w = static_cast<char *>(ws);
-    if ((st = run_vtx(ths, 1, L.vtx, L, w, x, th->d_in, T, stream)) != WL_OK) return st;
     const wl::Child ch = make_child(th, w, L.vtx[0], 0);
-    if ((st = run_proj(&ch, 1, false, th->d_in, T, x, y, th->d_out, stream)) != WL_OK) return st;
+    if ((st = run_proj(&ch, 1, false, th->d_in, T, x, y, th->d_out, w, L, L.vtx, stream)) != WL_OK) return st;
     return ok();
 }
 
@@ -367,14 +345,13 @@ wl_status wl_qkv_fused(const wl_theta *q, const wl_theta *k, const wl_theta *v, 
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     char *w = static_cast<char *>(ws);
-    if ((st = run_vtx(ths, 3, L.vtx, L, w, x, q->d_in, T, stream)) != WL_OK) return st;
     wl::Child ch[3];
     int col0 = 0;
     for (int c = 0; c < 3; ++c) {
         ch[c] = make_child(ths[c], w, L.vtx[c], col0);
         col0 += ths[c]->d_out;
     }
-    if ((st = run_proj(ch, 3, false, q->d_in, T, x, y_qkv, (int)width, stream)) != WL_OK) return st;
+    if ((st = run_proj(ch, 3, false, q->d_in, T, x, y_qkv, (int)width, w, L, L.vtx, stream)) != WL_OK) return st;
     return ok();
 }
 
@@ -404,16 +381,11 @@ wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta 
     char *w = static_cast<char *>(ws);
     void *h = w + L.h;
     const int d_ff = gate->d_out;
-    // gate/up -> h = bf16(gelu_tanh(g) * u)
-    if ((st = run_vtx(ths, 2, L.vtx, L, w, x, gate->d_in, T, stream)) != WL_OK) return st;
-    wl::Child gu[2] = {make_child(gate, w, L.vtx[0], 0), make_child(up, w, L.vtx[1], 0)};
-    if ((st = run_proj(gu, 2, true, gate->d_in, T, x, h, d_ff, stream)) != WL_OK) return st;
-    // down over h
-    const wl_theta *dn[1] = {down};
-    const size_t dn_off[1] = {L.vtx[2]};
-    if ((st = run_vtx(dn, 1, dn_off, L, w, h, d_ff, T, stream)) != WL_OK) return st;
+    // gate/up -> h = bf16(gelu_tanh(g) * u), then down over h
+    const wl::Child gu[2] = {make_child(gate, w, L.vtx[0], 0), make_child(up, w, L.vtx[1], 0)};
+    if ((st = run_proj(gu, 2, true, gate->d_in, T, x, h, d_ff, w, L, L.vtx, stream)) != WL_OK) return st;
     const wl::Child dc = make_child(down, w, L.vtx[2], 0);
-    if ((st = run_proj(&dc, 1, false, d_ff, T, h, y, down->d_out, stream)) != WL_OK) return st;
+    if ((st = run_proj(&dc, 1, false, d_ff, T, h, y, down->d_out, w, L, L.vtx + 2, stream)) != WL_OK) return st;
     return ok();
 }
 

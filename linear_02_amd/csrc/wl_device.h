@@ -25,13 +25,18 @@ __device__ __forceinline__ uint16_t f_bf16(float v) {
 }
 
 // acc + dot of two 16-byte pieces (8 bf16 each); products are exact in fp32
-// and are added into the fp32 accumulator.
+// and are added into the fp32 accumulator. The components are named one by
+// one: bit-casting a subscripted vector element inside an unrolled loop
+// (bit_cast(bf16x2, w[j])) reads element 0 for every j with this compiler.
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, x), acc,
+                                           false);
+}
 __device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float acc) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]),
-                                              __builtin_bit_cast(bf16x2, x[j]), acc, false);
-    return acc;
+    acc = dot2(w.x, x.x, acc);
+    acc = dot2(w.y, x.y, acc);
+    acc = dot2(w.z, x.z, acc);
+    return dot2(w.w, x.w, acc);
 }
 
 template <int ctrl, int row_mask = 0xF, bool bound_ctrl = true>

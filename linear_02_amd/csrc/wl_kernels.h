@@ -21,52 +21,73 @@ struct Child {
     const float *s;       // fp32 [d_out], or null: every s[o] is 1
     const uint16_t *U;    // bf16 [d_out][r]  (r > 0)
     const uint16_t *V;    // bf16 [d_in][r]   (r > 0)
-    const float *vtx;     // fp32 [T][r]: V^T x of this child (workspace); r > 0
+    const float *vtx;     // matrix-core regime: V^T x slice partials, fp32 [vtx_slices][T][r]
+    int vtx_slices;       //   (their sum over slices, in order, is vtx[t][k])
     int r, d_out, col0;
 };
 
 // ---------------------------------------------------------------------------
-// V^T x for up to three children that share one input x.
-//   vtx[c][t][k] = sum_i V_c[i][k] * x[t][i]         (fp32)
-// The input axis is cut into n_slices slices; each workgroup reduces one slice
-// for one child and a block of tokens, writes its partial sums, and the last
-// workgroup of that (child, token block) to finish adds the partials in slice
-// order (deterministic). counter[] must be zero on entry and is zero again when
-// the kernel has finished.
+// V^T x slice partials for up to three children that share one input x
+// (matrix-core regime):
+//   partial[c][slice][t][k] = sum over the slice's inputs i of V_c[i][k] * x[t][i]
+// Plain stores; the consumer, launched after on the same stream, adds the
+// slices in order.
 struct VtxJob {
     const uint16_t *x;                 // bf16 [T][d_in]
     const uint16_t *V[kMaxChildren];   // bf16 [d_in][r_c]
-    float *vtx[kMaxChildren];          // fp32 [T][r_c]
+    float *partial[kMaxChildren];      // fp32 [n_slices][ld_T][r_c]
     int r[kMaxChildren];
     int n_ch, d_in, T;
-    int n_slices, slice_len;           // slice_len: multiple of 8, n_slices*slice_len >= d_in
-    float *partial;                    // fp32 [n_tb][n_ch][n_slices][kVtxTok][kMaxRank]
-    uint32_t *counter;                 // [n_tb][n_ch]
+    int ld_T;                          // tokens per slice block of partial (>= T)
+    int n_slices, slice_len;           // slice_len: multiple of 8, <= kVtxMaxSlice
 };
-constexpr int kVtxTok = 8;             // tokens per workgroup
 constexpr int kVtxMaxSlice = 1024;     // input elements per slice (x slice staged in LDS)
 hipError_t launch_vtx(const VtxJob &job, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
-// Decode-sized GEMV over the concatenated rows of up to three children:
+// Decode-sized projection, one launch per pass of tt <= 8 tokens [t0, t0 + tt):
 //   y[t][col0_c + o] = bf16( s_c[o] * sum_i W0_c[o][i] x[t][i] + sum_k U_c[o][k] vtx_c[t][k] )
-// for tokens [t0, t0 + tt) of one pass (tt <= kGemvTok).
-// Pair mode (the MLP's gate/up): ch[0] = gate, ch[1] = up with equal shapes, and
+// over the concatenated rows of up to three children. Pair mode (the MLP's
+// gate/up): ch[0] = gate, ch[1] = up with equal shapes, and
 //   y[t][o] = bf16( gelu_tanh(gate value) * up value ).
-struct Gemv {
+// vtx comes either from every workgroup reading V itself (kVtxRedundant) or
+// from slice partials written by a V^T x launch just before (kVtxPartials).
+enum { kVtxNone = 0, kVtxRedundant = 1, kVtxPartials = 2 };
+constexpr int kGemvMaxTok = 8;                // tokens per pass
+constexpr int kGemvMaxDin = 32768;            // widest input of the decode kernel
+constexpr int kGemvMaxSlices = 64;
+constexpr size_t kGemvPartialPerChild = (size_t)kGemvMaxSlices * kGemvMaxTok * kMaxRank;
+constexpr int kRedMaxTok = 2;                 // redundant V^T x: at most 2 tokens per pass
+constexpr int kRedMaxPieces = 20;             //   and 20 16-byte pieces of V per lane
+constexpr int kRedUnits = 4;                  //   one unit per wave
+
+struct GemvF {
     Child ch[kMaxChildren];
     int n_ch;
     int pair;             // 1: gate/up pair mode
     int d_in;
-    int rows;             // total output rows (sum of d_out; d_ff in pair mode)
+    int rows;             // output rows (sum of d_out; d_ff in pair mode)
     int ldy;              // row stride of y (elements)
-    int T;
+    int T, t0;            // all tokens, first token of this pass
     const uint16_t *x;    // bf16 [T][d_in]
     uint16_t *y;          // bf16 [T][ldy]
+    float *partial;       // slice partials, child c at c * kGemvPartialPerChild: fp32 [S][tt][r_c]
+    // set from the plan
+    int nseg;             // segments per row (1, 2 or 4)
+    int S;                // slices of the partials
+    int vmode;            // kVtxNone / kVtxRedundant / kVtxPartials
+    int red_units;        // redundant mode: unit u = rows [red_lo, red_hi) of 16-byte
+    int red_c[kRedUnits], red_kc[kRedUnits], red_lo[kRedUnits], red_hi[kRedUnits];   // column red_kc of child red_c
 };
-constexpr int kGemvTok = 4;                   // tokens per pass
-constexpr int kGemvMaxStaged = 32768;         // tt * d_in elements staged in LDS (64 KiB)
-hipError_t launch_gemv(const Gemv &g, int n_cu, hipStream_t stream);
+struct GemvPlan {
+    int nseg = 1, R = 1, n_wg = 1, S = 0, slice_len = 0, vmode = kVtxNone, red_units = 0;
+    int red_c[kRedUnits] = {0, 0, 0, 0}, red_kc[kRedUnits] = {0, 0, 0, 0};
+    int red_lo[kRedUnits] = {0, 0, 0, 0}, red_hi[kRedUnits] = {0, 0, 0, 0};
+};
+int gemv_tokens_per_pass(int d_in, int T);
+int gemv_slice_len(int d_in);
+GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_redundant);
+hipError_t launch_gemv(const GemvF &g, const GemvPlan &plan, int tt, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Matrix-core GEMM for larger token counts, same result as Gemv (including pair

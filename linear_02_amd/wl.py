@@ -108,10 +108,9 @@ def workspace_bytes(op: int, thetas: list, T: int) -> int:
 
 
 class Workspace:
-    """A zero-filled device workspace per (device, stream) that grows on demand.
+    """A device workspace per (device, stream) that grows on demand.
 
-    Calls on one stream run in order, so they can share one workspace; every call
-    leaves it fit for the next (its counters are zero again)."""
+    Calls on one stream run in order, so they can share one workspace."""
 
     def __init__(self):
         self._bufs: dict = {}
@@ -190,11 +189,15 @@ def wl_materialize_weff(th: dict, W_eff: torch.Tensor | None = None):
     return W_eff
 
 
+REGIME_AUTO, REGIME_GEMV, REGIME_MFMA, REGIME_GEMV_TWO_LAUNCH = 0, 1, 2, 3
+
+
 def set_regime(regime: int) -> int:
-    """0 auto, 1 GEMV, 2 matrix-core GEMM; returns the previous setting."""
+    """0 auto, 1 decode GEMV, 2 matrix-core GEMM, 3 decode GEMV always after a
+    separate V^T x launch; returns the previous setting."""
     prev = int(lib.wl_set_regime(regime))
     if prev < 0:
-        raise ValueError(f"regime {regime} is not 0, 1 or 2")
+        raise ValueError(f"regime {regime} is not 0, 1, 2 or 3")
     return prev
 
 

@@ -5,8 +5,14 @@ Floating-point outputs pass when, over the whole output tensor of a call,
 and for every element
   |y_gpu - y_oracle| <= 8e-3 * bound,
 bound being the oracle's magnitude bound |s| sum|W0 x| + sum|U vtx| (for W_eff:
-|s W0| + sum|U V|). One bf16 rounding of the output costs at most 2^-9 relative,
-inside both bars; fp32 accumulation adds orders of magnitude less.
+|s W0| + sum|U V|). One bf16 rounding of the output costs at most half a unit in
+the last of bf16's 8 significant bits, 2^-8 of |y| at worst, inside the
+per-element bar since |y| <= bound; fp32 accumulation adds orders of magnitude
+less.
+relL2 is a statistical bar: a single correctly rounded bf16 value can carry a
+relative error of 2^-8, above 2e-3, so for outputs of fewer than
+MIN_REL_L2_ELEMS elements only the per-element bar applies. Over larger outputs
+the rounding error averages to about 1.6e-3.
 Integer-valued cases are compared bit for bit.
 """
 from __future__ import annotations
@@ -16,6 +22,7 @@ import torch
 
 REL_L2 = 2e-3
 ELEM = 8e-3
+MIN_REL_L2_ELEMS = 256
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
@@ -32,7 +39,8 @@ def check(y_gpu: torch.Tensor, y_ref: np.ndarray, bound: np.ndarray, what: str =
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = np.where(bound > 0, np.abs(diff) / bound, np.where(diff == 0, 0.0, np.inf))
     worst = float(ratio.max()) if ratio.size else 0.0
-    assert rel <= REL_L2, f"{what}: relL2 {rel:.3e} > {REL_L2}"
+    if y_ref.size >= MIN_REL_L2_ELEMS:
+        assert rel <= REL_L2, f"{what}: relL2 {rel:.3e} > {REL_L2}"
     assert worst <= ELEM, f"{what}: max |err|/bound {worst:.3e} > {ELEM} at {np.unravel_index(ratio.argmax(), ratio.shape)}"
     return dict(rel_l2=rel, max_err_over_bound=worst)
 

@@ -4,7 +4,8 @@ Every call goes through the C ABI (linear_02_amd.wl -> libwl.so). Floating-point
 cases must meet relL2 <= 2e-3 and |err| <= 8e-3 * bound per element; cases with
 small-integer inputs, whose every partial sum is exact in fp32 and whose outputs
 are exact in bf16, must match bit for bit. Both kernel regimes (wave-per-row GEMV
-and matrix-core GEMM) are run on the same cases.
+with V^T x in the same launch or in a launch of its own, and matrix-core GEMM)
+are run on the same cases.
 """
 from __future__ import annotations
 
@@ -32,9 +33,9 @@ def wl():
     return mod
 
 
-@pytest.fixture(params=["gemv", "mfma"])
+@pytest.fixture(params=["gemv", "mfma", "gemv2"])
 def regime(request, wl):
-    prev = wl.set_regime({"gemv": 1, "mfma": 2}[request.param])
+    prev = wl.set_regime({"gemv": 1, "mfma": 2, "gemv2": 3}[request.param])
     yield request.param
     wl.set_regime(prev)
 
@@ -284,3 +285,33 @@ def test_small_workspace_raises_and_nothing_breaks(wl, orc):
     assert e.value.status == 4
     y_ref, bound = orc.linear(th, x)
     check(wl.wl_linear(dth, xd), y_ref, bound, "after error")
+
+
+# -- the decode kernel's in-kernel V^T x handoff ----------------------------------------------
+
+@pytest.mark.parametrize("op", ["qkv", "mlp"])
+def test_decode_handoff_repeats_bitwise(wl, orc, op):
+    # Hundreds of back-to-back launches with no host synchronization in between:
+    # every result must carry the same bits as the first and meet the oracle.
+    g = gen(600)
+    dims = inputs.GEMMA3_1B
+    lay = inputs.layer(g, dims, 32)
+    x = inputs.activations(g, 1, dims["d_model"])
+    dl = {f: dev(lay[f]) for f in lay}
+    xd = x.to(DEV)
+    n = 300
+    if op == "qkv":
+        out = torch.empty(n, dims["q"] + 2 * dims["kv"], dtype=torch.bfloat16, device=DEV)
+        for i in range(n):
+            wl.wl_qkv_fused(dl["q"], dl["k"], dl["v"], xd, y=out[i:i + 1])
+        y_ref, bound = orc.qkv(lay["q"], lay["k"], lay["v"], x)
+    else:
+        out = torch.empty(n, dims["d_model"], dtype=torch.bfloat16, device=DEV)
+        for i in range(n):
+            wl.wl_mlp_fused(dl["gate"], dl["up"], dl["down"], xd, y=out[i:i + 1])
+        y_ref, bound, _ = orc.mlp(lay["gate"], lay["up"], lay["down"], x)
+    torch.cuda.synchronize()
+    bits = out.view(torch.int16)
+    same = (bits == bits[0:1]).all(dim=1)
+    assert bool(same.all()), f"{int((~same).sum())} of {n} launches differ from the first"
+    check(out[0:1], y_ref, bound, f"{op} repeated")
