@@ -1,25 +1,42 @@
-// Matrix-core path for larger token counts (prefill-sized calls).
+// Matrix-core path for larger token counts (prefill-sized calls), one launch.
 //
-//   m[t,o]  = sum_i x[t,i] W0[o,i]                  bf16 x bf16 -> fp32 on MFMA
-//   y[t,o]  = bf16( s[o] * m[t,o] + sum_k vtx[t,k] U[o,k] )
+//   m[t,o]   = sum_i x[t,i] W0[o,i]                 bf16 x bf16 -> fp32 on MFMA
+//   vtx[t,k] = sum_i x[t,i] V[i,k]                  same x tiles, same MFMA
+//   y[t,o]   = bf16( s[o] * m[t,o] + sum_k vtx[t,k] U[o,k] )
 //
-// ("In-kernel reconstruction", reconstruction equation and its GEMM form:
-// s scales the W0 product, the rank-r term is added unscaled.)
+// ("In-kernel reconstruction", introduction: the reconstruction formula and its
+// per-element expansion; s scales the W0 product, the rank-r term is added
+// unscaled.)
 //
-// Both operands are contiguous along the input axis (x[T][d_in], W0[d_out][d_in]),
-// so tiles go straight from global memory into LDS as 16-byte pieces without
-// any transpose. A workgroup owns a 128-token x 128-output tile; its four waves
-// each own 64 x 64 of it as a 2 x 2 grid of 32x32x16 bf16 MFMAs. The input
-// axis is walked 32 at a time through double-buffered LDS tiles.
+// Operands. x[T][d_in] and W0[d_out][d_in] are contiguous along the input axis,
+// so their tiles go to LDS as 16-byte pieces without any transpose. A
+// workgroup of WM x WN waves owns a BM x BN output tile (tokens x outputs);
+// each wave owns TM x TN 32x32 blocks, each the accumulator of one
+// v_mfma_f32_32x32x16_bf16 chain. The input axis is walked BK at a time through
+// a ring of D LDS stages filled by direct-to-LDS loads (global_load_lds, 16
+// bytes per lane, no registers), D-1 stages in flight while one is multiplied.
+// LDS rows of BK bf16 keep their 16-byte pieces XOR-swizzled by the row index
+// so that the fragment reads are free of bank conflicts.
 //
-// Epilogue: the accumulators are scaled by s[o] (one column per lane in the
-// 32x32 output layout), then the rank-r term runs on the matrix cores as a few
-// extra K steps with A = vtx and B = U. vtx (the sum, in slice order, of the
-// V^T x slice partials written by the preceding launch) is fp32; it is split into a bf16
-// head and a bf16 remainder (vtx = hi + lo up to about 2^-16 relative) and both
-// go through the MFMA, so the rank term keeps close to fp32 accuracy. Results
-// are rounded once to bf16. Pair mode (the MLP's gate/up) keeps two
-// accumulator sets over the same x tile and writes bf16(gelu_tanh(g) * u).
+// V^T x rides along: each stage also carries the matching BK rows of V (its
+// natural layout, rank-contiguous), and the waves multiply the x fragments
+// they already hold by V fragments gathered from LDS, splitting the K steps
+// among the WN waves of a workgroup row; the WN partial results are added in
+// wave order in the epilogue, so vtx never depends on scheduling. This costs
+// about 1/WN of one extra MFMA per K step per 32 ranks and needs no separate
+// launch and no workspace.
+//
+// Workgroups are numbered so that each of the 8 XCDs (which take workgroups
+// round-robin) works through its own contiguous band of output tiles, keeping
+// the W0 rows it reads in its own L2.
+//
+// Epilogue: the accumulators are scaled by s[o] (one output column per lane in
+// the 32x32 layout); vtx is staged in LDS, split into a bf16 head and a bf16
+// remainder (vtx = hi + lo to about 2^-16 relative) and both are run against U
+// on the matrix cores as extra K steps, so the rank term keeps close to fp32
+// accuracy. Results are rounded once to bf16. Pair mode (the MLP's gate/up)
+// keeps two accumulator sets over the same x tile and writes
+// bf16(gelu_tanh(g) * u).
 #include "wl_device.h"
 #include "wl_kernels.h"
 
@@ -27,183 +44,326 @@ namespace wl {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int LDC = BK / 8 + 1;          // 16-byte pieces per LDS row (one of padding)
-
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return (uint32_t)f_bf16(a) | ((uint32_t)f_bf16(b) << 16);
+}
 __device__ __forceinline__ u32x4 pack8(const float (&v)[8]) {
     u32x4 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        r[j] = (uint32_t)f_bf16(v[2 * j]) | ((uint32_t)f_bf16(v[2 * j + 1]) << 16);
+    r.x = pack2(v[0], v[1]);
+    r.y = pack2(v[2], v[3]);
+    r.z = pack2(v[4], v[5]);
+    r.w = pack2(v[6], v[7]);
     return r;
 }
 
-// Tile coordinates of workgroup blockIdx.x over the children's output tiles.
-__device__ __forceinline__ int tile_child(const Gemm &g, int bx, int &n0) {
-    int c = 0;
-    int left = bx;
-    for (; c < g.n_ch - 1; ++c) {
-        const int nt = (g.ch[c].d_out + BN - 1) / BN;
-        if (left < nt) break;
-        left -= nt;
-    }
-    n0 = left * BN;
-    return c;
+template <int WM, int WN, int TM, int TN, int BK, int P, int D, int NV>
+struct Cfg {
+    static constexpr int kThreads = WM * WN * kWave;
+    static constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+    static constexpr int KP = BK / 8;                          // 16-byte pieces per LDS row
+    static constexpr int A_PIECES = BM * KP, B_PIECES = BN * KP;
+    static constexpr int V_PIECES = BK * NV * 32 * 2 / 16;      // BK rows of V, up to NV*32 ranks
+    static constexpr int A_PER = A_PIECES / kThreads, B_PER = B_PIECES / kThreads;
+    static constexpr int V_PER = (V_PIECES + kThreads - 1) / kThreads;
+    static constexpr int STAGE_PIECES = A_PIECES + P * (B_PIECES + V_PIECES);
+    static constexpr int PER_STAGE = A_PER + P * (B_PER + V_PER);   // direct-to-LDS loads per thread
+    static constexpr int TILE_PIECES = D * STAGE_PIECES;
+    static constexpr int VT_LD = kMaxRank + 4;                 // fp32 row stride of the epilogue vtx
+    static constexpr int VT_PIECES = NV > 0 ? P * BM * VT_LD * 4 / 16 : 0;
+    static constexpr int LDS_PIECES = TILE_PIECES > VT_PIECES ? TILE_PIECES : VT_PIECES;
+    static_assert(A_PIECES % kThreads == 0 && B_PIECES % kThreads == 0, "tile pieces must split evenly");
+    static_assert(D >= 2 && D <= 4 && (D - 1) * PER_STAGE <= 63, "stages in flight must fit vmcnt");
+    static_assert((BK / 16) % WN == 0, "V^T x K steps must split evenly over the WN waves");
+};
+
+// Swizzled position of piece kc of LDS row `row` (rows of KP pieces). The XOR
+// pattern varies over 16 consecutive rows, so the 16 lanes that one LDS pass
+// serves (32 rows x one piece per fragment read) land on distinct 4-bank
+// groups of the 64 banks.
+template <int KP>
+__device__ __forceinline__ int swz_key(int row) {
+    constexpr int sh = KP == 8 ? 0 : KP == 4 ? 1 : 2;
+    return ((row >> sh) ^ (row >> 3)) & (KP - 1);
+}
+template <int KP>
+__device__ __forceinline__ int swz(int row, int kc) {
+    return row * KP + (kc ^ swz_key<KP>(row));
 }
 
-template <int P>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(Gemm g) {
-    __shared__ u32x4 As[2][BM * LDC];
-    __shared__ u32x4 Bs[2][P][BN * LDC];
+// A 16-byte piece of zeros: the source of every out-of-range piece of a
+// direct-to-LDS tile load (the load always writes its LDS slot).
+__device__ __attribute__((aligned(16))) const uint32_t kZeroPiece[4] = {0u, 0u, 0u, 0u};
+
+// One direct-to-LDS load: the wave's 64 lanes each fetch 16 bytes from their
+// own global address into 64 consecutive 16-byte LDS slots starting at dst.
+__device__ __forceinline__ void lds_dma16(const u32x4 *src, u32x4 *dst) {
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int WM, int WN, int TM, int TN, int BK, int P, int D, int NV>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(Gemm g) {
+    using C = Cfg<WM, WN, TM, TN, BK, P, D, NV>;
+    constexpr int BM = C::BM, BN = C::BN, KP = C::KP, NT = C::kThreads;
+    constexpr int NVA = NV > 0 ? NV : 1;
+    __shared__ u32x4 lds[C::LDS_PIECES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
-    int n0;
-    const int cidx = P == 2 ? 0 : tile_child(g, blockIdx.x, n0);
-    if (P == 2) n0 = blockIdx.x * BN;
-    const Child &C0 = P == 2 ? g.ch[0] : (cidx == 0 ? g.ch[0] : cidx == 1 ? g.ch[1] : g.ch[2]);
+    const int wm = wave % WM, wn = wave / WM;
+
+    // Tile numbering: XCD x (blockIdx % 8) takes a contiguous band of logical tiles.
+    int n_nt = 0;
+    if (g.pair)
+        n_nt = (g.ch[0].d_out + BN - 1) / BN;
+    else
+        for (int c = 0; c < g.n_ch; ++c) n_nt += (g.ch[c].d_out + BN - 1) / BN;
+    const int n_mt = (g.T + BM - 1) / BM;
+    const int total = n_nt * n_mt;
+    int tile;
+    {
+        const int per = (total + 7) / 8, x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        const int full = total - 8 * (per - 1);   // XCDs 0..full-1 hold `per` tiles, the rest per-1
+        tile = x < full ? x * per + slot : full * per + (x - full) * (per - 1) + slot;
+    }
+    // Within the band: token tiles fastest, so consecutive tiles share W0 rows.
+    const int mt = tile % n_mt, ntile = tile / n_mt;
+    int cidx = 0, n0 = ntile * BN;
+    if (!g.pair) {
+        int left = ntile;
+        for (; cidx < g.n_ch - 1; ++cidx) {
+            const int nt = (g.ch[cidx].d_out + BN - 1) / BN;
+            if (left < nt) break;
+            left -= nt;
+        }
+        n0 = left * BN;
+    }
+    const Child &C0 = g.ch[cidx];
     const int d_out = C0.d_out;
-    const int m0 = blockIdx.y * BM;
+    const int m0 = mt * BM;
     const int d_in = g.d_in, nch = d_in >> 3;
     const int nk = (d_in + BK - 1) / BK;
 
     const u32x4 *xg = reinterpret_cast<const u32x4 *>(g.x);
-    const u32x4 *wg[P];
+    const Child *ch[P];
 #pragma unroll
-    for (int p = 0; p < P; ++p) wg[p] = reinterpret_cast<const u32x4 *>((P == 2 ? g.ch[p] : C0).W0);
+    for (int p = 0; p < P; ++p) ch[p] = &g.ch[P == 2 ? p : cidx];
 
-    // Global -> register staging: two 16-byte pieces per thread per operand tile.
-    u32x4 ra[2], rb[2][P];
-    auto load_tile = [&](int kt) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int q = tid + kThreads * h;
-            const int row = q >> 2, kc = kt * (BK / 8) + (q & 3);
-            const bool kin = kc < nch;
-            ra[h] = (kin && m0 + row < g.T) ? xg[(size_t)(m0 + row) * nch + kc] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int p = 0; p < P; ++p)
-                rb[h][p] = (kin && n0 + row < d_out) ? __builtin_nontemporal_load(wg[p] + (size_t)(n0 + row) * nch + kc)
-                                                     : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int q = tid + kThreads * h;
-            const int row = q >> 2, kc = q & 3;
-            As[buf][row * LDC + kc] = ra[h];
-#pragma unroll
-            for (int p = 0; p < P; ++p) Bs[buf][p][row * LDC + kc] = rb[h][p];
-        }
-    };
-
-    f32x16 acc[P][2][2];
+    f32x16 acc[P][TM][TN];
+    f32x16 accv[P][TM][NVA];
 #pragma unroll
     for (int p = 0; p < P; ++p)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TM; ++i) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[p][i][j][e] = 0.f;
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    const int fr = lane & 31, fk = lane >> 5;   // fragment row / column, K half
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load_tile(kt + 1);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int kc = 2 * s + fk;
-            u32x4 a[2], b[P][2];
+            for (int v = 0; v < NVA; ++v)
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = As[buf][(wm * 64 + i * 32 + fr) * LDC + kc];
-#pragma unroll
-            for (int p = 0; p < P; ++p)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) b[p][j] = Bs[buf][p][(wn * 64 + j * 32 + fr) * LDC + kc];
-#pragma unroll
-            for (int p = 0; p < P; ++p)
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) acc[p][i][j] = mfma(a[i], b[p][j], acc[p][i][j]);
+                for (int e = 0; e < 16; ++e) accv[p][i][v][e] = 0.f;
         }
-        if (kt + 1 < nk) store_tile(buf ^ 1);
-        __syncthreads();
+
+    // The ring: the 64 lanes of one load write 64 consecutive 16-byte LDS slots,
+    // so each lane fetches the global piece that belongs in its (swizzled) slot.
+    const u32x4 *zero = reinterpret_cast<const u32x4 *>(kZeroPiece);
+    auto issue = [&](int kt, int sl) {
+        u32x4 *st = lds + sl * C::STAGE_PIECES;
+#pragma unroll
+        for (int h = 0; h < C::A_PER; ++h) {
+            const int q = h * NT + tid, row = q / KP, kc = (q % KP) ^ swz_key<KP>(row), gk = kt * KP + kc;
+            const u32x4 *src = (gk < nch && m0 + row < g.T) ? xg + (size_t)(m0 + row) * nch + gk : zero;
+            lds_dma16(src, st + h * NT + wave * kWave);
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const u32x4 *wgp = reinterpret_cast<const u32x4 *>(ch[p]->W0);
+            u32x4 *bst = st + C::A_PIECES + p * (C::B_PIECES + C::V_PIECES);
+#pragma unroll
+            for (int h = 0; h < C::B_PER; ++h) {
+                const int q = h * NT + tid, row = q / KP, kc = (q % KP) ^ swz_key<KP>(row), gk = kt * KP + kc;
+                const u32x4 *src = (gk < nch && n0 + row < d_out) ? wgp + (size_t)(n0 + row) * nch + gk : zero;
+                lds_dma16(src, bst + h * NT + wave * kWave);
+            }
+            if constexpr (NV > 0) {
+                // V rows [kt*BK, kt*BK + BK): BK*r bf16, contiguous, copied as they are.
+                const int r = ch[p]->r;
+                const u32x4 *vg = reinterpret_cast<const u32x4 *>(ch[p]->V);
+                const int q_end = BK * r / 8, q_all = d_in * r / 8, q0 = kt * BK * r / 8;
+#pragma unroll
+                for (int h = 0; h < C::V_PER; ++h) {
+                    const int q = h * NT + tid;
+                    const u32x4 *src = (q < q_end && q0 + q < q_all) ? vg + q0 + q : zero;
+                    lds_dma16(src, bst + C::B_PIECES + h * NT + wave * kWave);
+                }
+            }
+        }
+    };
+
+    const int fr = lane & 31, fk = lane >> 5;   // fragment row / column, K half of a 16-step
+    auto compute = [&](const u32x4 *st) {
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            const int kc = 2 * s + fk;
+            u32x4 a[TM], b[P][TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) a[i] = st[swz<KP>(wm * TM * 32 + i * 32 + fr, kc)];
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    b[p][j] = st[C::A_PIECES + p * (C::B_PIECES + C::V_PIECES) + swz<KP>(wn * TN * 32 + j * 32 + fr, kc)];
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) acc[p][i][j] = mfma(a[i], b[p][j], acc[p][i][j]);
+            if constexpr (NV > 0) {
+                if (s % WN == wn) {
+                    // V fragment: lane (fr, fk) needs V[i][k] for the 8 stage rows
+                    // i = 16s + 8fk + e and rank k = 32v + fr.
+#pragma unroll
+                    for (int p = 0; p < P; ++p) {
+                        const int r = ch[p]->r;
+                        const uint16_t *vl = reinterpret_cast<const uint16_t *>(
+                            st + C::A_PIECES + p * (C::B_PIECES + C::V_PIECES) + C::B_PIECES);
+#pragma unroll
+                        for (int v = 0; v < NV; ++v) {
+                            const int k = 32 * v + fr;
+                            u32x4 vf = {0u, 0u, 0u, 0u};
+                            if (k < r) {
+                                const uint16_t *col = vl + (16 * s + 8 * fk) * r + k;
+                                vf.x = (uint32_t)col[0] | ((uint32_t)col[r] << 16);
+                                vf.y = (uint32_t)col[2 * r] | ((uint32_t)col[3 * r] << 16);
+                                vf.z = (uint32_t)col[4 * r] | ((uint32_t)col[5 * r] << 16);
+                                vf.w = (uint32_t)col[6 * r] | ((uint32_t)col[7 * r] << 16);
+                            }
+#pragma unroll
+                            for (int i = 0; i < TM; ++i) accv[p][i][v] = mfma(a[i], vf, accv[p][i][v]);
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    for (int s0 = 0; s0 < D - 1 && s0 < nk; ++s0) issue(s0, s0);
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + D - 1 < nk) issue(kt + D - 1, (kt + D - 1) % D);
+        // Wait for this wave's loads of stage kt: the later stages may stay in flight.
+        const int ahead = min(D - 1, nk - 1 - kt);
+        if (ahead >= 3) wait_vm<3 * C::PER_STAGE>();
+        else if (ahead == 2) wait_vm<2 * C::PER_STAGE>();
+        else if (ahead == 1) wait_vm<C::PER_STAGE>();
+        else wait_vm<0>();
+        barrier();                                    // every wave's part of stage kt has landed
+        compute(lds + (kt % D) * C::STAGE_PIECES);
+        barrier();                                    // slot kt % D is free for reuse
     }
 
-    // Epilogue. Lane (fr, fk) of output tile (i, j) holds column o = n0 + wn*64 + j*32 + fr
-    // and rows m0 + wm*64 + i*32 + 8*(e/4) + 4*fk + (e%4), e = 0..15.
+    // ---- epilogue ----
+    // Lane (fr, fk) of block (i, j) holds output column o = n0 + (wn*TN + j)*32 + fr
+    // and token rows m0 + (wm*TM + i)*32 + 8*(e/4) + 4*fk + (e%4), e = 0..15.
+    if constexpr (NV > 0) {
+        // vtx of child p: fp32 [BM][VT_LD] at vt + p*BM*VT_LD, the WN partials added in wave
+        // order. The padded row stride puts the 16 rows one LDS pass reads on distinct banks.
+        float *vt = reinterpret_cast<float *>(lds);
+        for (int w = 0; w < WN; ++w) {
+            if (wn == w) {
+#pragma unroll
+                for (int p = 0; p < P; ++p)
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int v = 0; v < NV; ++v)
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) {
+                                const int row = (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * fk + (e & 3);
+                                float *dst = vt + (p * BM + row) * C::VT_LD + 32 * v + fr;
+                                *dst = w == 0 ? accv[p][i][v][e] : *dst + accv[p][i][v][e];
+                            }
+            }
+            barrier();
+        }
+    }
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        const Child &C = P == 2 ? g.ch[p] : C0;
+        const Child &Cp = *ch[p];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int o = n0 + wn * 64 + j * 32 + fr;
-            const float sv = (C.s && o < d_out) ? C.s[o] : 1.0f;
+        for (int j = 0; j < TN; ++j) {
+            const int o = n0 + (wn * TN + j) * 32 + fr;
+            const float sv = (Cp.s && o < d_out) ? Cp.s[o] : 1.0f;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) acc[p][i][j] *= sv;
+            for (int i = 0; i < TM; ++i) acc[p][i][j] *= sv;
         }
-        const int r = C.r;
-        for (int k0 = 0; k0 < r; k0 += 16) {
-            const int kb = k0 + 8 * fk;
-            u32x4 ahi[2], alo[2], bu[2];
+        if constexpr (NV > 0) {
+            const int r = Cp.r;
+            const float *vt = reinterpret_cast<const float *>(lds) + p * BM * C::VT_LD;
+            for (int k0 = 0; k0 < r; k0 += 16) {
+                const int kb = k0 + 8 * fk;
+                u32x4 ahi[TM], alo[TM], bu[TN];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int t = m0 + wm * 64 + i * 32 + fr;
-                float hi[8], lo[8];
+                for (int i = 0; i < TM; ++i) {
+                    // Columns up to kb + 7 < 64 are inside the row; those at or past r
+                    // (never written) are replaced by zeros.
+                    const f32x4 *row = reinterpret_cast<const f32x4 *>(vt + ((wm * TM + i) * 32 + fr) * C::VT_LD + kb);
+                    const f32x4 r0 = row[0], r1 = row[1];
+                    const float raw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+                    float hi[8], lo[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float v = 0.f;
-                    if (t < g.T && kb + e < r)
-                        for (int sl = 0; sl < C.vtx_slices; ++sl)
-                            v += C.vtx[((size_t)sl * g.T + t) * r + kb + e];
-                    hi[e] = bf16_f(f_bf16(v));
-                    lo[e] = v - hi[e];
+                    for (int e = 0; e < 8; ++e) {
+                        const float v = kb + e < r ? raw[e] : 0.f;
+                        hi[e] = bf16_f(f_bf16(v));
+                        lo[e] = v - hi[e];
+                    }
+                    ahi[i] = pack8(hi);
+                    alo[i] = pack8(lo);
                 }
-                ahi[i] = pack8(hi);
-                alo[i] = pack8(lo);
-            }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int o = n0 + wn * 64 + j * 32 + fr;
-                float u[8];
+                for (int j = 0; j < TN; ++j) {
+                    const int o = n0 + (wn * TN + j) * 32 + fr;
+                    float u[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    u[e] = (o < d_out && kb + e < r) ? bf16_f(C.U[(size_t)o * r + kb + e]) : 0.f;
-                bu[j] = pack8(u);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    acc[p][i][j] = mfma(ahi[i], bu[j], acc[p][i][j]);
-                    acc[p][i][j] = mfma(alo[i], bu[j], acc[p][i][j]);
+                    for (int e = 0; e < 8; ++e)
+                        u[e] = (o < d_out && kb + e < r) ? bf16_f(Cp.U[(size_t)o * r + kb + e]) : 0.f;
+                    bu[j] = pack8(u);
                 }
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        acc[p][i][j] = mfma(ahi[i], bu[j], acc[p][i][j]);
+                        acc[p][i][j] = mfma(alo[i], bu[j], acc[p][i][j]);
+                    }
+            }
         }
     }
 
-    const int col0 = P == 2 ? 0 : C0.col0;
+    const int col0 = g.pair ? 0 : C0.col0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int o = n0 + wn * 64 + j * 32 + fr;
+    for (int j = 0; j < TN; ++j) {
+        const int o = n0 + (wn * TN + j) * 32 + fr;
         if (o >= d_out) continue;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int t = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * fk + (e & 3);
+                const int t = m0 + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * fk + (e & 3);
                 if (t < g.T) {
                     const float v = P == 2 ? gelu_tanh(acc[0][i][j][e]) * acc[P - 1][i][j][e] : acc[0][i][j][e];
                     g.y[(size_t)t * g.ldy + col0 + o] = f_bf16(v);
@@ -212,20 +372,42 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Gemm g) {
     }
 }
 
+template <int WM, int WN, int TM, int TN, int BK, int D, int P, int NV>
+hipError_t launch_cfg(const Gemm &g, hipStream_t stream) {
+    using C = Cfg<WM, WN, TM, TN, BK, P, D, NV>;
+    int n_nt = 0;
+    if (g.pair)
+        n_nt = (g.ch[0].d_out + C::BN - 1) / C::BN;
+    else
+        for (int c = 0; c < g.n_ch; ++c) n_nt += (g.ch[c].d_out + C::BN - 1) / C::BN;
+    const int total = n_nt * ((g.T + C::BM - 1) / C::BM);
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BK, P, D, NV>), dim3(total), dim3(C::kThreads), 0, stream, g);
+    return hipGetLastError();
+}
+
+template <int WM, int WN, int TM, int TN, int BK, int D, int P>
+hipError_t launch_nv(const Gemm &g, hipStream_t stream) {
+    int max_r = 0;
+    for (int c = 0; c < (g.pair ? 2 : g.n_ch); ++c) max_r = g.ch[c].r > max_r ? g.ch[c].r : max_r;
+    if (max_r == 0) return launch_cfg<WM, WN, TM, TN, BK, D, P, 0>(g, stream);
+    if (max_r <= 32) return launch_cfg<WM, WN, TM, TN, BK, D, P, 1>(g, stream);
+    return launch_cfg<WM, WN, TM, TN, BK, D, P, 2>(g, stream);
+}
+
 }  // namespace
 
+// Tile configuration (waves M x N, 32x32 blocks per wave M x N, K depth, LDS
+// stages): chosen by measurement on the layer shapes; overridable at build time.
+#ifndef WL_GEMM_TILE
+#define WL_GEMM_TILE 2, 2, 2, 2, 64, 2
+#endif
+#ifndef WL_GEMM_TILE_PAIR
+#define WL_GEMM_TILE_PAIR 2, 2, 2, 2, 64, 2
+#endif
+
 hipError_t launch_gemm(const Gemm &g, hipStream_t stream) {
-    int ntiles = 0;
-    if (g.pair)
-        ntiles = (g.ch[0].d_out + BN - 1) / BN;
-    else
-        for (int c = 0; c < g.n_ch; ++c) ntiles += (g.ch[c].d_out + BN - 1) / BN;
-    const dim3 grid(ntiles, (g.T + BM - 1) / BM);
-    if (g.pair)
-        hipLaunchKernelGGL(gemm_kernel<2>, grid, dim3(kThreads), 0, stream, g);
-    else
-        hipLaunchKernelGGL(gemm_kernel<1>, grid, dim3(kThreads), 0, stream, g);
-    return hipGetLastError();
+    if (g.pair) return launch_nv<WL_GEMM_TILE_PAIR, 2>(g, stream);
+    return launch_nv<WL_GEMM_TILE, 1>(g, stream);
 }
 
 }  // namespace wl

@@ -389,8 +389,11 @@ GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_redundant) {
     if (sum_r == 0 || !allow_redundant || tt > kRedMaxTok) return p;
 
     // Redundant V^T x: every child's rank must be 4 or a multiple of 8, the
-    // columns (16-byte wide, or one for r == 4) at most one per wave, and each
-    // lane's share of its unit within kRedMaxPieces pieces.
+    // columns (16-byte wide, or one for r == 4) at most one per wave, each
+    // lane's share of its unit within kRedMaxPieces pieces, and the re-reads of
+    // V by all workgroups within kRedMaxTraffic bytes (measured: beyond a few MB
+    // they cost more than a separate V^T x launch).
+    if ((long long)p.n_wg * g.d_in * sum_r * 2 > kRedMaxTraffic) return p;
     int cols = 0;
     for (int c = 0; c < g.n_ch; ++c) {
         const int r = g.ch[c].r;

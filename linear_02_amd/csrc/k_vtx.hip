@@ -1,10 +1,10 @@
-// V^T x of the low-rank delta for the matrix-core regime: the inner sum over i
+// V^T x of the low-rank delta for the decode regime: the inner sum over i
 // of V[i,k] * x[t,i] in the per-element expansion of the reconstruction formula
 // ("In-kernel reconstruction", introduction).
 //
 // Workgroup (slice, child, token block): the input axis is cut into slices of
-// at most kVtxMaxSlice inputs, so the x slice fits in LDS and calls with few
-// tokens still spread over several compute units. Each workgroup writes the
+// at most kVtxMaxSlice inputs, so that calls with few tokens spread over
+// several compute units (and, for larger token blocks, the x slice fits in LDS). Each workgroup writes the
 // slice's partial sums; the consuming kernel (launched after this one on the
 // same stream) adds the slices in slice order, so the result does not depend
 // on scheduling. There is no cross-workgroup communication inside the kernel.
@@ -19,7 +19,11 @@ constexpr int kThreads = 256;
 
 template <int TB>
 __global__ __launch_bounds__(kThreads) void vtx_kernel(VtxJob job) {
-    __shared__ u32x4 xs_raw[TB * kVtxMaxSlice / 8];
+    // Up to two tokens per workgroup: every thread loads its x values straight
+    // from global memory together with its V entries (one round trip); more
+    // tokens: the x slice is staged in LDS first and shared.
+    constexpr bool kStage = TB > 2;
+    __shared__ u32x4 xs_raw[kStage ? TB * kVtxMaxSlice / 8 : 1];
     __shared__ float red[kThreads][TB + 1];
 
     const int slice = blockIdx.x, c = blockIdx.y, tb = blockIdx.z;
@@ -28,17 +32,19 @@ __global__ __launch_bounds__(kThreads) void vtx_kernel(VtxJob job) {
     const int tn = min(TB, job.T - t0);
     const int i0 = slice * job.slice_len;
     const int len = max(0, min(job.d_in - i0, job.slice_len));
-    const int nchunk = len >> 3;
 
-    // Stage x[t0 .. t0+TB)[i0 .. i0+len) as 16-byte pieces; absent tokens are zero.
-    const u32x4 *xg = reinterpret_cast<const u32x4 *>(job.x);
-    const int row_chunks = job.d_in >> 3;
-    for (int idx = tid; idx < TB * nchunk; idx += kThreads) {
-        const int t = idx / nchunk, j = idx - t * nchunk;
-        xs_raw[t * (kVtxMaxSlice / 8) + j] =
-            t < tn ? xg[(size_t)(t0 + t) * row_chunks + (i0 >> 3) + j] : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (kStage) {
+        // x[t0 .. t0+TB)[i0 .. i0+len) as 16-byte pieces; absent tokens are zero.
+        const int nchunk = len >> 3;
+        const u32x4 *xg = reinterpret_cast<const u32x4 *>(job.x);
+        const int row_chunks = job.d_in >> 3;
+        for (int idx = tid; idx < TB * nchunk; idx += kThreads) {
+            const int t = idx / nchunk, j = idx - t * nchunk;
+            xs_raw[t * (kVtxMaxSlice / 8) + j] =
+                t < tn ? xg[(size_t)(t0 + t) * row_chunks + (i0 >> 3) + j] : u32x4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
     }
-    __syncthreads();
     const uint16_t *xs = reinterpret_cast<const uint16_t *>(xs_raw);
 
     const int r = job.r[c];
@@ -47,25 +53,31 @@ __global__ __launch_bounds__(kThreads) void vtx_kernel(VtxJob job) {
     const int k = tid & (rp - 1), g = tid / rp, G = kThreads / rp;
     const uint16_t *__restrict__ V = job.V[c];
 
-    // Thread (g, k) sums rows g, g+G, ...; the V loads of 16 rows are issued
+    // Thread (g, k) sums rows g, g+G, ...; the loads of 16 rows are issued
     // before any of them is used.
     float acc[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t) acc[t] = 0.f;
     if (k < r) {
         for (int ib = g; ib < len; ib += 16 * G) {
-            float v[16];
+            float v[16], xv[16][TB];
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const int i = ib + u * G;
-                v[u] = i < len ? bf16_f(V[(size_t)(i0 + i) * r + k]) : 0.f;
+                const bool in = i < len;
+                v[u] = in ? bf16_f(V[(size_t)(i0 + i) * r + k]) : 0.f;
+#pragma unroll
+                for (int t = 0; t < TB; ++t) {
+                    if constexpr (kStage)
+                        xv[u][t] = bf16_f(xs[t * kVtxMaxSlice + min(i, len - 1)]);
+                    else
+                        xv[u][t] = (in && t < tn) ? bf16_f(job.x[(size_t)(t0 + t) * job.d_in + i0 + i]) : 0.f;
+                }
             }
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int i = min(ib + u * G, len - 1);
+            for (int u = 0; u < 16; ++u)
 #pragma unroll
-                for (int t = 0; t < TB; ++t) acc[t] += v[u] * bf16_f(xs[t * kVtxMaxSlice + i]);
-            }
+                for (int t = 0; t < TB; ++t) acc[t] += v[u] * xv[u][t];
         }
     }
 #pragma unroll

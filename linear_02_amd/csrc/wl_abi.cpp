@@ -86,40 +86,27 @@ void theta_ranges(const wl_theta *th, Range *out /* 4 */) {
 
 // ---------------------------------------------------------------------------
 // Workspace layout. One layout function serves both wl_workspace_bytes and the
-// calls, so the two always agree. Both regimes' regions are always reserved,
-// so the size does not depend on the regime switch.
+// calls, so the two always agree. The decode region is always reserved, so the
+// size does not depend on the regime switch.
 //
 //   [0, 256)          reserved
 //   gemv_partial      fp32 3 x [kGemvMaxSlices][kGemvMaxTok][kMaxRank] V^T x slices
-//   vtx[c]            matrix-core regime: fp32 [n_slices][T][r_c] V^T x slice
-//                     partials per child (MLP: gate, up, down)
+//                     (decode regime; the matrix-core kernel computes V^T x itself)
 //   h                 bf16 [T][d_ff] (MLP only)
 
-constexpr size_t kSyncBytes = 256;
-
-int mfma_vtx_slices(int d_in) { return (d_in + wl::kVtxMaxSlice - 1) / wl::kVtxMaxSlice; }
-int mfma_vtx_slice_len(int d_in) {
-    const int n = mfma_vtx_slices(d_in);
-    return ((d_in + n - 1) / n + 7) / 8 * 8;
-}
+constexpr size_t kReservedBytes = 256;
 
 struct Layout {
     size_t gemv_partial = 0;
-    size_t vtx[3] = {0, 0, 0};   // offsets
     size_t h = 0;
     size_t total = 0;
 };
 
 Layout layout(int op, const wl_theta *const *th, int T) {
     Layout L;
-    size_t off = kSyncBytes;
+    size_t off = kReservedBytes;
     L.gemv_partial = off;
     off = round_up(off + wl::kMaxChildren * wl::kGemvPartialPerChild * 4, kAlign);
-    const int n = op == WL_OP_LINEAR ? 1 : 3;
-    for (int c = 0; c < n; ++c) {
-        L.vtx[c] = off;
-        off = round_up(off + (size_t)mfma_vtx_slices(th[c]->d_in) * T * th[c]->r * 4, kAlign);
-    }
     if (op == WL_OP_MLP) {
         L.h = off;
         off = round_up(off + (size_t)T * th[0]->d_out * 2, kAlign);
@@ -128,14 +115,12 @@ Layout layout(int op, const wl_theta *const *th, int T) {
     return L;
 }
 
-wl::Child make_child(const wl_theta *th, char *ws, size_t vtx_off, int col0) {
+wl::Child make_child(const wl_theta *th, int col0) {
     wl::Child c;
     c.W0 = static_cast<const uint16_t *>(th->W0);
     c.s = th->s;
     c.U = static_cast<const uint16_t *>(th->U);
     c.V = static_cast<const uint16_t *>(th->V);
-    c.vtx = th->r > 0 ? reinterpret_cast<const float *>(ws + vtx_off) : nullptr;
-    c.vtx_slices = (th->d_in + mfma_vtx_slice_len(th->d_in) - 1) / mfma_vtx_slice_len(th->d_in);
     c.r = th->r;
     c.d_out = th->d_out;
     c.col0 = col0;
@@ -180,7 +165,7 @@ int gemv_tokens(int T, int d_in) {
 // One projection over shared input x: children side by side in y (ldy = total
 // width), or the gate/up pair (pair = true, y = h).
 wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, const void *x, void *y, int ldy,
-                   char *ws, const Layout &L, const size_t *vtx_off, hipStream_t stream) {
+                   char *ws, const Layout &L, hipStream_t stream) {
     hipError_t e = hipSuccess;
     const int tt = gemv_tokens(T, d_in);
     if (getenv("WL_LOG"))
@@ -219,9 +204,6 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
             e = wl::launch_gemv(g, plan, tt, stream);
         }
     } else {
-        auto part = [&](int c) { return reinterpret_cast<float *>(ws + vtx_off[c]); };
-        wl_status st = run_vtx(ch, n_ch, part, x, d_in, 0, T, T, mfma_vtx_slice_len(d_in), stream);
-        if (st != WL_OK) return st;
         wl::Gemm g{};
         for (int c = 0; c < n_ch; ++c) g.ch[c] = ch[c];
         g.n_ch = n_ch;
@@ -317,8 +299,8 @@ wl_status wl_linear(const wl_theta *th, const void *x, void *y, int32_t T, void 
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     char *w = static_cast<char *>(ws);
-    const wl::Child ch = make_child(th, w, L.vtx[0], 0);
-    if ((st = run_proj(&ch, 1, false, th->d_in, T, x, y, th->d_out, w, L, L.vtx, stream)) != WL_OK) return st;
+    const wl::Child ch = make_child(th, 0);
+    if ((st = run_proj(&ch, 1, false, th->d_in, T, x, y, th->d_out, w, L, stream)) != WL_OK) return st;
     return ok();
 }
 
@@ -348,10 +330,10 @@ wl_status wl_qkv_fused(const wl_theta *q, const wl_theta *k, const wl_theta *v, 
     wl::Child ch[3];
     int col0 = 0;
     for (int c = 0; c < 3; ++c) {
-        ch[c] = make_child(ths[c], w, L.vtx[c], col0);
+        ch[c] = make_child(ths[c], col0);
         col0 += ths[c]->d_out;
     }
-    if ((st = run_proj(ch, 3, false, q->d_in, T, x, y_qkv, (int)width, w, L, L.vtx, stream)) != WL_OK) return st;
+    if ((st = run_proj(ch, 3, false, q->d_in, T, x, y_qkv, (int)width, w, L, stream)) != WL_OK) return st;
     return ok();
 }
 
@@ -382,10 +364,10 @@ wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta 
     void *h = w + L.h;
     const int d_ff = gate->d_out;
     // gate/up -> h = bf16(gelu_tanh(g) * u), then down over h
-    const wl::Child gu[2] = {make_child(gate, w, L.vtx[0], 0), make_child(up, w, L.vtx[1], 0)};
-    if ((st = run_proj(gu, 2, true, gate->d_in, T, x, h, d_ff, w, L, L.vtx, stream)) != WL_OK) return st;
-    const wl::Child dc = make_child(down, w, L.vtx[2], 0);
-    if ((st = run_proj(&dc, 1, false, d_ff, T, h, y, down->d_out, w, L, L.vtx + 2, stream)) != WL_OK) return st;
+    const wl::Child gu[2] = {make_child(gate, 0), make_child(up, 0)};
+    if ((st = run_proj(gu, 2, true, gate->d_in, T, x, h, d_ff, w, L, stream)) != WL_OK) return st;
+    const wl::Child dc = make_child(down, 0);
+    if ((st = run_proj(&dc, 1, false, d_ff, T, h, y, down->d_out, w, L, stream)) != WL_OK) return st;
     return ok();
 }
 

@@ -21,14 +21,12 @@ struct Child {
     const float *s;       // fp32 [d_out], or null: every s[o] is 1
     const uint16_t *U;    // bf16 [d_out][r]  (r > 0)
     const uint16_t *V;    // bf16 [d_in][r]   (r > 0)
-    const float *vtx;     // matrix-core regime: V^T x slice partials, fp32 [vtx_slices][T][r]
-    int vtx_slices;       //   (their sum over slices, in order, is vtx[t][k])
     int r, d_out, col0;
 };
 
 // ---------------------------------------------------------------------------
 // V^T x slice partials for up to three children that share one input x
-// (matrix-core regime):
+// (decode regime, when the slices are computed by a launch of their own):
 //   partial[c][slice][t][k] = sum over the slice's inputs i of V_c[i][k] * x[t][i]
 // Plain stores; the consumer, launched after on the same stream, adds the
 // slices in order.
@@ -60,6 +58,7 @@ constexpr size_t kGemvPartialPerChild = (size_t)kGemvMaxSlices * kGemvMaxTok * k
 constexpr int kRedMaxTok = 2;                 // redundant V^T x: at most 2 tokens per pass
 constexpr int kRedMaxPieces = 20;             //   and 20 16-byte pieces of V per lane
 constexpr int kRedUnits = 4;                  //   one unit per wave
+constexpr long long kRedMaxTraffic = 4ll << 20;  //   V re-read by all workgroups
 
 struct GemvF {
     Child ch[kMaxChildren];
@@ -91,7 +90,8 @@ hipError_t launch_gemv(const GemvF &g, const GemvPlan &plan, int tt, hipStream_t
 
 // ---------------------------------------------------------------------------
 // Matrix-core GEMM for larger token counts, same result as Gemv (including pair
-// mode). Output tiles never span two children.
+// mode); V^T x is computed inside, from the x tiles it already loads. Output
+// tiles never span two children.
 struct Gemm {
     Child ch[kMaxChildren];
     int n_ch;

@@ -36,10 +36,10 @@ class Theta(ctypes.Structure):
                 ("r", ctypes.c_int32)]
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIBRARY):
-        raise ImportError(f"{LIBRARY} is not built; run `python -m linear_02_amd.build`")
-    lib = ctypes.CDLL(LIBRARY)
+def _load(path: str = LIBRARY) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m linear_02_amd.build`")
+    lib = ctypes.CDLL(path)
     P = ctypes.POINTER(Theta)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.wl_workspace_bytes.argtypes = [i32, ctypes.POINTER(P), i32, i32]

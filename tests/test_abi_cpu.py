@@ -121,9 +121,14 @@ def test_workspace_checks(wl):
 def test_workspace_bytes_grows_with_tokens_and_rejects_bad_args(wl):
     th = theta(d_in=1152, d_out=1152, r=32)
     arr = (ctypes.POINTER(wl.Theta) * 1)(ctypes.pointer(th))
-    sizes = [wl.lib.wl_workspace_bytes(0, arr, 1, T) for T in (0, 1, 8, 64, 2048)]
-    assert all(s % 256 == 0 for s in sizes)
-    assert sizes == sorted(sizes) and sizes[-1] > sizes[1]
+    lin = [wl.lib.wl_workspace_bytes(0, arr, 1, T) for T in (0, 1, 8, 64, 2048)]
+    assert all(s > 0 and s % 256 == 0 for s in lin)
+    # The MLP keeps h = [T][d_ff] bf16 in the workspace.
+    g, u = theta(d_in=1152, d_out=6912, r=32), theta(W0=A + 0x100000, d_in=1152, d_out=6912, r=32)
+    d = theta(W0=A + 0x200000, d_in=6912, d_out=1152, r=32)
+    mlp_arr = (ctypes.POINTER(wl.Theta) * 3)(ctypes.pointer(g), ctypes.pointer(u), ctypes.pointer(d))
+    mlp = [wl.lib.wl_workspace_bytes(2, mlp_arr, 3, T) for T in (1, 64, 2048)]
+    assert mlp == sorted(mlp) and mlp[-1] - mlp[0] >= (2048 - 1) * 6912 * 2
     assert wl.lib.wl_workspace_bytes(0, arr, 2, 1) == 0      # wrong count
     assert wl.lib.wl_workspace_bytes(7, arr, 1, 1) == 0      # unknown op
     assert wl.lib.wl_workspace_bytes(0, arr, 1, -1) == 0
@@ -181,3 +186,11 @@ def test_regime_switch(wl):
             wl.set_regime(5)
     finally:
         wl.set_regime(prev)
+
+
+def test_library_resolves_its_own_symbols(wl):
+    # A kernel whose host stub was not emitted shows up as an undefined symbol
+    # of the library's own namespace; loading would then fail on the GPU machine.
+    out = subprocess.run(["nm", "-u", "-C", wl.LIBRARY], capture_output=True, text=True, check=True).stdout
+    own = [line for line in out.splitlines() if "wl::" in line]
+    assert not own, f"unresolved library symbols: {own}"
