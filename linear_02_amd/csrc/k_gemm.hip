@@ -70,7 +70,8 @@ struct Cfg {
     static constexpr int V_PIECES = BK * NV * 32 * 2 / 16;      // BK rows of V, up to NV*32 ranks
     static constexpr int A_PER = A_PIECES / kThreads, B_PER = B_PIECES / kThreads;
     static constexpr int V_PER = (V_PIECES + kThreads - 1) / kThreads;
-    static constexpr int STAGE_PIECES = A_PIECES + P * (B_PIECES + V_PIECES);
+    static constexpr int V_SLOTS = V_PER * kThreads;           // every lane's load writes a slot
+    static constexpr int STAGE_PIECES = A_PIECES + P * (B_PIECES + V_SLOTS);
     static constexpr int PER_STAGE = A_PER + P * (B_PER + V_PER);   // direct-to-LDS loads per thread
     static constexpr int TILE_PIECES = D * STAGE_PIECES;
     static constexpr int VT_LD = kMaxRank + 4;                 // fp32 row stride of the epilogue vtx
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(Gemm g) {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const u32x4 *wgp = reinterpret_cast<const u32x4 *>(ch[p]->W0);
-            u32x4 *bst = st + C::A_PIECES + p * (C::B_PIECES + C::V_PIECES);
+            u32x4 *bst = st + C::A_PIECES + p * (C::B_PIECES + C::V_SLOTS);
 #pragma unroll
             for (int h = 0; h < C::B_PER; ++h) {
                 const int q = h * NT + tid, row = q / KP, kc = (q % KP) ^ swz_key<KP>(row), gk = kt * KP + kc;
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(Gemm g) {
             for (int p = 0; p < P; ++p)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    b[p][j] = st[C::A_PIECES + p * (C::B_PIECES + C::V_PIECES) + swz<KP>(wn * TN * 32 + j * 32 + fr, kc)];
+                    b[p][j] = st[C::A_PIECES + p * (C::B_PIECES + C::V_SLOTS) + swz<KP>(wn * TN * 32 + j * 32 + fr, kc)];
 #pragma unroll
             for (int p = 0; p < P; ++p)
 #pragma unroll
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(Gemm g) {
                     for (int p = 0; p < P; ++p) {
                         const int r = ch[p]->r;
                         const uint16_t *vl = reinterpret_cast<const uint16_t *>(
-                            st + C::A_PIECES + p * (C::B_PIECES + C::V_PIECES) + C::B_PIECES);
+                            st + C::A_PIECES + p * (C::B_PIECES + C::V_SLOTS) + C::B_PIECES);
 #pragma unroll
                         for (int v = 0; v < NV; ++v) {
                             const int k = 32 * v + fr;

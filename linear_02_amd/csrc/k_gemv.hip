@@ -23,6 +23,11 @@
 //   lane keeps the matching 16-byte pieces of the tokens in registers (no LDS
 //   staging, no barrier before the stream) and multiplies on v_dot2c_f32_bf16
 //   into fp32. The epilogue operands (U rows, s) are also loaded up front.
+// Loads are written so that the compiler can keep them in flight together:
+//   every address is valid (indices clamped, a valid stand-in pointer where a
+//   tensor is absent) and the value is masked afterwards, and per-child fields
+//   are chosen with selects rather than by indexing the kernel-argument array
+//   with a per-lane index (which becomes a chain of dependent vector loads).
 // Epilogue. The wave sums (DPP butterflies) meet in LDS, and one thread per
 //   (row, token) forms
 //     y[t,o] = s[o] * (W0 x)[t,o] + sum_k U[o,k] vtx[t,k]
@@ -48,41 +53,85 @@ __device__ __forceinline__ int child_index(const GemvF &g, int row) {
     return 0;
 }
 
+// Per-child fields chosen by a per-lane child index ci. Indexing the
+// kernel-argument array with a per-lane index becomes a dependent vector load,
+// and a chain of selects over the three values is turned by the compiler into
+// a table in scratch memory; a sum of masked differences is neither.
+template <class T>
+__device__ __forceinline__ T blend3(int ci, T a, T b, T c) {
+    return a + (ci > 0 ? b - a : T(0)) + (ci > 1 ? c - b : T(0));
+}
+struct ChFields {
+    uint64_t U0, U1, U2, s0, s1, s2;
+    int r0, r1, r2, c1, c2;   // ranks; first rows of children 1 and 2 (absent children are host-zeroed)
+    __device__ __forceinline__ explicit ChFields(const GemvF &g)
+        : U0((uint64_t)g.ch[0].U), U1((uint64_t)g.ch[1].U), U2((uint64_t)g.ch[2].U),
+          s0((uint64_t)g.ch[0].s), s1((uint64_t)g.ch[1].s), s2((uint64_t)g.ch[2].s),
+          r0(g.ch[0].r), r1(g.ch[1].r), r2(g.ch[2].r), c1(g.ch[1].col0), c2(g.ch[2].col0) {}
+    __device__ __forceinline__ int r(int ci) const { return blend3(ci, r0, r1, r2); }
+    __device__ __forceinline__ int col0(int ci) const { return blend3(ci, 0, c1, c2); }
+    __device__ __forceinline__ const uint16_t *U(int ci) const {
+        return reinterpret_cast<const uint16_t *>(blend3(ci, U0, U1, U2));
+    }
+    __device__ __forceinline__ const float *s(int ci) const {
+        return reinterpret_cast<const float *>(blend3(ci, s0, s1, s2));
+    }
+};
+__device__ __forceinline__ int ch_r(const GemvF &g, int ci) { return blend3(ci, g.ch[0].r, g.ch[1].r, g.ch[2].r); }
+
 // Rank entries of all children flattened: item -> (child, token, k), item < total.
 __device__ __forceinline__ int vtx_items(const GemvF &g, int tt) {
     return tt * (g.ch[0].r + (g.n_ch > 1 ? g.ch[1].r : 0) + (g.n_ch > 2 ? g.ch[2].r : 0));
 }
 __device__ __forceinline__ void vtx_item(const GemvF &g, int tt, int item, int &c, int &t, int &k) {
+    const int n0 = tt * g.ch[0].r, n1 = g.n_ch > 1 ? tt * g.ch[1].r : 0;
     c = 0;
-    while (c < g.n_ch - 1 && item >= tt * g.ch[c].r) {
-        item -= tt * g.ch[c].r;
-        ++c;
+    if (g.n_ch > 1 && item >= n0) {
+        item -= n0;
+        c = 1;
+        if (g.n_ch > 2 && item >= n1) {
+            item -= n1;
+            c = 2;
+        }
     }
-    t = item / g.ch[c].r;
-    k = item - t * g.ch[c].r;
+    const int r = max(ch_r(g, c), 1);
+    t = item / r;
+    k = item - t * r;
 }
 
 __device__ __forceinline__ float group_sum(const float *base, int stride, int s0, int s1) {
     float v[kGroup];
 #pragma unroll
-    for (int u = 0; u < kGroup; ++u) v[u] = s0 + u < s1 ? base[(size_t)(s0 + u) * stride] : 0.f;
+    for (int u = 0; u < kGroup; ++u) v[u] = base[(size_t)min(s0 + u, s1 - 1) * stride];
     float sum = 0.f;
 #pragma unroll
-    for (int u = 0; u < kGroup; ++u) sum += v[u];
+    for (int u = 0; u < kGroup; ++u) sum += s0 + u < s1 ? v[u] : 0.f;
     return sum;
 }
 
-// Slice partials, split mapping (items * groups <= threads): thread (item, group)
-// sums one group of slices with one batch of loads.
+// Slice partials, split mapping (items * groups <= threads): thread (item,
+// group) loads one group of slices before the W0 stream (every address valid,
+// the count of real slices kept in n) and adds them after it.
 template <int TT>
-__device__ __forceinline__ float gather_part(const GemvF &g, int n_items, int n_groups) {
-    const int item = threadIdx.x / n_groups, grp = threadIdx.x - item * n_groups;
-    if (item >= n_items) return 0.f;
+__device__ __forceinline__ void gather_issue(const GemvF &g, int n_items, int n_groups, float (&v)[kGroup], int &n) {
+    int item = threadIdx.x / n_groups;
+    const int grp = threadIdx.x - item * n_groups;
+    const bool ok = item < n_items;
+    item = ok ? item : 0;
     int c, t, k;
     vtx_item(g, TT, item, c, t, k);
-    const int r = g.ch[c].r;
+    const int r = ch_r(g, c);
     const float *base = g.partial + (size_t)c * kGemvPartialPerChild + t * r + k;
-    return group_sum(base, TT * r, grp * kGroup, min(g.S, grp * kGroup + kGroup));
+    const int s0 = grp * kGroup, s1 = min(g.S, s0 + kGroup);
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) v[u] = ldg(base + (size_t)min(s0 + u, s1 - 1) * (TT * r));
+    n = ok ? s1 - s0 : 0;
+}
+__device__ __forceinline__ float gather_finish(const float (&v)[kGroup], int n) {
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) sum += u < n ? v[u] : 0.f;
+    return sum;
 }
 
 // Slice partials, full mapping: thread per item, groups in order, into vs.
@@ -91,7 +140,7 @@ __device__ void gather_full(const GemvF &g, int n_items, float (*vs)[TT][kMaxRan
     for (int item = threadIdx.x; item < n_items; item += kThreads) {
         int c, t, k;
         vtx_item(g, TT, item, c, t, k);
-        const int r = g.ch[c].r;
+        const int r = ch_r(g, c);
         const float *base = g.partial + (size_t)c * kGemvPartialPerChild + t * r + k;
         float sum = 0.f;
         for (int s0 = 0; s0 < g.S; s0 += kGroup) sum += group_sum(base, TT * r, s0, min(g.S, s0 + kGroup));
@@ -118,13 +167,15 @@ __device__ __forceinline__ void red_issue(const GemvF &g, RedLoads<TT> &rl, int 
     for (int m = 0; m < kRedMaxPieces; ++m) {
         const int j = lo + lane + kWave * m;
         const bool in = j < hi;
-        rl.v[m] = in ? *reinterpret_cast<const u32x4 *>(r >= 8 ? c.V + (size_t)j * r + kc * 8 : c.V + (size_t)j * 8)
-                     : u32x4{0u, 0u, 0u, 0u};
+        const int jc = in ? j : lo;   // a valid piece; the value is dropped below
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(r >= 8 ? c.V + (size_t)jc * r + kc * 8 : c.V + (size_t)jc * 8);
+        rl.v[m] = in ? v : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
             const bool tin = in && g.t0 + t < g.T;
-            const uint16_t *xt = g.x + (size_t)(g.t0 + t) * g.d_in;
-            rl.x[m][t] = !tin ? 0u : r >= 8 ? (uint32_t)xt[j] : *reinterpret_cast<const uint32_t *>(xt + 2 * j);
+            const uint16_t *xt = g.x + (size_t)min(g.t0 + t, g.T - 1) * g.d_in;
+            const uint32_t xv = r >= 8 ? (uint32_t)xt[jc] : *reinterpret_cast<const uint32_t *>(xt + 2 * jc);
+            rl.x[m][t] = tin ? xv : 0u;
         }
     }
 }
@@ -178,7 +229,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     __shared__ float gsum[kThreads];
     __shared__ float upart[kWaves][8][TT];
 
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    // The wave index is uniform: keep it (and what derives from it) in scalar registers.
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nch = g.d_in >> 3;
     const int nseg = g.nseg;
     const int rows_g = (kWaves / nseg) * R;
@@ -187,6 +239,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     const bool parts = g.vmode == kVtxPartials;
 
     // ---- everything the epilogue needs, issued before the stream ----
+    const ChFields cf(g);
     RedLoads<RED_OK ? TT : 1> rl;
     if constexpr (RED_OK)
         if (red) red_issue<TT>(g, rl, wave, lane);
@@ -196,25 +249,28 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
         const int item = tid + u * kThreads;          // (jr, p, k) over [kMaxRowsG][P][64]
         const int jr = item / (P * kMaxRank), p = (item / kMaxRank) % P, k = item % kMaxRank;
         const int row = rowbase + jr;
-        float v = 0.f;
-        if (jr < rows_g && row < g.rows) {
-            const Child &c = g.ch[P == 2 ? p : child_index(g, row)];
-            if (k < c.r) v = bf16_f(c.U[(size_t)(row - c.col0) * c.r + k]);
-        }
-        upre[u] = v;
+        const int ci = P == 2 ? p : child_index(g, min(row, g.rows - 1));
+        const int r = cf.r(ci);
+        const bool ok = jr < rows_g && row < g.rows && k < r;
+        const uint16_t *src = ok ? cf.U(ci) + (size_t)(row - cf.col0(ci)) * r + k : g.x;
+        const float v = bf16_f(ldg(src));
+        upre[u] = ok ? v : 0.f;
     }
-    float spre = 1.f;
-    if (tid < rows_g * P) {
-        const int jr = tid / P, p = tid - jr * P;
+    float spre;
+    {
+        const int jr = min(tid / P, rows_g - 1), p = tid % P;
         const int row = min(rowbase + jr, g.rows - 1);
-        const Child &c = g.ch[P == 2 ? p : child_index(g, row)];
-        if (c.s) spre = c.s[row - c.col0];
+        const int ci = P == 2 ? p : child_index(g, row);
+        const float *sp = cf.s(ci);
+        const float v = ldg(sp ? sp + (row - cf.col0(ci)) : reinterpret_cast<const float *>(g.x));
+        spre = sp ? v : 1.f;
     }
     const int n_items = g.vmode != kVtxNone ? vtx_items(g, TT) : 0;
     const int n_groups = (g.S + kGroup - 1) / kGroup;
     const bool split = n_items * n_groups <= kThreads;
-    float gpre = 0.f;
-    if (parts && split) gpre = gather_part<TT>(g, n_items, n_groups);
+    float gv[kGroup];
+    int gn = 0;
+    if (parts && split) gather_issue<TT>(g, n_items, n_groups, gv, gn);
 
     // ---- W0 x ----
     {
@@ -287,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
         if (red) red_reduce<TT>(g, rl, wave, lane, upart);
     if (parts) {
         if (split)
-            gsum[tid] = gpre;
+            gsum[tid] = gather_finish(gv, gn);
         else
             gather_full<TT>(g, n_items, vs);
     }
@@ -305,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
             // Units of the column holding (c, k), in part order.
             int c, t, k;
             vtx_item(g, TT, item, c, t, k);
-            const bool wide = g.ch[c].r >= 8;
+            const bool wide = ch_r(g, c) >= 8;
             const int kc = wide ? k >> 3 : 0, e = wide ? (k & 7) : k;
             float sum = 0.f;
             for (int u = 0; u < g.red_units; ++u)
@@ -327,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
             float m = 0.f;
             for (int sg = 0; sg < nseg; ++sg) m += mbuf[rbi * nseg + sg][j][p][t];
             const int ci = P == 2 ? p : child_index(g, row);
-            const int r = g.ch[ci].r;
+            const int r = ch_r(g, ci);
             float d = 0.f;
             for (int k = 0; k < r; ++k) d += ulds[jr][p][k] * vs[ci][t][k];
             val[p] = slds[jr][p] * m + d;

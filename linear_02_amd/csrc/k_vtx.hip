@@ -61,17 +61,24 @@ __global__ __launch_bounds__(kThreads) void vtx_kernel(VtxJob job) {
     if (k < r) {
         for (int ib = g; ib < len; ib += 16 * G) {
             float v[16], xv[16][TB];
+            // Every address is valid (rows clamped into the slice, tokens into
+            // the block) and the values are masked afterwards, so the 16 rows'
+            // loads are all in flight at once.
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const int i = ib + u * G;
                 const bool in = i < len;
-                v[u] = in ? bf16_f(V[(size_t)(i0 + i) * r + k]) : 0.f;
+                const int ic = min(i, len - 1);
+                const float vv = bf16_f(V[(size_t)(i0 + ic) * r + k]);
+                v[u] = in ? vv : 0.f;
 #pragma unroll
                 for (int t = 0; t < TB; ++t) {
-                    if constexpr (kStage)
-                        xv[u][t] = bf16_f(xs[t * kVtxMaxSlice + min(i, len - 1)]);
-                    else
-                        xv[u][t] = (in && t < tn) ? bf16_f(job.x[(size_t)(t0 + t) * job.d_in + i0 + i]) : 0.f;
+                    if constexpr (kStage) {
+                        xv[u][t] = bf16_f(xs[t * kVtxMaxSlice + ic]);
+                    } else {
+                        const float xx = bf16_f(job.x[(size_t)(t0 + min(t, tn - 1)) * job.d_in + i0 + ic]);
+                        xv[u][t] = t < tn ? xx : 0.f;
+                    }
                 }
             }
 #pragma unroll

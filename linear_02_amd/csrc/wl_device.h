@@ -16,6 +16,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Load through the global address space. A pointer the compiler cannot trace to
+// a kernel argument (chosen by a select, rebuilt from registers) is otherwise
+// loaded with a flat instruction, which also counts on the scalar-load counter,
+// so the next wait for a scalar load would wait for this load as well.
+template <class T>
+__device__ __forceinline__ T ldg(const T *p) {
+    return *(const __attribute__((address_space(1))) T *)p;
+}
+
 // bf16 bit pattern -> fp32. Exact: a bf16 is the upper half of a binary32.
 __device__ __forceinline__ float bf16_f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
