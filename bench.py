@@ -1,24 +1,44 @@
 #!/usr/bin/env python3
-"""Decode benchmark of the fused reconstruct-and-project linear on one MI355X.
+"""Benchmark of the fused reconstruct-and-project linear on one MI355X.
 
-Workload: one Gemma-3-1B-shaped decoder layer at decode, T = 1 token, rank r
-(default 32): fused Q/K/V 1152 -> 1024 + 256 + 256, O 1024 -> 1152, fused MLP
-gate/up 1152 -> 6912, GELU-tanh, down 6912 -> 1152. A step is one pass of that
-layer (three library calls: wl_qkv_fused, wl_linear, wl_mlp_fused). Steps cycle
-over 26 resident layers with their own W0 (the passthrough point, one W0 per
-layer), so the 1.4 GB weight set is streamed from HBM rather than served from
-the 256 MB last-level cache. Inputs are seeded synthetic draws with the value
-distributions W0 ~ N(0, 0.02), s ~ 1 + N(0, 0.01), U, V ~ N(0, 0.01),
-x ~ N(0, 1), already resident on the GPU when timing starts.
+    y = s (.) (W0 x) + U (V^T x)      bf16 W0, U, V, x; fp32 s; fp32 accumulate; bf16 y
 
-Prints one JSON line: tokens/s per layer (value), the roofline record of the
-dominant operation (the fused MLP, about 86 % of a layer's bytes) measured with
-HIP events on the launch stream during the timed region, and the CPU oracle
-timed on a bounded sample of the same workload.
+Workloads (``--workload``; the default is the one the headline metric is quoted on):
+
+  layer-decode    one Gemma-3-1B-shaped decoder layer at T = 1 token, rank r
+                  (default 32): fused Q/K/V 1152 -> 1024 + 256 + 256, O 1024 ->
+                  1152, fused MLP gate/up 1152 -> 6912, GELU-tanh, down 6912 ->
+                  1152. A step is one layer (wl_qkv_fused, wl_linear,
+                  wl_mlp_fused); steps cycle over 26 resident layers with their
+                  own W0, so the 1.4 GB weight set streams from HBM rather than
+                  from the 256 MB last-level cache.
+  single          one 1152 -> 1152 projection, r = 4, T = 1; steps cycle over 400
+                  resident copies (about 1.07 GB).
+  batched-decode  the same layer shapes, 26 layers, T = 32 tokens (32 concurrent
+                  streams), r (default 32); a step is all 26 layers. --shared-w0
+                  gives every layer the same W0 (G = 1), the default is an own W0
+                  per layer (G = 26).
+  prefill         the same layer shapes at T = 2048 tokens, r = 32; a step is one
+                  layer, cycling over 26 layers. Also times wl_materialize_weff for
+                  the seven projections of a layer.
+  large           a hidden-5376 layer: Q/K/V 5376 -> 8192 + 2048 + 2048, O 8192 ->
+                  5376, MLP 5376 -> 21504 -> 5376, r = 32, T = --tokens (1 or
+                  512). W0 ~ N(0, 0.01), seed 1. A step is one layer.
+
+Inputs are seeded synthetic draws (linear_02_amd.inputs) with W0 ~ N(0, 0.02)
+(0.01 for large), s ~ 1 + N(0, 0.01), U, V ~ N(0, 0.01), x ~ N(0, 1), already
+resident in device memory when timing starts. Steps are replayed from HIP
+graphs, since at decode sizes a call is shorter than the host cost of its
+launches. The roofline record covers the dominant library call (the fused MLP):
+its algorithmic bytes (decode) or flops (prefill, large at T = 512) over its
+average duration, timed with HIP events on the stream the library launches on.
+The oracle (plain fp64 C, single thread) is timed on a bounded sample of the
+same work. One JSON line is printed.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,20 +48,27 @@ REPO = os.path.dirname(os.path.abspath(__file__))
 if REPO not in sys.path:
     sys.path.insert(0, REPO)
 
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix cores
 METRIC = "tokens/s + achieved HBM GB/s (T=1) / MFMA TFLOP/s (T=2048) per rank"
+WORKLOADS = ("layer-decode", "single", "batched-decode", "prefill", "large")
+DEFAULT_STEPS = {"layer-decode": 2600, "single": 4000, "batched-decode": 200, "prefill": 260, "large": 40}
 
 
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=2600)
-    p.add_argument("--warmup", type=int, default=260)
-    p.add_argument("--rank", type=int, default=32)
-    p.add_argument("--layers", type=int, default=26, help="distinct resident layers cycled through")
+    p.add_argument("--workload", choices=WORKLOADS, default="layer-decode")
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--rank", type=int, default=None, help="low-rank r (default per workload)")
+    p.add_argument("--tokens", type=int, default=None, help="T for the large workload (1 or 512)")
+    p.add_argument("--shared-w0", action="store_true", help="batched-decode: one W0 for all layers (G=1)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0 skips it)")
     return p.parse_args()
 
+
+# -- algorithmic work (counted once per call; what the method must move or compute) ----------
 
 def theta_bytes(th: dict) -> int:
     """W0 + s + U + V bytes of one theta."""
@@ -49,11 +76,360 @@ def theta_bytes(th: dict) -> int:
     return 2 * d_out * d_in + (4 * d_out if th.get("s") is not None else 0) + 2 * r * (d_out + d_in)
 
 
+def theta_flops(th: dict, T: int) -> int:
+    """Multiply-adds of W0 x, V^T x and U vtx (2 flops each) plus the s scaling."""
+    d_in, d_out, r = th["d_in"], th["d_out"], th["r"]
+    return 2 * T * d_out * d_in + 2 * T * r * (d_in + d_out) + 2 * T * d_out
+
+
+def call_bytes(thetas, T: int, d_x: int, d_y: int) -> int:
+    return sum(theta_bytes(t) for t in thetas) + 2 * T * d_x + 2 * T * d_y
+
+
+def layer_work(lay: dict, dims: dict, T: int):
+    """(bytes, flops) of one layer: Q/K/V call, O call, MLP call."""
+    d, width = dims["d_model"], dims["q"] + 2 * dims["kv"]
+    b = (call_bytes([lay[f] for f in "qkv"], T, d, width) + call_bytes([lay["o"]], T, dims["q"], d)
+         + call_bytes([lay[f] for f in ("gate", "up", "down")], T, d, d))
+    fl = sum(theta_flops(lay[f], T) for f in ("q", "k", "v", "o", "gate", "up", "down"))
+    return b, fl
+
+
+def mlp_work(lay: dict, dims: dict, T: int):
+    d = dims["d_model"]
+    b = call_bytes([lay[f] for f in ("gate", "up", "down")], T, d, d)
+    fl = sum(theta_flops(lay[f], T) for f in ("gate", "up", "down"))
+    return b, fl
+
+
+def source_digest() -> str:
+    """Digest of the kernel sources, to tell whether stored counter data still applies."""
+    import glob
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(REPO, "linear_02_amd", "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, rank: int, tokens: int):
+    """HBM bytes per call of the dominant operation from the committed counter summary
+    (rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes), or None when there is none or
+    the kernels changed since it was taken."""
+    path = os.path.join(REPO, "profiles", f"traffic_{workload}_r{rank}_T{tokens}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("sources") != source_digest():
+        return None
+    try:
+        return float(kv["bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+# -- timing -------------------------------------------------------------------------------
+
+class GraphSet:
+    """HIP graphs over a list of per-index callables: one graph holding all of them
+    in order and one per index, so that exactly K steps can be replayed."""
+
+    def __init__(self, torch, fns):
+        self.torch = torch
+        for fn in fns:      # eager pass: allocations and workspace before capture
+            fn()
+        torch.cuda.synchronize()
+        self.all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.all):
+            for fn in fns:
+                fn()
+        self.one = []
+        for fn in fns:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            self.one.append(g)
+        self.n = len(fns)
+
+    def run(self, k: int):
+        for _ in range(k // self.n):
+            self.all.replay()
+        for i in range(k % self.n):
+            self.one[i].replay()
+
+
+def time_steps(torch, gs: GraphSet, steps: int, warmup: int):
+    gs.run(warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall = time.perf_counter()
+    e0.record()
+    gs.run(steps)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall
+    return e0.elapsed_time(e1), wall
+
+
+def time_calls(torch, gs: GraphSet, calls: int) -> float:
+    """Average ms per call of the graph set's callables, replayed `calls` times in total."""
+    reps = max(1, calls // gs.n)
+    gs.all.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        gs.all.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * gs.n)
+
+
+def oracle_sample(budget_s: float, fn, units_per_call: float, unit: str, what: str):
+    """Time the oracle: call fn() until the budget is spent (at least once)."""
+    if budget_s <= 0:
+        return None
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": reps * units_per_call / el, "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x {what} in {el:.1f} s, single-threaded fp64 C oracle"}
+
+
+def rel_l2(np, y_gpu, y_ref) -> float:
+    yg = y_gpu.float().cpu().double().numpy()
+    return float(np.linalg.norm(yg - y_ref) / np.linalg.norm(y_ref))
+
+
+# -- workloads ----------------------------------------------------------------------------
+
+def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_std, seed, workload,
+               bound):
+    """Decoder-layer workloads: steps of one layer (or of all layers for batched decode)."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(seed)
+    t_gen = time.perf_counter()
+    host_layers = inputs.layers(gen, dims, r, n_layers, G, w0_std=w0_std)
+    acts = inputs.layer_inputs(gen, dims, T)
+    layers = [{f: wl.theta_to(lay[f], dev) for f in inputs.FAMILIES} for lay in host_layers]
+    # W0 blocks shared between layers stay shared on the device.
+    if G < n_layers:
+        band = -(-n_layers // G)
+        for l in range(n_layers):
+            for f in inputs.FAMILIES:
+                layers[l][f]["W0"] = layers[(l // band) * band][f]["W0"]
+    xa = {k: v.to(dev) for k, v in acts.items()}
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    d, width = dims["d_model"], dims["q"] + 2 * dims["kv"]
+    y_qkv = torch.empty(T, width, dtype=torch.bfloat16, device=dev)
+    y_o = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    y_mlp = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    l0 = layers[0]
+    ws_bytes = max(wl.workspace_bytes(wl.OP_QKV, [l0["q"], l0["k"], l0["v"]], T),
+                   wl.workspace_bytes(wl.OP_LINEAR, [l0["o"]], T),
+                   wl.workspace_bytes(wl.OP_MLP, [l0["gate"], l0["up"], l0["down"]], T))
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def qkv(l):
+        lay = layers[l]
+        wl.wl_qkv_fused(lay["q"], lay["k"], lay["v"], xa["x_attn"], y=y_qkv, ws=ws)
+
+    def o(l):
+        wl.wl_linear(layers[l]["o"], xa["x_o"], y=y_o, ws=ws)
+
+    def mlp(l):
+        lay = layers[l]
+        wl.wl_mlp_fused(lay["gate"], lay["up"], lay["down"], xa["x_mlp"], y=y_mlp, ws=ws)
+
+    def layer_step(l):
+        qkv(l)
+        o(l)
+        mlp(l)
+
+    # Parity spot check of layer 0 against the oracle (eager, outside the timed region).
+    layer_step(0)
+    torch.cuda.synchronize()
+    h0 = host_layers[0]
+    parity = {}
+    if T <= 64 or workload == "prefill":
+        # At prefill sizes the oracle takes a slice of the tokens: the first 16.
+        n_chk = min(T, 16)
+        sl = slice(0, n_chk)
+        parity["qkv"] = rel_l2(np, y_qkv[sl], orc.qkv(h0["q"], h0["k"], h0["v"], acts["x_attn"][sl])[0])
+        parity["o"] = rel_l2(np, y_o[sl], orc.linear(h0["o"], acts["x_o"][sl])[0])
+        parity["mlp"] = rel_l2(np, y_mlp[sl], orc.mlp(h0["gate"], h0["up"], h0["down"], acts["x_mlp"][sl])[0])
+        parity["tokens_checked"] = n_chk
+
+    if workload == "batched-decode":
+        steps_fns = [lambda: [layer_step(l) for l in range(n_layers)]]
+        tokens_per_step = T
+        unit_layers = n_layers
+    else:
+        steps_fns = [lambda l=l: layer_step(l) for l in range(n_layers)]
+        tokens_per_step = T
+        unit_layers = 1
+    gs = GraphSet(torch, steps_fns)
+    gs_mlp = GraphSet(torch, [lambda l=l: mlp(l) for l in range(n_layers)])
+
+    K = args.steps if args.steps is not None else DEFAULT_STEPS[workload]
+    W = args.warmup if args.warmup is not None else max(1, K // 10)
+    ms_total, wall = time_steps(torch, gs, K, W)
+    ms_per_step = ms_total / K
+    mlp_ms = time_calls(torch, gs_mlp, max(n_layers, K * unit_layers))
+
+    lay_b, lay_f = layer_work(h0, dims, T)
+    mlp_b, mlp_f = mlp_work(h0, dims, T)
+    step_b, step_f = lay_b * unit_layers, lay_f * unit_layers
+    if bound == "hbm":
+        achieved = mlp_b / (mlp_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(workload, r, T),
+                "kernel": "wl_mlp_fused (all of its kernels, back to back)", "bytes_per_launch": mlp_b,
+                "us_per_launch": mlp_ms * 1e3}
+    else:
+        achieved = mlp_f / (mlp_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_BF16_PEAK_TFS, "traffic": stored_traffic(workload, r, T),
+                "kernel": "wl_mlp_fused (all of its kernels, back to back)", "flops_per_launch": mlp_f,
+                "us_per_launch": mlp_ms * 1e3}
+
+    # Oracle sample: whole layers at decode sizes, a few tokens of a layer otherwise.
+    n_tok = T if T <= 32 else (8 if T <= 512 else 4)
+    sl = slice(0, n_tok)
+
+    def oracle_layer():
+        orc.qkv(h0["q"], h0["k"], h0["v"], acts["x_attn"][sl])
+        orc.linear(h0["o"], acts["x_o"][sl])
+        orc.mlp(h0["gate"], h0["up"], h0["down"], acts["x_mlp"][sl])
+
+    cpu = oracle_sample(args.cpu_seconds, oracle_layer, n_tok, "tokens/s",
+                        f"one layer (QKV + O + MLP) at {n_tok} token(s), r={r}")
+
+    extra = {}
+    if workload == "prefill":
+        extra.update(materialize_and_dense(torch, wl, layers, xa, dims, T, ws))
+
+    out = {
+        "value": K * tokens_per_step / (ms_total * 1e-3),
+        "unit": "tokens/s",
+        "steps": K, "warmup": W, "ms_per_step": ms_per_step,
+        "config": {"workload": workload_name(workload, dims, r, T, n_layers, G),
+                   "T": T, "rank": r, "layers": n_layers, "G": G, "d_model": d, "q": dims["q"],
+                   "kv": dims["kv"], "d_ff": dims["ff"], "parallelism": "single-gpu"},
+        "roofline": roof,
+        "step_hbm_gbs": step_b / (ms_per_step * 1e-3) / 1e9,
+        "step_tflops": step_f / (ms_per_step * 1e-3) / 1e12,
+        "step_bytes": step_b, "step_flops": step_f,
+        "wall_s_timed": wall,
+        "parity_rel_l2": parity,
+        "cpu_baseline": cpu,
+        "setup_s": t_gen,
+    }
+    out.update(extra)
+    return out
+
+
+def materialize_and_dense(torch, wl, layers, xa, dims, T, ws):
+    """The precompute-outside path at prefill: W_eff for the seven projections of a
+    layer, and the dense products with those W_eff (s = 1, r = 0 through the same
+    library), against the fused path."""
+    dev = layers[0]["q"]["W0"].device
+    lay = layers[0]
+    weff = {f: torch.empty_like(lay[f]["W0"]) for f in lay}
+
+    def materialize():
+        for f in lay:
+            wl.wl_materialize_weff(lay[f], W_eff=weff[f])
+
+    dense = {f: dict(W0=weff[f], s=None, U=None, V=None, d_in=lay[f]["d_in"], d_out=lay[f]["d_out"], r=0)
+             for f in lay}
+    d, width = dims["d_model"], dims["q"] + 2 * dims["kv"]
+    y_qkv = torch.empty(T, width, dtype=torch.bfloat16, device=dev)
+    y_o = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    y_mlp = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+
+    def dense_layer():
+        wl.wl_qkv_fused(dense["q"], dense["k"], dense["v"], xa["x_attn"], y=y_qkv, ws=ws)
+        wl.wl_linear(dense["o"], xa["x_o"], y=y_o, ws=ws)
+        wl.wl_mlp_fused(dense["gate"], dense["up"], dense["down"], xa["x_mlp"], y=y_mlp, ws=ws)
+
+    gm = GraphSet(torch, [materialize])
+    gd = GraphSet(torch, [dense_layer])
+    m_ms = time_calls(torch, gm, 20)
+    d_ms = time_calls(torch, gd, 20)
+    w_bytes = sum(2 * 2 * lay[f]["d_out"] * lay[f]["d_in"] + 4 * lay[f]["d_out"]
+                  + 2 * lay[f]["r"] * (lay[f]["d_in"] + lay[f]["d_out"]) for f in lay)
+    return {"materialize_weff": {"us_per_layer": m_ms * 1e3, "hbm_gbs": w_bytes / (m_ms * 1e-3) / 1e9,
+                                 "bytes_per_layer": w_bytes},
+            "dense_on_weff": {"us_per_layer": d_ms * 1e3}}
+
+
+def workload_name(workload, dims, r, T, n_layers, G):
+    if workload == "large":
+        return f"hidden-5376 layer (QKV fused + O + MLP fused), T={T}, r={r}"
+    if workload == "batched-decode":
+        return f"gemma3-1b-shaped {n_layers} layers, batched decode T={T}, r={r}, G={G}"
+    if workload == "prefill":
+        return f"gemma3-1b-shaped layer prefill T={T}, r={r}"
+    return f"gemma3-1b-shaped layer decode (QKV fused + O + MLP fused), T={T}, r={r}"
+
+
+def run_single(args, torch, np, wl, inputs, orc):
+    dev = torch.device("cuda:0")
+    r, T, d, copies = (args.rank if args.rank is not None else 4), 1, 1152, 400
+    gen = torch.Generator().manual_seed(0)
+    host = inputs.theta(gen, d, d, r)
+    x_host = inputs.activations(gen, T, d)
+    # The copies share s, U and V draws and differ in W0 only (fresh draws are slow on
+    # the host); every call still reads its own 2.65 MB W0 from HBM.
+    ths = []
+    for c in range(copies):
+        th = wl.theta_to(host, dev)
+        if c > 0:
+            th["W0"] = torch.randn(d, d, generator=gen).mul_(0.02).to(torch.bfloat16).to(dev)
+        ths.append(th)
+    x = x_host.to(dev)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(wl.workspace_bytes(wl.OP_LINEAR, [ths[0]], T), dtype=torch.uint8, device=dev)
+    wl.wl_linear(ths[0], x, y=y, ws=ws)
+    torch.cuda.synchronize()
+    parity = {"linear": rel_l2(np, y, orc.linear(host, x_host)[0])}
+    gs = GraphSet(torch, [lambda c=c: wl.wl_linear(ths[c], x, y=y, ws=ws) for c in range(copies)])
+    K = args.steps if args.steps is not None else DEFAULT_STEPS["single"]
+    W = args.warmup if args.warmup is not None else max(1, K // 10)
+    ms_total, wall = time_steps(torch, gs, K, W)
+    ms = ms_total / K
+    b = call_bytes([host], T, d, d)
+    achieved = b / (ms * 1e-3) / 1e9
+    cpu = oracle_sample(args.cpu_seconds, lambda: orc.linear(host, x_host), 1, "tokens/s",
+                        f"one 1152->1152 projection at T=1, r={r}")
+    return {
+        "value": K * T / (ms_total * 1e-3), "unit": "tokens/s", "steps": K, "warmup": W, "ms_per_step": ms,
+        "config": {"workload": f"single projection 1152->1152, T=1, r={r}, {copies} resident copies",
+                   "T": T, "rank": r, "copies": copies, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic("single", r, T),
+                     "kernel": "wl_linear (all of its kernels, back to back)", "bytes_per_launch": b,
+                     "us_per_launch": ms * 1e3},
+        "wall_s_timed": wall, "parity_rel_l2": parity, "cpu_baseline": cpu,
+    }
+
+
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path is single-device; sharding is described in DESIGN.md)", file=sys.stderr)
+              "(the path is single-device; how it would shard is described in DESIGN.md)", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -62,166 +438,35 @@ def main() -> int:
     if not os.path.exists(wl_build.LIBRARY):
         wl_build.build()
     from linear_02_amd import inputs, wl
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    dims = inputs.GEMMA3_1B
-    r, L, T = args.rank, args.layers, 1
-    gen = torch.Generator().manual_seed(0)
-
-    # Resident layers (device) and the host copy of layer 0 for the oracle.
-    t_gen = time.perf_counter()
-    layers_dev, acts_dev = [], []
-    host_layer0 = host_acts0 = None
-    for l in range(L):
-        lay = inputs.layer(gen, dims, r)
-        acts = inputs.layer_inputs(gen, dims, T)
-        if l == 0:
-            host_layer0, host_acts0 = lay, acts
-        layers_dev.append({f: wl.theta_to(lay[f], dev) for f in inputs.FAMILIES})
-        acts_dev.append({k: v.to(dev) for k, v in acts.items()})
-    torch.cuda.synchronize()
-    t_gen = time.perf_counter() - t_gen
-
-    width_qkv = dims["q"] + 2 * dims["kv"]
-    y_qkv = torch.empty(T, width_qkv, dtype=torch.bfloat16, device=dev)
-    y_o = torch.empty(T, dims["d_model"], dtype=torch.bfloat16, device=dev)
-    y_mlp = torch.empty(T, dims["d_model"], dtype=torch.bfloat16, device=dev)
-    lay0 = layers_dev[0]
-    ws_bytes = max(wl.workspace_bytes(wl.OP_QKV, [lay0["q"], lay0["k"], lay0["v"]], T),
-                   wl.workspace_bytes(wl.OP_LINEAR, [lay0["o"]], T),
-                   wl.workspace_bytes(wl.OP_MLP, [lay0["gate"], lay0["up"], lay0["down"]], T))
-    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
-
-    def mlp(l: int):
-        lay, a = layers_dev[l], acts_dev[l]
-        wl.wl_mlp_fused(lay["gate"], lay["up"], lay["down"], a["x_mlp"], y=y_mlp, ws=ws)
-
-    def step(l: int):
-        lay, a = layers_dev[l], acts_dev[l]
-        wl.wl_qkv_fused(lay["q"], lay["k"], lay["v"], a["x_attn"], y=y_qkv, ws=ws)
-        wl.wl_linear(lay["o"], a["x_o"], y=y_o, ws=ws)
-        mlp(l)
-
-    # Parity spot check of layer 0 against the oracle (eager, outside the timed region).
-    step(0)
-    torch.cuda.synchronize()
     from oracle import oracle as oracle_mod
+
+    torch.cuda.set_device(0)
     orc = oracle_mod.default()
-    h0, a0 = host_layer0, host_acts0
-    parity = {}
-    for name, y_gpu, (y_ref, bound) in (
-            ("qkv", y_qkv, orc.qkv(h0["q"], h0["k"], h0["v"], a0["x_attn"])),
-            ("o", y_o, orc.linear(h0["o"], a0["x_o"])),
-            ("mlp", y_mlp, orc.mlp(h0["gate"], h0["up"], h0["down"], a0["x_mlp"])[:2])):
-        yg = y_gpu.float().cpu().double().numpy()
-        parity[name] = float(np.linalg.norm(yg - y_ref) / np.linalg.norm(y_ref))
-
-    # At one token a layer is ~10 us of GPU work, less than the host cost of its
-    # launches, so steps are replayed from HIP graphs: one graph holding all L
-    # layer steps, and one graph per single layer step so that exactly K steps
-    # run. The fused MLP of every layer is captured alone as well, for the
-    # per-operation timing of the roofline record.
-    for l in range(L):
-        step(l)
-    torch.cuda.synchronize()
-    g_all, g_one, g_mlp = torch.cuda.CUDAGraph(), [], torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all):
-        for l in range(L):
-            step(l)
-    for l in range(L):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(l)
-        g_one.append(g)
-    with torch.cuda.graph(g_mlp):
-        for l in range(L):
-            mlp(l)
-
-    def run_steps(n: int):
-        for _ in range(n // L):
-            g_all.replay()
-        for l in range(n % L):
-            g_one[l].replay()
-
-    run_steps(args.warmup)
-    torch.cuda.synchronize()
-
-    K = args.steps
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter()
-    start.record()
-    run_steps(K)
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall
-    ms_total = start.elapsed_time(stop)
-    ms_per_step = ms_total / K
-
-    # Dominant operation: the fused MLP, all L layers per replay, timed with HIP
-    # events on the launch stream.
-    n_mlp = max(1, K // L)
-    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g_mlp.replay()
-    m0.record()
-    for _ in range(n_mlp):
-        g_mlp.replay()
-    m1.record()
-    torch.cuda.synchronize()
-    mlp_ms = m0.elapsed_time(m1) / (n_mlp * L)
-
-    # Algorithmic bytes: every theta tensor once, plus the call's x and y.
-    lay0 = host_layer0
-    d = dims["d_model"]
-    mlp_bytes = sum(theta_bytes(lay0[f]) for f in ("gate", "up", "down")) + 2 * T * d + 2 * T * d
-    layer_bytes = (sum(theta_bytes(lay0[f]) for f in inputs.FAMILIES)
-                   + 2 * T * (d + width_qkv) + 2 * T * (dims["q"] + d) + 2 * T * (d + d))
-    mlp_gbs = mlp_bytes / (mlp_ms * 1e-3) / 1e9
-    layer_gbs = layer_bytes / (ms_per_step * 1e-3) / 1e9
-
-    cpu = None
-    if args.cpu_seconds > 0:
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            orc.qkv(h0["q"], h0["k"], h0["v"], a0["x_attn"])
-            orc.linear(h0["o"], a0["x_o"])
-            orc.mlp(h0["gate"], h0["up"], h0["down"], a0["x_mlp"])
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds and reps >= 2:
-                break
-        cpu = {"value": reps * T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{reps} passes of layer 0 (QKV + O + MLP, T=1, r={r}) in {el:.1f} s, "
-                         "single-threaded fp64 C oracle"}
-
-    out = {
-        "metric": METRIC,
-        "value": K * T / (ms_total * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "gemma3-1b-shaped layer decode (QKV fused + O + MLP fused)",
-                   "T": T, "rank": r, "layers_cycled": L, "G": L, "d_model": d, "q": dims["q"],
-                   "kv": dims["kv"], "d_ff": dims["ff"], "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "achieved": mlp_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": mlp_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "wl_mlp_fused (T=1), graph of all layers", "bytes_per_launch": mlp_bytes,
-                     "us_per_launch": mlp_ms * 1e3},
-        "layer_hbm_gbs": layer_gbs,
-        "layer_bytes": layer_bytes,
-        "wall_s_timed": wall,
-        "parity_rel_l2": parity,
-        "cpu_baseline": cpu,
-        "setup_s": t_gen,
-    }
+    wk = args.workload
+    if wk == "single":
+        res = run_single(args, torch, np, wl, inputs, orc)
+    elif wk == "layer-decode":
+        res = run_layers(args, torch, np, wl, inputs, orc, dims=inputs.GEMMA3_1B,
+                         r=args.rank if args.rank is not None else 32, T=1, n_layers=26, G=26,
+                         w0_std=0.02, seed=0, workload=wk, bound="hbm")
+    elif wk == "batched-decode":
+        res = run_layers(args, torch, np, wl, inputs, orc, dims=inputs.GEMMA3_1B,
+                         r=args.rank if args.rank is not None else 32, T=32, n_layers=26,
+                         G=1 if args.shared_w0 else 26, w0_std=0.02, seed=0, workload=wk, bound="hbm")
+    elif wk == "prefill":
+        res = run_layers(args, torch, np, wl, inputs, orc, dims=inputs.GEMMA3_1B,
+                         r=args.rank if args.rank is not None else 32, T=2048, n_layers=26, G=26,
+                         w0_std=0.02, seed=0, workload=wk, bound="mfma")
+    else:
+        T = args.tokens if args.tokens is not None else 1
+        res = run_layers(args, torch, np, wl, inputs, orc, dims=inputs.LARGE_5376,
+                         r=args.rank if args.rank is not None else 32, T=T, n_layers=1, G=1,
+                         w0_std=0.01, seed=1, workload=wk, bound="hbm" if T <= 64 else "mfma")
+    out = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,
+           "steps": res.pop("steps"), "warmup": res.pop("warmup"), "ms_per_step": res.pop("ms_per_step"),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic"}
+    out.update(res)
     print(json.dumps(out))
     return 0
 

@@ -154,9 +154,12 @@ wl_status wl_materialize_weff(const wl_theta *th, void *W_eff, void *hip_stream)
  * default), 1 forces the decode GEMV wherever it applies (V^T x computed by
  * every workgroup when V is small, else by a separate launch before it), 2
  * forces the matrix-core GEMM, 3 forces the decode GEMV with V^T x always
- * computed by a separate launch. Results agree within rounding in every
- * regime; the switch exists for tests and measurements. Process-wide; returns
- * the previous value, or -1 (and changes nothing) for any other argument. */
+ * computed by a separate launch, 4 forces the few-token path (split matrix-core
+ * products and an epilogue launch) wherever it applies (T <= 64, d_in <= 8192).
+ * Where a forced regime does not apply the matrix-core GEMM runs. Results agree
+ * within rounding in every regime; the switch exists for tests and
+ * measurements. Process-wide; returns the previous value, or -1 (and changes
+ * nothing) for any other argument. */
 int32_t wl_set_regime(int32_t regime);
 
 /* Static description of a status code. */

@@ -18,7 +18,7 @@
 namespace {
 
 thread_local std::string g_error;
-std::atomic<int> g_regime{0};   // 0 auto, 1 GEMV, 2 matrix-core GEMM, 3 GEMV always after a V^T x launch
+std::atomic<int> g_regime{0};   // 0 auto, 1 GEMV, 2 matrix-core GEMM, 3 GEMV always after a V^T x launch, 4 skinny
 
 constexpr size_t kAlign = 256;
 
@@ -85,28 +85,96 @@ void theta_ranges(const wl_theta *th, Range *out /* 4 */) {
 }
 
 // ---------------------------------------------------------------------------
+// Kernel regime of one projection: decode GEMV (T up to kGemvMaxTok), the
+// two-launch skinny path (a few tens of tokens), or the matrix-core GEMM.
+enum Kind { kKindGemv, kKindSkinny, kKindGemm };
+
+bool skinny_ok(int T, int d_in, int sum_r) {
+    (void)sum_r;
+    return T >= 1 && T <= wl::kSkMaxTok && d_in <= wl::kSkMaxDin;
+}
+
+Kind choose(int T, int d_in, int sum_r) {
+    const int regime = g_regime.load(std::memory_order_relaxed);
+    const int tt = wl::gemv_tokens_per_pass(d_in, T);
+    const bool sk = skinny_ok(T, d_in, sum_r);
+    switch (regime) {
+        case 1:
+        case 3: return tt ? kKindGemv : kKindGemm;
+        case 2: return kKindGemm;
+        case 4: return sk ? kKindSkinny : kKindGemm;
+        default: break;
+    }
+    if (T <= wl::kGemvMaxTok && tt) return kKindGemv;
+    return sk ? kKindSkinny : kKindGemm;
+}
+
 // Workspace layout. One layout function serves both wl_workspace_bytes and the
-// calls, so the two always agree. The decode region is always reserved, so the
-// size does not depend on the regime switch.
+// calls, so the two always agree. Every region any regime could use at this T
+// is reserved, so the size does not depend on the regime switch.
 //
 //   [0, 256)          reserved
 //   gemv_partial      fp32 3 x [kGemvMaxSlices][kGemvMaxTok][kMaxRank] V^T x slices
 //                     (decode regime; the matrix-core kernel computes V^T x itself)
+//   skinny part       fp32 [S][P][T][rows] split partials (T <= kSkMaxTok), the
+//                     largest of the call's projections
+//   skinny vpart      fp32 [n_vsl][n_ch][T][kMaxRank] V^T x slice partials
 //   h                 bf16 [T][d_ff] (MLP only)
 
 constexpr size_t kReservedBytes = 256;
 
 struct Layout {
     size_t gemv_partial = 0;
+    size_t sk_part = 0, sk_vpart = 0;
     size_t h = 0;
     size_t total = 0;
 };
+
+struct ProjShape {
+    int rows, d_in, P, n_ch, sum_r, n_vtx_ch;
+};
+
+// The projections a call runs, in order.
+int proj_shapes(int op, const wl_theta *const *th, ProjShape *out) {
+    auto nv = [](const wl_theta *const *t, int n) {
+        int c = 0;
+        for (int j = 0; j < n; ++j) c += t[j]->r > 0;
+        return c;
+    };
+    if (op == WL_OP_LINEAR) {
+        out[0] = {th[0]->d_out, th[0]->d_in, 1, 1, th[0]->r, nv(th, 1)};
+        return 1;
+    }
+    if (op == WL_OP_QKV) {
+        out[0] = {th[0]->d_out + th[1]->d_out + th[2]->d_out, th[0]->d_in, 1, 3, th[0]->r + th[1]->r + th[2]->r,
+                  nv(th, 3)};
+        return 1;
+    }
+    out[0] = {th[0]->d_out, th[0]->d_in, 2, 2, th[0]->r + th[1]->r, nv(th, 2)};
+    out[1] = {th[2]->d_out, th[2]->d_in, 1, 1, th[2]->r, nv(th + 2, 1)};
+    return 2;
+}
 
 Layout layout(int op, const wl_theta *const *th, int T) {
     Layout L;
     size_t off = kReservedBytes;
     L.gemv_partial = off;
     off = round_up(off + wl::kMaxChildren * wl::kGemvPartialPerChild * 4, kAlign);
+    ProjShape ps[2];
+    const int n = proj_shapes(op, th, ps);
+    size_t part = 0, vpart = 0;
+    for (int j = 0; j < n; ++j) {
+        if (!skinny_ok(T, ps[j].d_in, ps[j].sum_r)) continue;
+        const wl::SkinnyPlan p = wl::skinny_plan(ps[j].rows, ps[j].d_in, T, ps[j].P, ps[j].n_vtx_ch);
+        const size_t a = (size_t)p.S * ps[j].P * T * ps[j].rows * 4;
+        const size_t b = (size_t)p.n_vsl * ps[j].n_ch * T * wl::kMaxRank * 4;
+        part = a > part ? a : part;
+        vpart = b > vpart ? b : vpart;
+    }
+    L.sk_part = off;
+    off = round_up(off + part, kAlign);
+    L.sk_vpart = off;
+    off = round_up(off + vpart, kAlign);
     if (op == WL_OP_MLP) {
         L.h = off;
         off = round_up(off + (size_t)T * th[0]->d_out * 2, kAlign);
@@ -153,39 +221,53 @@ wl_status run_vtx(const wl::Child *ch, int n, PartialOf partial_c, const void *x
     return WL_OK;
 }
 
-// Tokens per decode pass, or 0 when the matrix-core regime is to be used.
-int gemv_tokens(int T, int d_in) {
-    const int regime = g_regime.load(std::memory_order_relaxed);
-    const int tt = wl::gemv_tokens_per_pass(d_in, T);
-    if (tt == 0 || regime == 2) return 0;
-    if (regime == 1 || regime == 3) return tt;
-    return T <= wl::kGemvMaxTok ? tt : 0;
-}
-
 // One projection over shared input x: children side by side in y (ldy = total
 // width), or the gate/up pair (pair = true, y = h).
 wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, const void *x, void *y, int ldy,
                    char *ws, const Layout &L, hipStream_t stream) {
     hipError_t e = hipSuccess;
-    const int tt = gemv_tokens(T, d_in);
+    int sum_r = 0, rows = 0;
+    for (int c = 0; c < n_ch; ++c) {
+        sum_r += ch[c].r;
+        rows += ch[c].d_out;
+    }
+    if (pair) rows = ch[0].d_out;
+    const Kind kind = choose(T, d_in, sum_r);
+    const int tt = kind == kKindGemv ? wl::gemv_tokens_per_pass(d_in, T) : 0;
     if (getenv("WL_LOG"))
         fprintf(stderr, "wl: proj n_ch=%d pair=%d d_in=%d T=%d -> %s (tt=%d)\n", n_ch, (int)pair, d_in, T,
-                tt ? "gemv" : "mfma", tt);
-    if (tt > 0) {
-        wl::GemvF g{};
-        int sum_r = 0;
+                kind == kKindGemv ? "gemv" : kind == kKindSkinny ? "skinny" : "mfma", tt);
+    if (kind == kKindSkinny) {
+        wl::Skinny g{};
+        int nv = 0;
         for (int c = 0; c < n_ch; ++c) {
             g.ch[c] = ch[c];
-            sum_r += ch[c].r;
+            if (ch[c].r > 0) g.vtx_ch[nv++] = c;
         }
         g.n_ch = n_ch;
         g.pair = pair;
         g.d_in = d_in;
-        g.rows = 0;
-        if (pair)
-            g.rows = ch[0].d_out;
-        else
-            for (int c = 0; c < n_ch; ++c) g.rows += ch[c].d_out;
+        g.rows = rows;
+        g.ldy = ldy;
+        g.T = T;
+        g.x = static_cast<const uint16_t *>(x);
+        g.y = static_cast<uint16_t *>(y);
+        g.part = reinterpret_cast<float *>(ws + L.sk_part);
+        g.vpart = reinterpret_cast<float *>(ws + L.sk_vpart);
+        const wl::SkinnyPlan p = wl::skinny_plan(rows, d_in, T, pair ? 2 : 1, nv);
+        g.S = p.S;
+        g.n_rowblk = p.n_rowblk;
+        g.kb_per_split = p.kb_per_split;
+        g.n_vsl = p.n_vsl;
+        g.n_vtx_wg = p.n_vtx_wg;
+        e = wl::launch_skinny(g, stream);
+    } else if (kind == kKindGemv) {
+        wl::GemvF g{};
+        for (int c = 0; c < n_ch; ++c) g.ch[c] = ch[c];
+        g.n_ch = n_ch;
+        g.pair = pair;
+        g.d_in = d_in;
+        g.rows = rows;
         g.ldy = ldy;
         g.T = T;
         g.x = static_cast<const uint16_t *>(x);
@@ -264,7 +346,7 @@ const char *wl_status_str(wl_status st) {
 const char *wl_last_error(void) { return g_error.c_str(); }
 
 int32_t wl_set_regime(int32_t regime) {
-    if (regime < 0 || regime > 3) return -1;
+    if (regime < 0 || regime > 4) return -1;
     return g_regime.exchange(regime);
 }
 

@@ -89,6 +89,39 @@ GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_redundant);
 hipError_t launch_gemv(const GemvF &g, const GemvPlan &plan, int tt, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
+// A few tens of tokens (8 < T <= kSkMaxTok), same result as Gemv (including pair
+// mode), in two launches: split-K matrix-core products into fp32 partials (and
+// V^T x slice partials from extra workgroups of the same launch), then an
+// epilogue launch that adds both in order.
+constexpr int kSkMaxTok = 64;
+constexpr int kSkMaxDin = 8192;
+constexpr int kSkMaxPartials = 8;     // split partials x pair x token blocks per output
+constexpr int kSkVtxTok = 8;          // tokens per V^T x workgroup
+constexpr int kSkVtxSlice = 512;      // inputs per V^T x workgroup
+constexpr int kSkEpiMaxLoads = 16384; // fp32 slice partials staged at once by one epilogue workgroup
+struct Skinny {
+    Child ch[kMaxChildren];
+    int n_ch;
+    int pair;
+    int d_in;
+    int rows;             // output rows (sum of d_out; d_ff in pair mode)
+    int ldy;
+    int T;
+    const uint16_t *x;    // bf16 [T][d_in]
+    uint16_t *y;          // bf16 [T][ldy]
+    float *part;          // fp32 [S][P][T][rows]
+    float *vpart;         // fp32 [n_vsl][n_ch][T][kMaxRank]
+    // plan
+    int S, n_rowblk, kb_per_split, n_vsl, n_vtx_wg;
+    int vtx_ch[kMaxChildren];   // children with r > 0, in order
+};
+struct SkinnyPlan {
+    int S = 1, n_rowblk = 0, kb_per_split = 0, n_vsl = 0, n_vtx_wg = 0;
+};
+SkinnyPlan skinny_plan(int rows, int d_in, int T, int P, int n_vtx_ch);
+hipError_t launch_skinny(const Skinny &g, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
 // Matrix-core GEMM for larger token counts, same result as Gemv (including pair
 // mode); V^T x is computed inside, from the x tiles it already loads. Output
 // tiles never span two children.

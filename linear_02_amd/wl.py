@@ -189,15 +189,15 @@ def wl_materialize_weff(th: dict, W_eff: torch.Tensor | None = None):
     return W_eff
 
 
-REGIME_AUTO, REGIME_GEMV, REGIME_MFMA, REGIME_GEMV_TWO_LAUNCH = 0, 1, 2, 3
+REGIME_AUTO, REGIME_GEMV, REGIME_MFMA, REGIME_GEMV_TWO_LAUNCH, REGIME_SKINNY = 0, 1, 2, 3, 4
 
 
 def set_regime(regime: int) -> int:
     """0 auto, 1 decode GEMV, 2 matrix-core GEMM, 3 decode GEMV always after a
-    separate V^T x launch; returns the previous setting."""
+    separate V^T x launch, 4 few-token split path; returns the previous setting."""
     prev = int(lib.wl_set_regime(regime))
     if prev < 0:
-        raise ValueError(f"regime {regime} is not 0, 1, 2 or 3")
+        raise ValueError(f"regime {regime} is not 0, 1, 2, 3 or 4")
     return prev
 
 

@@ -1,9 +1,10 @@
 """HIP graph capture of the library calls: every replay equals the eager result.
 
 The benchmark replays captured graphs, so captured calls must keep producing
-the eager bits: the workspace counters must come back to zero after every
-replay and nothing in the captured work may depend on state left by the host.
-Replays are interleaved with unrelated eager work and synchronizations.
+the eager bits: nothing in the captured work may depend on state left by the
+host or by an earlier replay. Replays are interleaved with unrelated eager work
+and synchronizations. T = 1 and 3 run the decode kernels, T = 40 the few-token
+split path.
 """
 from __future__ import annotations
 

@@ -3,9 +3,10 @@
 Every call goes through the C ABI (linear_02_amd.wl -> libwl.so). Floating-point
 cases must meet relL2 <= 2e-3 and |err| <= 8e-3 * bound per element; cases with
 small-integer inputs, whose every partial sum is exact in fp32 and whose outputs
-are exact in bf16, must match bit for bit. Both kernel regimes (wave-per-row GEMV
-with V^T x in the same launch or in a launch of its own, and matrix-core GEMM)
-are run on the same cases.
+are exact in bf16, must match bit for bit. All kernel regimes (wave-per-row GEMV
+with V^T x in the same launch or in a launch of its own, matrix-core GEMM, and
+the few-token split path) are run on the same cases (a forced regime that
+does not apply to a case runs the matrix-core GEMM).
 """
 from __future__ import annotations
 
@@ -33,9 +34,9 @@ def wl():
     return mod
 
 
-@pytest.fixture(params=["gemv", "mfma", "gemv2"])
+@pytest.fixture(params=["gemv", "mfma", "gemv2", "skinny"])
 def regime(request, wl):
-    prev = wl.set_regime({"gemv": 1, "mfma": 2, "gemv2": 3}[request.param])
+    prev = wl.set_regime({"gemv": 1, "mfma": 2, "gemv2": 3, "skinny": 4}[request.param])
     yield request.param
     wl.set_regime(prev)
 
@@ -70,6 +71,10 @@ LINEAR_CASES = [
     (264, 520, 0, 9),         # no low-rank term
     (520, 264, 32, 33),
     (1152, 1536, 16, 130),    # several token tiles with a ragged tail
+    (1152, 1152, 32, 32),     # batched decode: one full 32-token block
+    (6912, 1152, 32, 17),     # long input axis, many splits, ragged tokens
+    (1024, 1152, 4, 64),      # two token blocks
+    (136, 129, 17, 12),       # ragged rows and input axis
 ]
 
 
@@ -197,7 +202,7 @@ def test_qkv_mixed_children(wl, orc, regime):
 # -- wl_mlp_fused ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("d_model,d_ff,r,T", [
-    (1152, 6912, 4, 1), (1152, 6912, 32, 1), (264, 520, 16, 3), (264, 520, 32, 33)])
+    (1152, 6912, 4, 1), (1152, 6912, 32, 1), (264, 520, 16, 3), (264, 520, 32, 33), (1152, 6912, 32, 32)])
 def test_mlp_matches_oracle(wl, orc, regime, d_model, d_ff, r, T):
     g = gen(300 + d_ff + r + T)
     gate = inputs.theta(g, d_model, d_ff, r)
