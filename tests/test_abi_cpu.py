@@ -128,7 +128,7 @@ def test_workspace_bytes_grows_with_tokens_and_rejects_bad_args(wl):
     d = theta(W0=A + 0x200000, d_in=6912, d_out=1152, r=32)
     mlp_arr = (ctypes.POINTER(wl.Theta) * 3)(ctypes.pointer(g), ctypes.pointer(u), ctypes.pointer(d))
     mlp = [wl.lib.wl_workspace_bytes(2, mlp_arr, 3, T) for T in (1, 64, 2048)]
-    assert mlp == sorted(mlp) and mlp[-1] - mlp[0] >= (2048 - 1) * 6912 * 2
+    assert mlp == sorted(mlp) and mlp[-1] >= 2048 * 6912 * 2
     assert wl.lib.wl_workspace_bytes(0, arr, 2, 1) == 0      # wrong count
     assert wl.lib.wl_workspace_bytes(7, arr, 1, 1) == 0      # unknown op
     assert wl.lib.wl_workspace_bytes(0, arr, 1, -1) == 0
