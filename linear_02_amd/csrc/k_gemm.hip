@@ -14,7 +14,8 @@
 // each wave owns TM x TN 32x32 blocks, each the accumulator of one
 // v_mfma_f32_32x32x16_bf16 chain. The input axis is walked BK at a time through
 // a ring of D LDS stages filled by direct-to-LDS loads (global_load_lds, 16
-// bytes per lane, no registers), D-1 stages in flight while one is multiplied.
+// bytes per lane, no registers), D-1 stages in flight while one is multiplied,
+// one barrier per step.
 // LDS rows of BK bf16 keep their 16-byte pieces XOR-swizzled by the row index
 // so that the fragment reads are free of bank conflicts.
 //
@@ -79,6 +80,7 @@ struct Cfg {
     static constexpr int LDS_PIECES = TILE_PIECES > VT_PIECES ? TILE_PIECES : VT_PIECES;
     static_assert(A_PIECES % kThreads == 0 && B_PIECES % kThreads == 0, "tile pieces must split evenly");
     static_assert(D >= 2 && D <= 4 && (D - 1) * PER_STAGE <= 63, "stages in flight must fit vmcnt");
+    static_assert(D - 2 <= 2, "wait counts cover at most two stages ahead");
     static_assert((BK / 16) % WN == 0, "V^T x K steps must split evenly over the WN waves");
 };
 
@@ -263,19 +265,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(Gemm g) {
         }
     };
 
+    // One barrier per step: after it, stage kt has landed for every wave and every
+    // wave has finished step kt - 1, so that step's slot takes stage kt + D - 1.
     for (int s0 = 0; s0 < D - 1 && s0 < nk; ++s0) issue(s0, s0);
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + D - 1 < nk) issue(kt + D - 1, (kt + D - 1) % D);
-        // Wait for this wave's loads of stage kt: the later stages may stay in flight.
-        const int ahead = min(D - 1, nk - 1 - kt);
-        if (ahead >= 3) wait_vm<3 * C::PER_STAGE>();
-        else if (ahead == 2) wait_vm<2 * C::PER_STAGE>();
+        // This wave's loads of stage kt are done; up to D - 2 later stages stay in flight.
+        const int ahead = min(D - 2, nk - 1 - kt);
+        if (ahead >= 2) wait_vm<2 * C::PER_STAGE>();
         else if (ahead == 1) wait_vm<C::PER_STAGE>();
         else wait_vm<0>();
-        barrier();                                    // every wave's part of stage kt has landed
+        barrier();
+        if (kt + D - 1 < nk) issue(kt + D - 1, (kt + D - 1) % D);
         compute(lds + (kt % D) * C::STAGE_PIECES);
-        barrier();                                    // slot kt % D is free for reuse
     }
+    barrier();                                        // the ring is free for the epilogue
 
     // ---- epilogue ----
     // Lane (fr, fk) of block (i, j) holds output column o = n0 + (wn*TN + j)*32 + fr
@@ -397,18 +400,57 @@ hipError_t launch_nv(const Gemm &g, hipStream_t stream) {
 
 }  // namespace
 
-// Tile configuration (waves M x N, 32x32 blocks per wave M x N, K depth, LDS
-// stages): chosen by measurement on the layer shapes; overridable at build time.
+// Tile configurations (waves M x N, 32x32 blocks per wave M x N, K depth, LDS
+// stages), chosen by measurement on the layer shapes; overridable at build time.
+// The largest tile whose grid still gives most compute units a workgroup is used.
+#ifndef WL_GEMM_TILE_BIG
+#define WL_GEMM_TILE_BIG 4, 2, 2, 4, 64, 2
+#endif
+#ifndef WL_GEMM_TILE_BIG_PAIR
+#define WL_GEMM_TILE_BIG_PAIR 4, 2, 2, 2, 64, 2
+#endif
 #ifndef WL_GEMM_TILE
 #define WL_GEMM_TILE 2, 2, 2, 2, 64, 2
 #endif
 #ifndef WL_GEMM_TILE_PAIR
 #define WL_GEMM_TILE_PAIR 2, 2, 2, 2, 64, 2
 #endif
+#ifndef WL_GEMM_TILE_SMALL
+#define WL_GEMM_TILE_SMALL 2, 2, 2, 1, 64, 2
+#endif
+#ifndef WL_GEMM_TILE_SMALL_PAIR
+#define WL_GEMM_TILE_SMALL_PAIR 2, 2, 2, 1, 64, 2
+#endif
+
+namespace {
+
+constexpr int kFillTiles = 232;   // workgroups that count as filling the 256 compute units
+
+template <int WM, int WN, int TM, int TN, int BK, int D>
+int tiles_of(const Gemm &g) {
+    constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+    int n_nt = 0;
+    if (g.pair)
+        n_nt = (g.ch[0].d_out + BN - 1) / BN;
+    else
+        for (int c = 0; c < g.n_ch; ++c) n_nt += (g.ch[c].d_out + BN - 1) / BN;
+    return n_nt * ((g.T + BM - 1) / BM);
+}
+
+}  // namespace
 
 hipError_t launch_gemm(const Gemm &g, hipStream_t stream) {
-    if (g.pair) return launch_nv<WL_GEMM_TILE_PAIR, 2>(g, stream);
-    return launch_nv<WL_GEMM_TILE, 1>(g, stream);
+    int max_r = 0;
+    for (int c = 0; c < (g.pair ? 2 : g.n_ch); ++c) max_r = g.ch[c].r > max_r ? g.ch[c].r : max_r;
+    if (g.pair) {
+        if (max_r == 0 && tiles_of<WL_GEMM_TILE_BIG_PAIR>(g) >= kFillTiles)
+            return launch_nv<WL_GEMM_TILE_BIG_PAIR, 2>(g, stream);
+        if (tiles_of<WL_GEMM_TILE_PAIR>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_PAIR, 2>(g, stream);
+        return launch_nv<WL_GEMM_TILE_SMALL_PAIR, 2>(g, stream);
+    }
+    if (max_r <= 32 && tiles_of<WL_GEMM_TILE_BIG>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_BIG, 1>(g, stream);
+    if (tiles_of<WL_GEMM_TILE>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE, 1>(g, stream);
+    return launch_nv<WL_GEMM_TILE_SMALL, 1>(g, stream);
 }
 
 }  // namespace wl

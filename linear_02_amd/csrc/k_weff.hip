@@ -7,9 +7,10 @@
 // The low-rank product U V^T is a contraction over the rank only (K = r <= 64),
 // done on the matrix cores: A = U (rows o, contiguous in k) and B = V (columns
 // i, contiguous in k) both load straight from global memory as 16-byte pieces.
-// The fp32 result is combined with the s-scaled W0 element and rounded once.
-// Each wave owns a 32-row x 64-column tile (two 32x32 MFMA outputs), so every
-// W0/W_eff row segment it touches is 128 contiguous bytes.
+// The kernel is bound by memory traffic (W0 read and W_eff written, 2 bytes each
+// per element), so the fp32 product goes through LDS to be read back along rows:
+// every lane then reads W0 and writes W_eff in 16-byte pieces, 256 contiguous
+// bytes per 16 lanes. The W0 pieces are loaded before the products start.
 #include "wl_device.h"
 #include "wl_kernels.h"
 
@@ -18,14 +19,16 @@ namespace wl {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int TM = 128, TN = 64;   // workgroup tile: rows o x columns i
+constexpr int TM = 128, TN = 128;             // workgroup tile: rows o x columns i
+constexpr int LDT = TN + 4;                   // fp32 row stride of the staged product
+constexpr int kChunks = TM * TN / 8 / kThreads;   // 16-byte pieces per thread
 
 __device__ __forceinline__ u32x4 load8(const uint16_t *p, int row, int ld, int k0, int r, bool ok) {
     // bf16 row[k0 .. k0+8) of a [*][r] matrix, zero past r or when !ok.
     u32x4 v{0u, 0u, 0u, 0u};
     if (!ok) return v;
     if ((r & 7) == 0) {
-        if (k0 < r) v = *reinterpret_cast<const u32x4 *>(p + (size_t)row * ld + k0);
+        if (k0 < r) v = ldg(reinterpret_cast<const u32x4 *>(p + (size_t)row * ld + k0));
         return v;
     }
 #pragma unroll
@@ -37,45 +40,85 @@ __device__ __forceinline__ u32x4 load8(const uint16_t *p, int row, int ld, int k
 }
 
 __global__ __launch_bounds__(kThreads) void weff_kernel(Weff w) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ float prod[TM * LDT];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int fr = lane & 31, fk = lane >> 5;
-    const int o0 = blockIdx.y * TM + wave * 32;
-    const int i0 = blockIdx.x * TN;
-    if (o0 >= w.d_out) return;
+    const int ob = blockIdx.y * TM, ib = blockIdx.x * TN;
+    const int nch = w.d_in >> 3;
 
-    f32x16 acc[2];
+    // This thread's pieces: row ob + c / 16, columns ib + 8 * (c % 16), c = tid + 256 m.
+    u32x4 w0[kChunks];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
-
-    for (int k0 = 0; k0 < w.r; k0 += 16) {
-        const int kb = k0 + 8 * fk;
-        const u32x4 a = load8(w.U, o0 + fr, w.r, kb, w.r, o0 + fr < w.d_out);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int i = i0 + j * 32 + fr;
-            const u32x4 b = load8(w.V, i, w.r, kb, w.r, i < w.d_in);
-            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                            __builtin_bit_cast(bf16x8, b), acc[j], 0, 0, 0);
-        }
+    for (int m = 0; m < kChunks; ++m) {
+        const int c = tid + m * kThreads, o = min(ob + c / 16, w.d_out - 1), j = min((ib >> 3) + c % 16, nch - 1);
+        w0[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w.W0) + (size_t)o * nch + j);
     }
 
-    // Lane (fr, fk) of output tile j holds column i = i0 + 32j + fr, rows
-    // o0 + 8*(e/4) + 4*fk + (e%4).
+    if (w.r > 0) {
+        // Wave: rows ob + 32 * wave .. +32, all TN columns (four 32x32 outputs).
+        f32x16 acc[TN / 32];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int o = o0 + 8 * (e >> 2) + 4 * fk + (e & 3);
-        if (o >= w.d_out) continue;
-        const float sv = w.s ? w.s[o] : 1.0f;
+        for (int j = 0; j < TN / 32; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int i = i0 + j * 32 + fr;
-            if (i < w.d_in) {
-                const size_t idx = (size_t)o * w.d_in + i;
-                w.W_eff[idx] = f_bf16(sv * bf16_f(w.W0[idx]) + acc[j][e]);
+            for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+        // All U and V pieces (at most kMaxRank / 16 steps) are loaded before the products.
+        constexpr int kSteps = kMaxRank / 16;
+        const int o = ob + wave * 32 + fr;
+        u32x4 a[kSteps], b[kSteps][TN / 32];
+#pragma unroll
+        for (int q = 0; q < kSteps; ++q) {
+            const int kb = 16 * q + 8 * fk;
+            a[q] = load8(w.U, o, w.r, kb, w.r, o < w.d_out && 16 * q < w.r);
+#pragma unroll
+            for (int j = 0; j < TN / 32; ++j) {
+                const int i = ib + j * 32 + fr;
+                b[q][j] = load8(w.V, i, w.r, kb, w.r, i < w.d_in && 16 * q < w.r);
             }
         }
+#pragma unroll
+        for (int q = 0; q < kSteps; ++q) {
+            if (16 * q >= w.r) break;
+#pragma unroll
+            for (int j = 0; j < TN / 32; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[q]),
+                                                                __builtin_bit_cast(bf16x8, b[q][j]), acc[j], 0, 0, 0);
+        }
+        // Lane (fr, fk) of output j holds column 32j + fr, rows 8*(e/4) + 4*fk + (e%4).
+        // The empty asm statements keep these stores apart: this compiler merges
+        // them into paired LDS stores with wrong offsets for this row stride.
+        float *base = prod + (wave * 32 + 4 * fk) * LDT + fr;
+#pragma unroll
+        for (int j = 0; j < TN / 32; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                base[(8 * (e >> 2) + (e & 3)) * LDT + j * 32] = acc[j][e];
+                asm volatile("" ::: "memory");
+            }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int m = 0; m < kChunks; ++m) {
+        const int c = tid + m * kThreads, ol = c / 16, jl = c % 16;
+        const int o = ob + ol, j = (ib >> 3) + jl;
+        if (o >= w.d_out || j >= nch) continue;
+        float lr[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (w.r > 0) {
+            const f32x4 p0 = *reinterpret_cast<const f32x4 *>(&prod[ol * LDT + 8 * jl]);
+            const f32x4 p1 = *reinterpret_cast<const f32x4 *>(&prod[ol * LDT + 8 * jl + 4]);
+            lr[0] = p0.x; lr[1] = p0.y; lr[2] = p0.z; lr[3] = p0.w;
+            lr[4] = p1.x; lr[5] = p1.y; lr[6] = p1.z; lr[7] = p1.w;
+        }
+        const float sv = w.s ? ldg(w.s + o) : 1.0f;
+        const uint32_t wv[4] = {w0[m].x, w0[m].y, w0[m].z, w0[m].w};
+        uint32_t out[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float v0 = sv * bf16_f(wv[q] & 0xFFFFu) + lr[2 * q];
+            const float v1 = sv * bf16_f(wv[q] >> 16) + lr[2 * q + 1];
+            out[q] = (uint32_t)f_bf16(v0) | ((uint32_t)f_bf16(v1) << 16);
+        }
+        reinterpret_cast<u32x4 *>(w.W_eff)[(size_t)o * nch + j] = u32x4{out[0], out[1], out[2], out[3]};
     }
 }
 
