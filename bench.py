@@ -24,6 +24,13 @@ Workloads (``--workload``; the default is the one the headline metric is quoted 
   large           a hidden-5376 layer: Q/K/V 5376 -> 8192 + 2048 + 2048, O 8192 ->
                   5376, MLP 5376 -> 21504 -> 5376, r = 32, T = --tokens (1 or
                   512). W0 ~ N(0, 0.01), seed 1. A step is one layer.
+  copy            a plain 512 MiB device copy, the reference that scales the
+                  FETCH_SIZE / WRITE_SIZE hardware counters to bytes.
+
+For hardware-counter passes, --dominant-only runs just the dominant call, and
+--traffic-from turns the passes' counter files into the per-call HBM traffic
+that the roofline record reports (profiles/traffic_*.txt, tied to a digest of
+the kernel sources; a record whose kernels changed since reports null).
 
 Inputs are seeded synthetic draws (linear_02_amd.inputs) with W0 ~ N(0, 0.02)
 (0.01 for large), s ~ 1 + N(0, 0.01), U, V ~ N(0, 0.01), x ~ N(0, 1), already
@@ -51,7 +58,7 @@ if REPO not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix cores
 METRIC = "tokens/s + achieved HBM GB/s (T=1) / MFMA TFLOP/s (T=2048) per rank"
-WORKLOADS = ("layer-decode", "single", "batched-decode", "prefill", "large")
+WORKLOADS = ("layer-decode", "single", "batched-decode", "prefill", "large", "copy")
 DEFAULT_STEPS = {"layer-decode": 2600, "single": 4000, "batched-decode": 200, "prefill": 260, "large": 40}
 
 
@@ -65,6 +72,12 @@ def parse_args():
     p.add_argument("--tokens", type=int, default=None, help="T for the large workload (1 or 512)")
     p.add_argument("--shared-w0", action="store_true", help="batched-decode: one W0 for all layers (G=1)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0 skips it)")
+    p.add_argument("--dominant-only", action="store_true",
+                   help="run only the dominant call (for hardware-counter passes) and print the call count")
+    p.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                   help="write the dominant call's HBM traffic from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                        "counter files (of a --dominant-only run and of --workload copy) and exit")
+    p.add_argument("--traffic-calls", type=int, default=0, help="dominant calls in the counted run")
     return p.parse_args()
 
 
@@ -256,6 +269,14 @@ def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_
         o(l)
         mlp(l)
 
+    if args.dominant_only:
+        n = args.steps if args.steps is not None else n_layers
+        for i in range(n):
+            mlp(i % n_layers)
+        torch.cuda.synchronize()
+        print(json.dumps({"dominant_calls": n, "call": "wl_mlp_fused", "workload": workload}))
+        return None
+
     # Parity spot check of layer 0 against the oracle (eager, outside the timed region).
     layer_step(0)
     torch.cuda.synchronize()
@@ -401,6 +422,13 @@ def run_single(args, torch, np, wl, inputs, orc):
     x = x_host.to(dev)
     y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
     ws = torch.zeros(wl.workspace_bytes(wl.OP_LINEAR, [ths[0]], T), dtype=torch.uint8, device=dev)
+    if args.dominant_only:
+        n = args.steps if args.steps is not None else copies
+        for i in range(n):
+            wl.wl_linear(ths[i % copies], x, y=y, ws=ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"dominant_calls": n, "call": "wl_linear", "workload": "single"}))
+        return None
     wl.wl_linear(ths[0], x, y=y, ws=ws)
     torch.cuda.synchronize()
     parity = {"linear": rel_l2(np, y, orc.linear(host, x_host)[0])}
@@ -425,8 +453,69 @@ def run_single(args, torch, np, wl, inputs, orc):
     }
 
 
+COPY_BYTES = 512 << 20
+
+
+def run_copy(args, torch):
+    """A plain device copy of known size: the reference for scaling the FETCH_SIZE and
+    WRITE_SIZE counters to bytes."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    K = args.steps if args.steps is not None else 20
+    for _ in range(K):
+        torch.mul(src, 1.0, out=dst)      # one elementwise kernel: reads and writes the buffer once
+    torch.cuda.synchronize()
+    return {"metric": "device copy for counter calibration", "bytes_read_per_copy": COPY_BYTES,
+            "bytes_written_per_copy": COPY_BYTES, "copies": K}
+
+
+def _counter_rows(path: str, counter: str):
+    import csv
+    rows = []
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                rows.append((row["Kernel_Name"], float(row["Counter_Value"])))
+    return rows
+
+
+def write_traffic(args) -> int:
+    """Per-call HBM bytes of the dominant call from the counter passes, each counter
+    scaled by what it reads for the plain copy of known size."""
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.traffic_from
+    copy_f = [v for n, v in _counter_rows(cfetch_csv, "FETCH_SIZE") if "elementwise" in n or "copy" in n.lower()]
+    copy_w = [v for n, v in _counter_rows(cwrite_csv, "WRITE_SIZE") if "elementwise" in n or "copy" in n.lower()]
+    # The copy dispatches are the ones that move the full buffer: the largest values.
+    kf = COPY_BYTES / (max(copy_f) * 1024.0)
+    kw = COPY_BYTES / (max(copy_w) * 1024.0)
+    f_kib = sum(v for n, v in _counter_rows(fetch_csv, "FETCH_SIZE") if "wl::" in n)
+    w_kib = sum(v for n, v in _counter_rows(write_csv, "WRITE_SIZE") if "wl::" in n)
+    calls = args.traffic_calls
+    if calls <= 0:
+        print("--traffic-calls is required", file=sys.stderr)
+        return 2
+    per_call = (f_kib * 1024.0 * kf + w_kib * 1024.0 * kw) / calls
+    r = args.rank if args.rank is not None else (4 if args.workload == "single" else 32)
+    T = {"single": 1, "layer-decode": 1, "batched-decode": 32, "prefill": 2048}.get(
+        args.workload, args.tokens if args.tokens is not None else 1)
+    path = os.path.join(REPO, "profiles", f"traffic_{args.workload}_r{r}_T{T}.txt")
+    with open(path, "w") as f:
+        f.write(f"# HBM traffic of the dominant call of bench.py --workload {args.workload} (r={r}, T={T}),\n"
+                f"# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE passes over a --dominant-only run,\n"
+                f"# each scaled by the counter's reading for a plain {COPY_BYTES >> 20} MiB device copy.\n")
+        f.write(f"sources = {source_digest()}\n")
+        f.write(f"calls = {calls}\n")
+        f.write(f"fetch_kib_total = {f_kib:.1f}\nwrite_kib_total = {w_kib:.1f}\n")
+        f.write(f"copy_fetch_scale = {kf:.4f}\ncopy_write_scale = {kw:.4f}\n")
+        f.write(f"bytes_per_call = {per_call:.0f}\n")
+    print(path)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
+    if args.traffic_from:
+        return write_traffic(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path is single-device; how it would shard is described in DESIGN.md)", file=sys.stderr)
@@ -441,8 +530,11 @@ def main() -> int:
     from oracle import oracle as oracle_mod
 
     torch.cuda.set_device(0)
-    orc = oracle_mod.default()
     wk = args.workload
+    if wk == "copy":
+        print(json.dumps(run_copy(args, torch)))
+        return 0
+    orc = oracle_mod.default()
     if wk == "single":
         res = run_single(args, torch, np, wl, inputs, orc)
     elif wk == "layer-decode":
@@ -462,6 +554,8 @@ def main() -> int:
         res = run_layers(args, torch, np, wl, inputs, orc, dims=inputs.LARGE_5376,
                          r=args.rank if args.rank is not None else 32, T=T, n_layers=1, G=1,
                          w0_std=0.01, seed=1, workload=wk, bound="hbm" if T <= 64 else "mfma")
+    if res is None:
+        return 0
     out = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,
            "steps": res.pop("steps"), "warmup": res.pop("warmup"), "ms_per_step": res.pop("ms_per_step"),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
