@@ -58,7 +58,10 @@ constexpr size_t kGemvPartialPerChild = (size_t)kGemvMaxSlices * kGemvMaxTok * k
 constexpr int kRedMaxTok = 2;                 // redundant V^T x: at most 2 tokens per pass
 constexpr int kRedMaxPieces = 20;             //   and 20 16-byte pieces of V per lane
 constexpr int kRedUnits = 4;                  //   one unit per wave
-constexpr long long kRedMaxTraffic = 4ll << 20;  //   V re-read by all workgroups
+#ifndef WL_RED_CAP_MB
+#define WL_RED_CAP_MB 4
+#endif
+constexpr long long kRedMaxTraffic = (long long)WL_RED_CAP_MB << 20;  //   V re-read by all workgroups
 
 struct GemvF {
     Child ch[kMaxChildren];
