@@ -119,7 +119,7 @@ __device__ __forceinline__ void barrier() {
 }
 
 template <int WM, int WN, int TM, int TN, int BK, int P, int D, int NV>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(Gemm g) {
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(Gemm g) {
     using C = Cfg<WM, WN, TM, TN, BK, P, D, NV>;
     constexpr int BM = C::BM, BN = C::BN, KP = C::KP, NT = C::kThreads;
     constexpr int NVA = NV > 0 ? NV : 1;
@@ -205,69 +205,143 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(Gemm g) {
             if constexpr (NV > 0) {
                 // V rows [kt*BK, kt*BK + BK): BK*r bf16, contiguous, copied as they are.
                 const int r = ch[p]->r;
-                const u32x4 *vg = reinterpret_cast<const u32x4 *>(ch[p]->V);
+                const u32x4 *vgp = reinterpret_cast<const u32x4 *>(ch[p]->V);
                 const int q_end = BK * r / 8, q_all = d_in * r / 8, q0 = kt * BK * r / 8;
 #pragma unroll
                 for (int h = 0; h < C::V_PER; ++h) {
                     const int q = h * NT + tid;
-                    const u32x4 *src = (q < q_end && q0 + q < q_all) ? vg + q0 + q : zero;
+                    const u32x4 *src = (q < q_end && q0 + q < q_all) ? vgp + q0 + q : zero;
                     lds_dma16(src, bst + C::B_PIECES + h * NT + wave * kWave);
                 }
             }
         }
     };
 
-    const int fr = lane & 31, fk = lane >> 5;   // fragment row / column, K half of a 16-step
-    auto compute = [&](const u32x4 *st) {
+
+    // Full steps (the whole 64-wide K block inside d_in) take precomputed per-lane
+    // piece offsets: tile rows past T or d_out read the last valid row instead (their
+    // outputs are never stored), so no step but a partial last one needs a check.
+    int a_off[C::A_PER];
 #pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            const int kc = 2 * s + fk;
-            u32x4 a[TM], b[P][TN];
+    for (int h = 0; h < C::A_PER; ++h) {
+        const int q = h * NT + tid, row = q / KP, kc = (q % KP) ^ swz_key<KP>(row);
+        a_off[h] = min(m0 + row, g.T - 1) * nch + kc;
+    }
+    int b_off[P][C::B_PER];
+    const u32x4 *wg[P];
+    const u32x4 *vg[P];
+    int vstep[P];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) a[i] = st[swz<KP>(wm * TM * 32 + i * 32 + fr, kc)];
+    for (int p = 0; p < P; ++p) {
+        wg[p] = reinterpret_cast<const u32x4 *>(ch[p]->W0);
+        vg[p] = reinterpret_cast<const u32x4 *>(ch[p]->V);
+        vstep[p] = BK * ch[p]->r / 8;
+        const int dout_p = ch[p]->d_out;
 #pragma unroll
-            for (int p = 0; p < P; ++p)
+        for (int h = 0; h < C::B_PER; ++h) {
+            const int q = h * NT + tid, row = q / KP, kc = (q % KP) ^ swz_key<KP>(row);
+            b_off[p][h] = min(n0 + row, dout_p - 1) * nch + kc;
+        }
+    }
+    auto issue_full = [&](int kt, int sl) {
+        u32x4 *st = lds + sl * C::STAGE_PIECES;
+        const u32x4 *xk = xg + kt * KP;
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    b[p][j] = st[C::A_PIECES + p * (C::B_PIECES + C::V_SLOTS) + swz<KP>(wn * TN * 32 + j * 32 + fr, kc)];
+        for (int h = 0; h < C::A_PER; ++h) lds_dma16(xk + a_off[h], st + h * NT + wave * kWave);
 #pragma unroll
-            for (int p = 0; p < P; ++p)
+        for (int p = 0; p < P; ++p) {
+            u32x4 *bst = st + C::A_PIECES + p * (C::B_PIECES + C::V_SLOTS);
+            const u32x4 *wk = wg[p] + kt * KP;
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) acc[p][i][j] = mfma(a[i], b[p][j], acc[p][i][j]);
+            for (int h = 0; h < C::B_PER; ++h) lds_dma16(wk + b_off[p][h], bst + h * NT + wave * kWave);
             if constexpr (NV > 0) {
-                if (s % WN == wn) {
-                    // V fragment: lane (fr, fk) needs V[i][k] for the 8 stage rows
-                    // i = 16s + 8fk + e and rank k = 32v + fr.
+                // Slots past the stage's BK * r / 8 pieces are never read: they repeat the
+                // last piece. A child without a rank term (r = 0, V absent) reads the zero piece.
+                const u32x4 *vk = vg[p] + kt * vstep[p];
 #pragma unroll
-                    for (int p = 0; p < P; ++p) {
-                        const int r = ch[p]->r;
-                        const uint16_t *vl = reinterpret_cast<const uint16_t *>(
-                            st + C::A_PIECES + p * (C::B_PIECES + C::V_SLOTS) + C::B_PIECES);
+                for (int h = 0; h < C::V_PER; ++h)
+                    lds_dma16(vstep[p] > 0 ? vk + min(h * NT + tid, vstep[p] - 1) : zero,
+                              bst + C::B_PIECES + h * NT + wave * kWave);
+            }
+        }
+    };
+    auto issue_any = [&](int kt, int sl) {
+        if ((kt + 1) * BK <= d_in)
+            issue_full(kt, sl);
+        else
+            issue(kt, sl);
+    };
+
+
+    const int fr = lane & 31, fk = lane >> 5;   // fragment row / column, K half of a 16-step
+    // Fragments of 16-wide step s of a stage; the next step's fragments are read
+    // while the current step's products run (two register sets).
+    auto load_frags = [&](const u32x4 *st, int s, u32x4 (&a)[TM], u32x4 (&b)[P][TN]) {
+        const int kc = 2 * s + fk;
 #pragma unroll
-                        for (int v = 0; v < NV; ++v) {
-                            const int k = 32 * v + fr;
-                            u32x4 vf = {0u, 0u, 0u, 0u};
-                            if (k < r) {
-                                const uint16_t *col = vl + (16 * s + 8 * fk) * r + k;
-                                vf.x = (uint32_t)col[0] | ((uint32_t)col[r] << 16);
-                                vf.y = (uint32_t)col[2 * r] | ((uint32_t)col[3 * r] << 16);
-                                vf.z = (uint32_t)col[4 * r] | ((uint32_t)col[5 * r] << 16);
-                                vf.w = (uint32_t)col[6 * r] | ((uint32_t)col[7 * r] << 16);
-                            }
+        for (int i = 0; i < TM; ++i) a[i] = st[swz<KP>(wm * TM * 32 + i * 32 + fr, kc)];
 #pragma unroll
-                            for (int i = 0; i < TM; ++i) accv[p][i][v] = mfma(a[i], vf, accv[p][i][v]);
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                b[p][j] = st[C::A_PIECES + p * (C::B_PIECES + C::V_SLOTS) + swz<KP>(wn * TN * 32 + j * 32 + fr, kc)];
+    };
+    auto step_mfma = [&](const u32x4 *st, int s, const u32x4 (&a)[TM], const u32x4 (&b)[P][TN]) {
+        // Diagonal order: every fragment is used early and late in the step, so all
+        // of them stay in registers of their own (and the next step's reads can be
+        // issued before this step's products) instead of sharing one register set.
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int d = 0; d < TN; ++d)
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const int j = (i + d) % TN;
+                    acc[p][i][j] = mfma(a[i], b[p][j], acc[p][i][j]);
+                }
+        if constexpr (NV > 0) {
+            if (s % WN == wn) {
+                // V fragment: lane (fr, fk) needs V[i][k] for the 8 stage rows
+                // i = 16s + 8fk + e and rank k = 32v + fr.
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    const int r = ch[p]->r;
+                    const uint16_t *vl = reinterpret_cast<const uint16_t *>(
+                        st + C::A_PIECES + p * (C::B_PIECES + C::V_SLOTS) + C::B_PIECES);
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) {
+                        const int k = 32 * v + fr;
+                        u32x4 vf = {0u, 0u, 0u, 0u};
+                        if (k < r) {
+                            const uint16_t *col = vl + (16 * s + 8 * fk) * r + k;
+                            vf.x = (uint32_t)col[0] | ((uint32_t)col[r] << 16);
+                            vf.y = (uint32_t)col[2 * r] | ((uint32_t)col[3 * r] << 16);
+                            vf.z = (uint32_t)col[4 * r] | ((uint32_t)col[5 * r] << 16);
+                            vf.w = (uint32_t)col[6 * r] | ((uint32_t)col[7 * r] << 16);
                         }
+#pragma unroll
+                        for (int i = 0; i < TM; ++i) accv[p][i][v] = mfma(a[i], vf, accv[p][i][v]);
                     }
                 }
             }
         }
     };
+    static_assert((BK / 16) % 2 == 0, "steps are taken in pairs");
+    auto compute = [&](const u32x4 *st) {
+        u32x4 a0[TM], b0[P][TN], a1[TM], b1[P][TN];
+        load_frags(st, 0, a0, b0);
+#pragma unroll
+        for (int s = 0; s < BK / 16; s += 2) {
+            load_frags(st, s + 1, a1, b1);
+            step_mfma(st, s, a0, b0);
+            if (s + 2 < BK / 16) load_frags(st, s + 2, a0, b0);
+            step_mfma(st, s + 1, a1, b1);
+        }
+    };
 
     // One barrier per step: after it, stage kt has landed for every wave and every
     // wave has finished step kt - 1, so that step's slot takes stage kt + D - 1.
-    for (int s0 = 0; s0 < D - 1 && s0 < nk; ++s0) issue(s0, s0);
+    for (int s0 = 0; s0 < D - 1 && s0 < nk; ++s0) issue_any(s0, s0);
     for (int kt = 0; kt < nk; ++kt) {
         // This wave's loads of stage kt are done; up to D - 2 later stages stay in flight.
         const int ahead = min(D - 2, nk - 1 - kt);
@@ -275,7 +349,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(Gemm g) {
         else if (ahead == 1) wait_vm<C::PER_STAGE>();
         else wait_vm<0>();
         barrier();
-        if (kt + D - 1 < nk) issue(kt + D - 1, (kt + D - 1) % D);
+        if (kt + D - 1 < nk) issue_any(kt + D - 1, (kt + D - 1) % D);
         compute(lds + (kt % D) * C::STAGE_PIECES);
     }
     barrier();                                        // the ring is free for the epilogue
@@ -389,20 +463,21 @@ hipError_t launch_cfg(const Gemm &g, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int WM, int WN, int TM, int TN, int BK, int D, int P>
+template <int WM, int WN, int TM, int TN, int BK, int D, int P, int NV_MAX = 2>
 hipError_t launch_nv(const Gemm &g, hipStream_t stream) {
     int max_r = 0;
     for (int c = 0; c < (g.pair ? 2 : g.n_ch); ++c) max_r = g.ch[c].r > max_r ? g.ch[c].r : max_r;
-    if (max_r == 0) return launch_cfg<WM, WN, TM, TN, BK, D, P, 0>(g, stream);
-    if (max_r <= 32) return launch_cfg<WM, WN, TM, TN, BK, D, P, 1>(g, stream);
-    return launch_cfg<WM, WN, TM, TN, BK, D, P, 2>(g, stream);
+    if (max_r == 0 || NV_MAX == 0) return launch_cfg<WM, WN, TM, TN, BK, D, P, 0>(g, stream);
+    if (max_r <= 32 || NV_MAX == 1) return launch_cfg<WM, WN, TM, TN, BK, D, P, (NV_MAX < 1 ? NV_MAX : 1)>(g, stream);
+    return launch_cfg<WM, WN, TM, TN, BK, D, P, NV_MAX>(g, stream);
 }
 
 }  // namespace
 
 // Tile configurations (waves M x N, 32x32 blocks per wave M x N, K depth, LDS
 // stages), chosen by measurement on the layer shapes; overridable at build time.
-// The largest tile whose grid still gives most compute units a workgroup is used.
+// The largest tile whose grid still gives most compute units a workgroup is used
+// (the largest only without a rank term, whose extra registers it has no room for).
 #ifndef WL_GEMM_TILE_BIG
 #define WL_GEMM_TILE_BIG 4, 2, 2, 4, 64, 2
 #endif
@@ -444,11 +519,11 @@ hipError_t launch_gemm(const Gemm &g, hipStream_t stream) {
     for (int c = 0; c < (g.pair ? 2 : g.n_ch); ++c) max_r = g.ch[c].r > max_r ? g.ch[c].r : max_r;
     if (g.pair) {
         if (max_r == 0 && tiles_of<WL_GEMM_TILE_BIG_PAIR>(g) >= kFillTiles)
-            return launch_nv<WL_GEMM_TILE_BIG_PAIR, 2>(g, stream);
+            return launch_nv<WL_GEMM_TILE_BIG_PAIR, 2, 0>(g, stream);
         if (tiles_of<WL_GEMM_TILE_PAIR>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_PAIR, 2>(g, stream);
         return launch_nv<WL_GEMM_TILE_SMALL_PAIR, 2>(g, stream);
     }
-    if (max_r <= 32 && tiles_of<WL_GEMM_TILE_BIG>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_BIG, 1>(g, stream);
+    if (max_r == 0 && tiles_of<WL_GEMM_TILE_BIG>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_BIG, 1, 0>(g, stream);
     if (tiles_of<WL_GEMM_TILE>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE, 1>(g, stream);
     return launch_nv<WL_GEMM_TILE_SMALL, 1>(g, stream);
 }
