@@ -1,7 +1,7 @@
 // Matrix-core path for larger token counts (prefill-sized calls), one launch.
 //
 //   m[t,o]   = sum_i x[t,i] W0[o,i]                 bf16 x bf16 -> fp32 on MFMA
-//   vtx[t,k] = sum_i x[t,i] V[i,k]                  same x tiles, same MFMA
+//   vtx[t,k] = sum_i x[t,i] V[i,k]                  computed before, split partials
 //   y[t,o]   = bf16( s[o] * m[t,o] + sum_k vtx[t,k] U[o,k] )
 //
 // ("In-kernel reconstruction", introduction: the reconstruction formula and its
@@ -19,20 +19,18 @@
 // LDS rows of BK bf16 keep their 16-byte pieces XOR-swizzled by the row index
 // so that the fragment reads are free of bank conflicts.
 //
-// V^T x rides along: each stage also carries the matching BK rows of V (its
-// natural layout, rank-contiguous), and the waves multiply the x fragments
-// they already hold by V fragments gathered from LDS, splitting the K steps
-// among the WN waves of a workgroup row; the WN partial results are added in
-// wave order in the epilogue, so vtx never depends on scheduling. This costs
-// about 1/WN of one extra MFMA per K step per 32 ranks and needs no separate
-// launch and no workspace.
-//
+// V^T x is not computed here: a small matrix-core launch before this one writes
+// it as S split partials over the input axis (fp32 [S][T][r] per child), and
+// the epilogue adds them in split order, so vtx never depends on scheduling.
+// Keeping it out of the main loop leaves every K step to the W0 product.
+
 // Workgroups are numbered so that each of the 8 XCDs (which take workgroups
 // round-robin) works through its own contiguous band of output tiles, keeping
 // the W0 rows it reads in its own L2.
 //
 // Epilogue: the accumulators are scaled by s[o] (one output column per lane in
-// the 32x32 layout); vtx is staged in LDS, split into a bf16 head and a bf16
+// the 32x32 layout); vtx (its partials summed) is read straight into the
+// A-operand layout (8 ranks of one token row per lane), split into a bf16 head and a bf16
 // remainder (vtx = hi + lo to about 2^-16 relative) and both are run against U
 // on the matrix cores as extra K steps, so the rank term keeps close to fp32
 // accuracy. Results are rounded once to bf16. Pair mode (the MLP's gate/up)
@@ -68,20 +66,14 @@ struct Cfg {
     static constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     static constexpr int KP = BK / 8;                          // 16-byte pieces per LDS row
     static constexpr int A_PIECES = BM * KP, B_PIECES = BN * KP;
-    static constexpr int V_PIECES = BK * NV * 32 * 2 / 16;      // BK rows of V, up to NV*32 ranks
     static constexpr int A_PER = A_PIECES / kThreads, B_PER = B_PIECES / kThreads;
-    static constexpr int V_PER = (V_PIECES + kThreads - 1) / kThreads;
-    static constexpr int V_SLOTS = V_PER * kThreads;           // every lane's load writes a slot
-    static constexpr int STAGE_PIECES = A_PIECES + P * (B_PIECES + V_SLOTS);
-    static constexpr int PER_STAGE = A_PER + P * (B_PER + V_PER);   // direct-to-LDS loads per thread
+    static constexpr int STAGE_PIECES = A_PIECES + P * B_PIECES;
+    static constexpr int PER_STAGE = A_PER + P * B_PER;        // direct-to-LDS loads per thread
     static constexpr int TILE_PIECES = D * STAGE_PIECES;
-    static constexpr int VT_LD = kMaxRank + 4;                 // fp32 row stride of the epilogue vtx
-    static constexpr int VT_PIECES = NV > 0 ? P * BM * VT_LD * 4 / 16 : 0;
-    static constexpr int LDS_PIECES = TILE_PIECES > VT_PIECES ? TILE_PIECES : VT_PIECES;
+    static constexpr int LDS_PIECES = TILE_PIECES;
     static_assert(A_PIECES % kThreads == 0 && B_PIECES % kThreads == 0, "tile pieces must split evenly");
     static_assert(D >= 2 && D <= 4 && (D - 1) * PER_STAGE <= 63, "stages in flight must fit vmcnt");
     static_assert(D - 2 <= 2, "wait counts cover at most two stages ahead");
-    static_assert((BK / 16) % WN == 0, "V^T x K steps must split evenly over the WN waves");
 };
 
 // Swizzled position of piece kc of LDS row `row` (rows of KP pieces). The XOR
@@ -122,7 +114,6 @@ template <int WM, int WN, int TM, int TN, int BK, int P, int D, int NV>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(Gemm g) {
     using C = Cfg<WM, WN, TM, TN, BK, P, D, NV>;
     constexpr int BM = C::BM, BN = C::BN, KP = C::KP, NT = C::kThreads;
-    constexpr int NVA = NV > 0 ? NV : 1;
     __shared__ u32x4 lds[C::LDS_PIECES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -166,20 +157,14 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
     for (int p = 0; p < P; ++p) ch[p] = &g.ch[P == 2 ? p : cidx];
 
     f32x16 acc[P][TM][TN];
-    f32x16 accv[P][TM][NVA];
 #pragma unroll
     for (int p = 0; p < P; ++p)
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[p][i][j][e] = 0.f;
-#pragma unroll
-            for (int v = 0; v < NVA; ++v)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) accv[p][i][v][e] = 0.f;
-        }
 
     // The ring: the 64 lanes of one load write 64 consecutive 16-byte LDS slots,
     // so each lane fetches the global piece that belongs in its (swizzled) slot.
@@ -195,24 +180,12 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const u32x4 *wgp = reinterpret_cast<const u32x4 *>(ch[p]->W0);
-            u32x4 *bst = st + C::A_PIECES + p * (C::B_PIECES + C::V_SLOTS);
+            u32x4 *bst = st + C::A_PIECES + p * C::B_PIECES;
 #pragma unroll
             for (int h = 0; h < C::B_PER; ++h) {
                 const int q = h * NT + tid, row = q / KP, kc = (q % KP) ^ swz_key<KP>(row), gk = kt * KP + kc;
                 const u32x4 *src = (gk < nch && n0 + row < d_out) ? wgp + (size_t)(n0 + row) * nch + gk : zero;
                 lds_dma16(src, bst + h * NT + wave * kWave);
-            }
-            if constexpr (NV > 0) {
-                // V rows [kt*BK, kt*BK + BK): BK*r bf16, contiguous, copied as they are.
-                const int r = ch[p]->r;
-                const u32x4 *vgp = reinterpret_cast<const u32x4 *>(ch[p]->V);
-                const int q_end = BK * r / 8, q_all = d_in * r / 8, q0 = kt * BK * r / 8;
-#pragma unroll
-                for (int h = 0; h < C::V_PER; ++h) {
-                    const int q = h * NT + tid;
-                    const u32x4 *src = (q < q_end && q0 + q < q_all) ? vgp + q0 + q : zero;
-                    lds_dma16(src, bst + C::B_PIECES + h * NT + wave * kWave);
-                }
             }
         }
     };
@@ -229,13 +202,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
     }
     int b_off[P][C::B_PER];
     const u32x4 *wg[P];
-    const u32x4 *vg[P];
-    int vstep[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         wg[p] = reinterpret_cast<const u32x4 *>(ch[p]->W0);
-        vg[p] = reinterpret_cast<const u32x4 *>(ch[p]->V);
-        vstep[p] = BK * ch[p]->r / 8;
         const int dout_p = ch[p]->d_out;
 #pragma unroll
         for (int h = 0; h < C::B_PER; ++h) {
@@ -250,19 +219,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
         for (int h = 0; h < C::A_PER; ++h) lds_dma16(xk + a_off[h], st + h * NT + wave * kWave);
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            u32x4 *bst = st + C::A_PIECES + p * (C::B_PIECES + C::V_SLOTS);
+            u32x4 *bst = st + C::A_PIECES + p * C::B_PIECES;
             const u32x4 *wk = wg[p] + kt * KP;
 #pragma unroll
             for (int h = 0; h < C::B_PER; ++h) lds_dma16(wk + b_off[p][h], bst + h * NT + wave * kWave);
-            if constexpr (NV > 0) {
-                // Slots past the stage's BK * r / 8 pieces are never read: they repeat the
-                // last piece. A child without a rank term (r = 0, V absent) reads the zero piece.
-                const u32x4 *vk = vg[p] + kt * vstep[p];
-#pragma unroll
-                for (int h = 0; h < C::V_PER; ++h)
-                    lds_dma16(vstep[p] > 0 ? vk + min(h * NT + tid, vstep[p] - 1) : zero,
-                              bst + C::B_PIECES + h * NT + wave * kWave);
-            }
         }
     };
     auto issue_any = [&](int kt, int sl) {
@@ -284,7 +244,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
         for (int p = 0; p < P; ++p)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                b[p][j] = st[C::A_PIECES + p * (C::B_PIECES + C::V_SLOTS) + swz<KP>(wn * TN * 32 + j * 32 + fr, kc)];
+                b[p][j] = st[C::A_PIECES + p * C::B_PIECES + swz<KP>(wn * TN * 32 + j * 32 + fr, kc)];
     };
     auto step_mfma = [&](const u32x4 *st, int s, const u32x4 (&a)[TM], const u32x4 (&b)[P][TN]) {
         // Diagonal order: every fragment is used early and late in the step, so all
@@ -299,32 +259,6 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
                     const int j = (i + d) % TN;
                     acc[p][i][j] = mfma(a[i], b[p][j], acc[p][i][j]);
                 }
-        if constexpr (NV > 0) {
-            if (s % WN == wn) {
-                // V fragment: lane (fr, fk) needs V[i][k] for the 8 stage rows
-                // i = 16s + 8fk + e and rank k = 32v + fr.
-#pragma unroll
-                for (int p = 0; p < P; ++p) {
-                    const int r = ch[p]->r;
-                    const uint16_t *vl = reinterpret_cast<const uint16_t *>(
-                        st + C::A_PIECES + p * (C::B_PIECES + C::V_SLOTS) + C::B_PIECES);
-#pragma unroll
-                    for (int v = 0; v < NV; ++v) {
-                        const int k = 32 * v + fr;
-                        u32x4 vf = {0u, 0u, 0u, 0u};
-                        if (k < r) {
-                            const uint16_t *col = vl + (16 * s + 8 * fk) * r + k;
-                            vf.x = (uint32_t)col[0] | ((uint32_t)col[r] << 16);
-                            vf.y = (uint32_t)col[2 * r] | ((uint32_t)col[3 * r] << 16);
-                            vf.z = (uint32_t)col[4 * r] | ((uint32_t)col[5 * r] << 16);
-                            vf.w = (uint32_t)col[6 * r] | ((uint32_t)col[7 * r] << 16);
-                        }
-#pragma unroll
-                        for (int i = 0; i < TM; ++i) accv[p][i][v] = mfma(a[i], vf, accv[p][i][v]);
-                    }
-                }
-            }
-        }
     };
     static_assert((BK / 16) % 2 == 0, "steps are taken in pairs");
     auto compute = [&](const u32x4 *st) {
@@ -352,74 +286,81 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
         if (kt + D - 1 < nk) issue_any(kt + D - 1, (kt + D - 1) % D);
         compute(lds + (kt % D) * C::STAGE_PIECES);
     }
-    barrier();                                        // the ring is free for the epilogue
 
     // ---- epilogue ----
     // Lane (fr, fk) of block (i, j) holds output column o = n0 + (wn*TN + j)*32 + fr
     // and token rows m0 + (wm*TM + i)*32 + 8*(e/4) + 4*fk + (e%4), e = 0..15.
-    if constexpr (NV > 0) {
-        // vtx of child p: fp32 [BM][VT_LD] at vt + p*BM*VT_LD, the WN partials added in wave
-        // order. The padded row stride puts the 16 rows one LDS pass reads on distinct banks.
-        float *vt = reinterpret_cast<float *>(lds);
-        for (int w = 0; w < WN; ++w) {
-            if (wn == w) {
-#pragma unroll
-                for (int p = 0; p < P; ++p)
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int v = 0; v < NV; ++v)
-#pragma unroll
-                            for (int e = 0; e < 16; ++e) {
-                                const int row = (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * fk + (e & 3);
-                                float *dst = vt + (p * BM + row) * C::VT_LD + 32 * v + fr;
-                                *dst = w == 0 ? accv[p][i][v][e] : *dst + accv[p][i][v][e];
-                            }
-            }
-            barrier();
-        }
-    }
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         const Child &Cp = *ch[p];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int o = n0 + (wn * TN + j) * 32 + fr;
-            const float sv = (Cp.s && o < d_out) ? Cp.s[o] : 1.0f;
+            const float sv = Cp.s ? ldg(Cp.s + min(o, d_out - 1)) : 1.0f;
 #pragma unroll
             for (int i = 0; i < TM; ++i) acc[p][i][j] *= sv;
         }
         if constexpr (NV > 0) {
-            const int r = Cp.r;
-            const float *vt = reinterpret_cast<const float *>(lds) + p * BM * C::VT_LD;
+            const int r = Cp.r, S = Cp.vtx_splits;
+            const size_t ss = (size_t)g.T * r;        // split stride of the partials
             for (int k0 = 0; k0 < r; k0 += 16) {
                 const int kb = k0 + 8 * fk;
                 u32x4 ahi[TM], alo[TM], bu[TN];
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
-                    // Columns up to kb + 7 < 64 are inside the row; those at or past r
-                    // (never written) are replaced by zeros.
-                    const f32x4 *row = reinterpret_cast<const f32x4 *>(vt + ((wm * TM + i) * 32 + fr) * C::VT_LD + kb);
-                    const f32x4 r0 = row[0], r1 = row[1];
-                    const float raw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+                    // vtx[t][kb .. kb+8) for this lane's token row, its split partials
+                    // added in split order; every load unconditional at a clamped
+                    // address, values past T or r masked to zero.
+                    const int t = m0 + (wm * TM + i) * 32 + fr;
+                    const float *src = Cp.vtx + (size_t)min(t, g.T - 1) * r;
+                    float v[8];
+                    if ((r & 3) == 0) {
+                        const int ka = min(kb, r - 4), kc = min(kb + 4, r - 4);
+                        f32x4 s0 = ldg(reinterpret_cast<const f32x4 *>(src + ka));
+                        f32x4 s1 = ldg(reinterpret_cast<const f32x4 *>(src + kc));
+                        for (int q = 1; q < S; ++q) {
+                            s0 += ldg(reinterpret_cast<const f32x4 *>(src + q * ss + ka));
+                            s1 += ldg(reinterpret_cast<const f32x4 *>(src + q * ss + kc));
+                        }
+                        const bool ok0 = kb < r, ok1 = kb + 4 < r;
+                        v[0] = ok0 ? s0.x : 0.f; v[1] = ok0 ? s0.y : 0.f; v[2] = ok0 ? s0.z : 0.f; v[3] = ok0 ? s0.w : 0.f;
+                        v[4] = ok1 ? s1.x : 0.f; v[5] = ok1 ? s1.y : 0.f; v[6] = ok1 ? s1.z : 0.f; v[7] = ok1 ? s1.w : 0.f;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int kk = min(kb + e, r - 1);
+                            float a = ldg(src + kk);
+                            for (int q = 1; q < S; ++q) a += ldg(src + q * ss + kk);
+                            v[e] = kb + e < r ? a : 0.f;
+                        }
+                    }
                     float hi[8], lo[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float v = kb + e < r ? raw[e] : 0.f;
-                        hi[e] = bf16_f(f_bf16(v));
-                        lo[e] = v - hi[e];
+                        hi[e] = bf16_f(f_bf16(v[e]));
+                        lo[e] = v[e] - hi[e];
                     }
                     ahi[i] = pack8(hi);
                     alo[i] = pack8(lo);
                 }
+                // U[o][kb .. kb+8): every load unconditional at a clamped address, the
+                // values past d_out or r masked to zero.
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int o = n0 + (wn * TN + j) * 32 + fr;
-                    float u[8];
+                    const uint16_t *urow = Cp.U + (size_t)min(o, d_out - 1) * r;
+                    if ((r & 7) == 0) {
+                        const u32x4 v = ldg(reinterpret_cast<const u32x4 *>(urow + min(kb, r - 8)));
+                        bu[j] = (o < d_out && kb < r) ? v : u32x4{0u, 0u, 0u, 0u};
+                    } else {
+                        uint32_t h[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        u[e] = (o < d_out && kb + e < r) ? bf16_f(Cp.U[(size_t)o * r + kb + e]) : 0.f;
-                    bu[j] = pack8(u);
+                        for (int e = 0; e < 8; ++e) {
+                            const uint32_t b = ldg(urow + min(kb + e, r - 1));
+                            h[e] = (o < d_out && kb + e < r) ? b : 0u;
+                        }
+                        bu[j] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
@@ -463,21 +404,19 @@ hipError_t launch_cfg(const Gemm &g, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int WM, int WN, int TM, int TN, int BK, int D, int P, int NV_MAX = 2>
+template <int WM, int WN, int TM, int TN, int BK, int D, int P>
 hipError_t launch_nv(const Gemm &g, hipStream_t stream) {
     int max_r = 0;
     for (int c = 0; c < (g.pair ? 2 : g.n_ch); ++c) max_r = g.ch[c].r > max_r ? g.ch[c].r : max_r;
-    if (max_r == 0 || NV_MAX == 0) return launch_cfg<WM, WN, TM, TN, BK, D, P, 0>(g, stream);
-    if (max_r <= 32 || NV_MAX == 1) return launch_cfg<WM, WN, TM, TN, BK, D, P, (NV_MAX < 1 ? NV_MAX : 1)>(g, stream);
-    return launch_cfg<WM, WN, TM, TN, BK, D, P, NV_MAX>(g, stream);
+    if (max_r == 0) return launch_cfg<WM, WN, TM, TN, BK, D, P, 0>(g, stream);
+    return launch_cfg<WM, WN, TM, TN, BK, D, P, 1>(g, stream);
 }
 
 }  // namespace
 
 // Tile configurations (waves M x N, 32x32 blocks per wave M x N, K depth, LDS
 // stages), chosen by measurement on the layer shapes; overridable at build time.
-// The largest tile whose grid still gives most compute units a workgroup is used
-// (the largest only without a rank term, whose extra registers it has no room for).
+// The largest tile whose grid still gives most compute units a workgroup is used.
 #ifndef WL_GEMM_TILE_BIG
 #define WL_GEMM_TILE_BIG 4, 2, 2, 4, 64, 2
 #endif
@@ -515,15 +454,12 @@ int tiles_of(const Gemm &g) {
 }  // namespace
 
 hipError_t launch_gemm(const Gemm &g, hipStream_t stream) {
-    int max_r = 0;
-    for (int c = 0; c < (g.pair ? 2 : g.n_ch); ++c) max_r = g.ch[c].r > max_r ? g.ch[c].r : max_r;
     if (g.pair) {
-        if (max_r == 0 && tiles_of<WL_GEMM_TILE_BIG_PAIR>(g) >= kFillTiles)
-            return launch_nv<WL_GEMM_TILE_BIG_PAIR, 2, 0>(g, stream);
+        if (tiles_of<WL_GEMM_TILE_BIG_PAIR>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_BIG_PAIR, 2>(g, stream);
         if (tiles_of<WL_GEMM_TILE_PAIR>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_PAIR, 2>(g, stream);
         return launch_nv<WL_GEMM_TILE_SMALL_PAIR, 2>(g, stream);
     }
-    if (max_r == 0 && tiles_of<WL_GEMM_TILE_BIG>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_BIG, 1, 0>(g, stream);
+    if (tiles_of<WL_GEMM_TILE_BIG>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_BIG, 1>(g, stream);
     if (tiles_of<WL_GEMM_TILE>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE, 1>(g, stream);
     return launch_nv<WL_GEMM_TILE_SMALL, 1>(g, stream);
 }

@@ -115,10 +115,12 @@ Kind choose(int T, int d_in, int sum_r) {
 //
 //   [0, 256)          reserved
 //   gemv_partial      fp32 3 x [kGemvMaxSlices][kGemvMaxTok][kMaxRank] V^T x slices
-//                     (decode regime; the matrix-core kernel computes V^T x itself)
+//                     (decode regime)
 //   skinny part       fp32 [S][P][T][rows] split partials (T <= kSkMaxTok), the
 //                     largest of the call's projections
 //   skinny vpart      fp32 [n_vsl][n_ch][T][kMaxRank] V^T x slice partials
+//   mm_vtx            fp32 [S][T][r_c] per child: V^T x split partials of the
+//                     matrix-core regime (the largest of the call's projections)
 //   h                 bf16 [T][d_ff] (MLP only)
 
 constexpr size_t kReservedBytes = 256;
@@ -126,6 +128,7 @@ constexpr size_t kReservedBytes = 256;
 struct Layout {
     size_t gemv_partial = 0;
     size_t sk_part = 0, sk_vpart = 0;
+    size_t mm_vtx = 0;
     size_t h = 0;
     size_t total = 0;
 };
@@ -175,6 +178,13 @@ Layout layout(int op, const wl_theta *const *th, int T) {
     off = round_up(off + part, kAlign);
     L.sk_vpart = off;
     off = round_up(off + vpart, kAlign);
+    size_t mm = 0;
+    for (int j = 0; j < n; ++j) {
+        const size_t b = (size_t)wl::vtxmm_splits(ps[j].d_in, wl::kMaxRank) * T * ps[j].sum_r * 4 + wl::kMaxChildren * kAlign;
+        mm = ps[j].sum_r > 0 && b > mm ? b : mm;
+    }
+    L.mm_vtx = off;
+    off = round_up(off + mm, kAlign);
     if (op == WL_OP_MLP) {
         L.h = off;
         off = round_up(off + (size_t)T * th[0]->d_out * 2, kAlign);
@@ -189,6 +199,8 @@ wl::Child make_child(const wl_theta *th, int col0) {
     c.s = th->s;
     c.U = static_cast<const uint16_t *>(th->U);
     c.V = static_cast<const uint16_t *>(th->V);
+    c.vtx = nullptr;
+    c.vtx_splits = 0;
     c.r = th->r;
     c.d_out = th->d_out;
     c.col0 = col0;
@@ -288,6 +300,33 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
     } else {
         wl::Gemm g{};
         for (int c = 0; c < n_ch; ++c) g.ch[c] = ch[c];
+        if (sum_r > 0) {
+            // V^T x split partials on the matrix cores, added in order by the GEMM epilogue.
+            wl::VtxMM mm{};
+            mm.x = static_cast<const uint16_t *>(x);
+            mm.d_in = d_in;
+            mm.T = T;
+            int max_r = 0;
+            for (int c = 0; c < n_ch; ++c) max_r = ch[c].r > max_r ? ch[c].r : max_r;
+            mm.S = wl::vtxmm_splits(d_in, max_r);
+            const int nkb = (d_in + 63) / 64;
+            mm.kb_per_split = (nkb + mm.S - 1) / mm.S;
+            mm.S = (nkb + mm.kb_per_split - 1) / mm.kb_per_split;
+            size_t moff = L.mm_vtx;
+            for (int c = 0; c < n_ch; ++c) {
+                if (ch[c].r == 0) continue;
+                float *part = reinterpret_cast<float *>(ws + moff);
+                moff += round_up((size_t)mm.S * T * ch[c].r * 4, kAlign);
+                g.ch[c].vtx = part;
+                g.ch[c].vtx_splits = mm.S;
+                mm.V[mm.n] = ch[c].V;
+                mm.part[mm.n] = part;
+                mm.r[mm.n] = ch[c].r;
+                ++mm.n;
+            }
+            e = wl::launch_vtxmm(mm, stream);
+            if (e != hipSuccess) return fail(WL_ERR_HIP, "V^T x launch failed: %s", hipGetErrorString(e));
+        }
         g.n_ch = n_ch;
         g.pair = pair;
         g.d_in = d_in;

@@ -21,8 +21,25 @@ struct Child {
     const float *s;       // fp32 [d_out], or null: every s[o] is 1
     const uint16_t *U;    // bf16 [d_out][r]  (r > 0)
     const uint16_t *V;    // bf16 [d_in][r]   (r > 0)
+    const float *vtx;     // matrix-core regime: V^T x split partials, fp32 [vtx_splits][T][r]
+    int vtx_splits;
     int r, d_out, col0;
 };
+
+// V^T x of up to three children on the matrix cores (matrix-core regime):
+//   part[c][split][t][k] = sum over the split's inputs i of x[t][i] V[c][i][k],
+// splits of kb_per_split 64-wide blocks of the input axis, added in order by the GEMM.
+// vtxmm_splits gives the split count for an input width and the largest rank.
+constexpr int kVtxMaxSplits = 8;
+struct VtxMM {
+    const uint16_t *x;                 // bf16 [T][d_in]
+    const uint16_t *V[kMaxChildren];   // bf16 [d_in][r_c], 1 <= r_c <= kMaxRank
+    float *part[kMaxChildren];         // fp32 [S][T][r_c]
+    int r[kMaxChildren];
+    int n, d_in, T, S, kb_per_split;
+};
+int vtxmm_splits(int d_in, int max_r);
+hipError_t launch_vtxmm(const VtxMM &job, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // V^T x slice partials for up to three children that share one input x
