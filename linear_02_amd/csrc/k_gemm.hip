@@ -76,34 +76,10 @@ struct Cfg {
     static_assert(D - 2 <= 2, "wait counts cover at most two stages ahead");
 };
 
-// Swizzled position of piece kc of LDS row `row` (rows of KP pieces). The XOR
-// pattern varies over 16 consecutive rows, so the 16 lanes that one LDS pass
-// serves (32 rows x one piece per fragment read) land on distinct 4-bank
-// groups of the 64 banks.
-template <int KP>
-__device__ __forceinline__ int swz_key(int row) {
-    constexpr int sh = KP == 8 ? 0 : KP == 4 ? 1 : 2;
-    return ((row >> sh) ^ (row >> 3)) & (KP - 1);
-}
-template <int KP>
-__device__ __forceinline__ int swz(int row, int kc) {
-    return row * KP + (kc ^ swz_key<KP>(row));
-}
-
 // A 16-byte piece of zeros: the source of every out-of-range piece of a
 // direct-to-LDS tile load (the load always writes its LDS slot).
 __device__ __attribute__((aligned(16))) const uint32_t kZeroPiece[4] = {0u, 0u, 0u, 0u};
 
-// One direct-to-LDS load: the wave's 64 lanes each fetch 16 bytes from their
-// own global address into 64 consecutive 16-byte LDS slots starting at dst.
-__device__ __forceinline__ void lds_dma16(const u32x4 *src, u32x4 *dst) {
-    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 __device__ __forceinline__ void barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();

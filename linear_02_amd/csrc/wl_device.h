@@ -13,6 +13,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -73,6 +74,30 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_last(v)), 63));
 }
 
+// Swizzled position of piece kc of LDS row `row` (rows of KP pieces). The XOR
+// pattern varies over 16 consecutive rows, so the 16 lanes that one LDS pass
+// serves (32 rows x one piece per fragment read) land on distinct 4-bank
+// groups of the 64 banks.
+template <int KP>
+__device__ __forceinline__ int swz_key(int row) {
+    constexpr int sh = KP == 8 ? 0 : KP == 4 ? 1 : 2;
+    return ((row >> sh) ^ (row >> 3)) & (KP - 1);
+}
+template <int KP>
+__device__ __forceinline__ int swz(int row, int kc) {
+    return row * KP + (kc ^ swz_key<KP>(row));
+}
+
+// One direct-to-LDS load: the wave's 64 lanes each fetch 16 bytes from their
+// own global address into 64 consecutive 16-byte LDS slots starting at dst.
+__device__ __forceinline__ void lds_dma16(const u32x4 *src, u32x4 *dst) {
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 // tanh-approximated GELU (Hendrycks & Gimpel, 2016), fp32, device tanhf.
 __device__ __forceinline__ float gelu_tanh(float z) {
     const float c0 = 0.7978845608028654f;   // sqrt(2 / pi)

@@ -118,7 +118,6 @@ constexpr int kSkMaxDin = 8192;
 constexpr int kSkMaxPartials = 8;     // split partials x pair x token blocks per output
 constexpr int kSkVtxTok = 8;          // tokens per V^T x workgroup
 constexpr int kSkVtxSlice = 512;      // inputs per V^T x workgroup
-constexpr int kSkEpiMaxLoads = 16384; // fp32 slice partials staged at once by one epilogue workgroup
 struct Skinny {
     Child ch[kMaxChildren];
     int n_ch;
