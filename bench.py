@@ -115,13 +115,27 @@ def mlp_work(lay: dict, dims: dict, T: int):
     return b, fl
 
 
-def source_digest() -> str:
-    """Digest of the kernel sources, to tell whether stored counter data still applies."""
-    import glob
+# Sources of the kernels each token-count range runs (the ABI and the shared
+# headers always count): the decode GEMV with its V^T x launch, the skinny path,
+# the matrix-core GEMM with its V^T x launch.
+_COMMON_SOURCES = ("wl_abi.cpp", "wl_kernels.h", "wl_device.h")
+
+
+def _regime_sources(tokens: int) -> tuple:
+    if tokens <= 8:
+        return ("k_gemv.hip", "k_vtx.hip")
+    if tokens <= 64:
+        return ("k_skinny.hip",)
+    return ("k_gemm.hip", "k_vtxmm.hip")
+
+
+def source_digest(tokens: int) -> str:
+    """Digest of the sources of the kernels that run at this token count, to tell
+    whether stored counter data still applies."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(REPO, "linear_02_amd", "csrc", "*"))):
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    for name in sorted(_COMMON_SOURCES + _regime_sources(tokens)):
+        with open(os.path.join(REPO, "linear_02_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -138,7 +152,7 @@ def stored_traffic(workload: str, rank: int, tokens: int):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("sources") != source_digest():
+    if kv.get("sources") != source_digest(tokens):
         return None
     try:
         return float(kv["bytes_per_call"])
@@ -499,11 +513,20 @@ def write_traffic(args) -> int:
     T = {"single": 1, "layer-decode": 1, "batched-decode": 32, "prefill": 2048}.get(
         args.workload, args.tokens if args.tokens is not None else 1)
     path = os.path.join(REPO, "profiles", f"traffic_{args.workload}_r{r}_T{T}.txt")
+    def rel(pth):
+        return os.path.relpath(os.path.dirname(os.path.abspath(pth)), REPO)
+    run = f"python3 bench.py --workload {args.workload} --rank {r}"
     with open(path, "w") as f:
         f.write(f"# HBM traffic of the dominant call of bench.py --workload {args.workload} (r={r}, T={T}),\n"
                 f"# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE passes over a --dominant-only run,\n"
-                f"# each scaled by the counter's reading for a plain {COPY_BYTES >> 20} MiB device copy.\n")
-        f.write(f"sources = {source_digest()}\n")
+                f"# each scaled by the counter's reading for a plain {COPY_BYTES >> 20} MiB device copy.\n"
+                f"# Commands (repository root):\n"
+                f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {rel(fetch_csv)} -o p -- {run} --dominant-only --steps {calls}\n"
+                f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {rel(write_csv)} -o p -- {run} --dominant-only --steps {calls}\n"
+                f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {rel(cfetch_csv)} -o p -- python3 bench.py --workload copy --steps 4\n"
+                f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {rel(cwrite_csv)} -o p -- python3 bench.py --workload copy --steps 4\n"
+                f"#   {run} --traffic-calls {calls} --traffic-from {' '.join(os.path.relpath(os.path.abspath(c), REPO) for c in args.traffic_from)}\n")
+        f.write(f"sources = {source_digest(T)}\n")
         f.write(f"calls = {calls}\n")
         f.write(f"fetch_kib_total = {f_kib:.1f}\nwrite_kib_total = {w_kib:.1f}\n")
         f.write(f"copy_fetch_scale = {kf:.4f}\ncopy_write_scale = {kw:.4f}\n")

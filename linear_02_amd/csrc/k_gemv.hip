@@ -28,8 +28,9 @@
 //   tensor is absent) and the value is masked afterwards, and per-child fields
 //   are chosen with selects rather than by indexing the kernel-argument array
 //   with a per-lane index (which becomes a chain of dependent vector loads).
-// Epilogue. The wave sums (DPP butterflies) meet in LDS, and one thread per
-//   (row, token) forms
+// Epilogue. The wave sums (DPP butterflies) meet in LDS; the rank term
+//   sum_k U[o,k] vtx[t,k] of each output is one wave's sum (lane k takes one
+//   product); then one thread per (row, token) forms
 //     y[t,o] = s[o] * (W0 x)[t,o] + sum_k U[o,k] vtx[t,k]
 //   adding row segments in order, and rounds once to bf16. Pair mode (gate/up
 //   of the MLP) streams the gate row and the up row together and writes
@@ -228,6 +229,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     __shared__ float slds[kMaxRowsG][P];
     __shared__ float gsum[kThreads];
     __shared__ float upart[kWaves][8][TT];
+    __shared__ float rterm[kMaxRowsG][P][TT];
 
     // The wave index is uniform: keep it (and what derives from it) in scalar registers.
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -371,6 +373,22 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
         }
     __syncthreads();
 
+    // Rank term of each (row, p, token): one wave per output, lane k takes
+    // U[o,k] vtx[t,k], and a wave sum (fixed butterfly order) adds them.
+    if (n_items > 0) {
+        const int n_out = rows_g * P * TT;
+        for (int oi = wave; oi < n_out; oi += kWaves) {
+            const int jr = oi / (P * TT), p = (oi / TT) % P, t = oi % TT;
+            const int row = min(rowbase + jr, g.rows - 1);
+            const int ci = P == 2 ? p : child_index(g, row);
+            const int r = ch_r(g, ci);
+            const float prod = lane < r ? ulds[jr][p][lane] * vs[ci][t][lane] : 0.f;
+            const float sum = wave_sum(prod);
+            if (lane == 0) rterm[jr][p][t] = sum;
+        }
+        __syncthreads();
+    }
+
     for (int idx = tid; idx < rows_g * TT; idx += kThreads) {
         const int jr = idx / TT, t = idx - jr * TT;
         const int rbi = jr / R, j = jr - rbi * R;
@@ -382,11 +400,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
         for (int p = 0; p < P; ++p) {
             float m = 0.f;
             for (int sg = 0; sg < nseg; ++sg) m += mbuf[rbi * nseg + sg][j][p][t];
-            const int ci = P == 2 ? p : child_index(g, row);
-            const int r = ch_r(g, ci);
-            float d = 0.f;
-            for (int k = 0; k < r; ++k) d += ulds[jr][p][k] * vs[ci][t][k];
-            val[p] = slds[jr][p] * m + d;
+            val[p] = slds[jr][p] * m + (n_items > 0 ? rterm[jr][p][t] : 0.f);
         }
         const float out = P == 2 ? gelu_tanh(val[0]) * val[P - 1] : val[0];
         g.y[(size_t)tok * g.ldy + row] = f_bf16(out);
