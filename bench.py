@@ -139,6 +139,12 @@ def source_digest(tokens: int) -> str:
     return h.hexdigest()[:16]
 
 
+def traffic_key(args, workload: str) -> str:
+    """Name of a workload's traffic record: one W0 shared by all layers (--shared-w0)
+    moves other bytes than one W0 per layer, so it has a record of its own."""
+    return workload + "-G1" if getattr(args, "shared_w0", False) else workload
+
+
 def stored_traffic(workload: str, rank: int, tokens: int):
     """HBM bytes per call of the dominant operation from the committed counter summary
     (rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes), or None when there is none or
@@ -328,13 +334,13 @@ def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_
     if bound == "hbm":
         achieved = mlp_b / (mlp_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(workload, r, T),
+                "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(traffic_key(args, workload), r, T),
                 "kernel": "wl_mlp_fused (all of its kernels, back to back)", "bytes_per_launch": mlp_b,
                 "us_per_launch": mlp_ms * 1e3}
     else:
         achieved = mlp_f / (mlp_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_BF16_PEAK_TFS, "traffic": stored_traffic(workload, r, T),
+                "frac": achieved / MFMA_BF16_PEAK_TFS, "traffic": stored_traffic(traffic_key(args, workload), r, T),
                 "kernel": "wl_mlp_fused (all of its kernels, back to back)", "flops_per_launch": mlp_f,
                 "us_per_launch": mlp_ms * 1e3}
 
@@ -512,10 +518,10 @@ def write_traffic(args) -> int:
     r = args.rank if args.rank is not None else (4 if args.workload == "single" else 32)
     T = {"single": 1, "layer-decode": 1, "batched-decode": 32, "prefill": 2048}.get(
         args.workload, args.tokens if args.tokens is not None else 1)
-    path = os.path.join(REPO, "profiles", f"traffic_{args.workload}_r{r}_T{T}.txt")
+    path = os.path.join(REPO, "profiles", f"traffic_{traffic_key(args, args.workload)}_r{r}_T{T}.txt")
     def rel(pth):
         return os.path.relpath(os.path.dirname(os.path.abspath(pth)), REPO)
-    run = f"python3 bench.py --workload {args.workload} --rank {r}"
+    run = f"python3 bench.py --workload {args.workload} --rank {r}" + (" --shared-w0" if args.shared_w0 else "")
     with open(path, "w") as f:
         f.write(f"# HBM traffic of the dominant call of bench.py --workload {args.workload} (r={r}, T={T}),\n"
                 f"# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE passes over a --dominant-only run,\n"
