@@ -109,8 +109,11 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
         const int full = total - 8 * (per - 1);   // XCDs 0..full-1 hold `per` tiles, the rest per-1
         tile = x < full ? x * per + slot : full * per + (x - full) * (per - 1) + slot;
     }
-    // Within the band: token tiles fastest, so consecutive tiles share W0 rows.
-    const int mt = tile % n_mt, ntile = tile / n_mt;
+    // Within the band: token tiles fastest (consecutive tiles share W0 rows), or
+    // output tiles fastest (they share x rows) when x is the larger operand, so
+    // that each XCD re-reads the smaller one.
+    const int mt = g.col_fast ? tile / n_nt : tile % n_mt;
+    const int ntile = g.col_fast ? tile % n_nt : tile / n_mt;
     int cidx = 0, n0 = ntile * BN;
     if (!g.pair) {
         int left = ntile;
@@ -400,10 +403,10 @@ hipError_t launch_nv(const Gemm &g, hipStream_t stream) {
 #define WL_GEMM_TILE_BIG_PAIR 4, 2, 2, 2, 64, 2
 #endif
 #ifndef WL_GEMM_TILE
-#define WL_GEMM_TILE 2, 2, 2, 2, 64, 2
+#define WL_GEMM_TILE 2, 2, 2, 2, 64, 4
 #endif
 #ifndef WL_GEMM_TILE_PAIR
-#define WL_GEMM_TILE_PAIR 2, 2, 2, 2, 64, 2
+#define WL_GEMM_TILE_PAIR 2, 2, 2, 2, 64, 3
 #endif
 #ifndef WL_GEMM_TILE_SMALL
 #define WL_GEMM_TILE_SMALL 2, 2, 2, 1, 64, 2
@@ -414,7 +417,10 @@ hipError_t launch_nv(const Gemm &g, hipStream_t stream) {
 
 namespace {
 
-constexpr int kFillTiles = 232;   // workgroups that count as filling the 256 compute units
+#ifndef WL_GEMM_FILL
+#define WL_GEMM_FILL 232
+#endif
+constexpr int kFillTiles = WL_GEMM_FILL;   // workgroups that count as filling the 256 compute units
 
 template <int WM, int WN, int TM, int TN, int BK, int D>
 int tiles_of(const Gemm &g) {
@@ -429,7 +435,11 @@ int tiles_of(const Gemm &g) {
 
 }  // namespace
 
-hipError_t launch_gemm(const Gemm &g, hipStream_t stream) {
+hipError_t launch_gemm(const Gemm &g_in, hipStream_t stream) {
+    Gemm g = g_in;
+    int rows = 0;
+    for (int c = 0; c < (g.pair ? 1 : g.n_ch); ++c) rows += g.ch[c].d_out;
+    g.col_fast = g.T > rows * (g.pair ? 2 : 1);   // x ([T][d_in]) larger than the W0 rows it meets
     if (g.pair) {
         if (tiles_of<WL_GEMM_TILE_BIG_PAIR>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_BIG_PAIR, 2>(g, stream);
         if (tiles_of<WL_GEMM_TILE_PAIR>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_PAIR, 2>(g, stream);

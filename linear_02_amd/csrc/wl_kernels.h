@@ -142,8 +142,8 @@ hipError_t launch_skinny(const Skinny &g, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Matrix-core GEMM for larger token counts, same result as Gemv (including pair
-// mode); V^T x is computed inside, from the x tiles it already loads. Output
-// tiles never span two children.
+// mode); V^T x comes from the split partials of a VtxMM launch just before.
+// Output tiles never span two children.
 struct Gemm {
     Child ch[kMaxChildren];
     int n_ch;
@@ -153,6 +153,7 @@ struct Gemm {
     int T;
     const uint16_t *x;    // bf16 [T][d_in]
     uint16_t *y;          // bf16 [T][ldy]
+    int col_fast;         // tile order within an XCD's band (set by launch_gemm)
 };
 hipError_t launch_gemm(const Gemm &g, hipStream_t stream);
 
