@@ -403,10 +403,10 @@ hipError_t launch_nv(const Gemm &g, hipStream_t stream) {
 #define WL_GEMM_TILE_BIG_PAIR 4, 2, 2, 2, 64, 2
 #endif
 #ifndef WL_GEMM_TILE
-#define WL_GEMM_TILE 2, 2, 2, 2, 64, 4
+#define WL_GEMM_TILE 2, 2, 2, 2, 64, 2
 #endif
 #ifndef WL_GEMM_TILE_PAIR
-#define WL_GEMM_TILE_PAIR 2, 2, 2, 2, 64, 3
+#define WL_GEMM_TILE_PAIR 2, 2, 2, 2, 64, 2
 #endif
 #ifndef WL_GEMM_TILE_SMALL
 #define WL_GEMM_TILE_SMALL 2, 2, 2, 1, 64, 2
@@ -418,7 +418,7 @@ hipError_t launch_nv(const Gemm &g, hipStream_t stream) {
 namespace {
 
 #ifndef WL_GEMM_FILL
-#define WL_GEMM_FILL 232
+#define WL_GEMM_FILL 200
 #endif
 constexpr int kFillTiles = WL_GEMM_FILL;   // workgroups that count as filling the 256 compute units
 
