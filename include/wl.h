@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define WL_ABI_VERSION 1
+#define WL_ABI_VERSION 2
 
 typedef enum {
     WL_OK = 0,
@@ -149,6 +149,32 @@ wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta 
  * W_eff: bf16 [th->d_out][th->d_in], written; must not overlap any input.
  * Needs no workspace. */
 wl_status wl_materialize_weff(const wl_theta *th, void *W_eff, void *hip_stream);
+
+/* Size of a set of theta bundles against the dense weights they replace
+ * ("What weightless inference costs", "Compression": the ratio of the theta
+ * bundle, W0 + s + U + V across every layer and family, to the original
+ * projection weights). For th[0 .. n_th):
+ *   *bundle_bytes = 2 d_out d_in once per distinct W0 pointer
+ *                   + per theta: 4 d_out (when s is not NULL) + 2 r (d_out + d_in)
+ *   *dense_bytes  = per theta: 2 d_out d_in (the bf16 weight it stands for)
+ * Thetas that share a W0 pointer must share its shape (else
+ * WL_ERR_INVALID_ARG). Host only: reads the structs, never the tensors. */
+wl_status wl_bundle_size(const wl_theta *const *th, int32_t n_th,
+                         size_t *bundle_bytes, size_t *dense_bytes);
+
+/* Reconstruction fidelity ("What weightless inference costs", "Reconstruction
+ * fidelity"): result[0] = ||W - R||_F / ||W||_F, accumulated in fp64 (the
+ * differences and squares of bf16 values are exact there), in a fixed order
+ * that depends on n only.
+ *   W, R    bf16 [n] device tensors, 16-byte aligned: e.g. an original weight
+ *           and the W_eff of wl_materialize_weff
+ *   n       elements, 1 <= n < 2^40
+ *   result  device pointer to one double, 8-byte aligned, written
+ *   ws      workspace, ws_bytes >= wl_rel_frob_workspace_bytes(n)
+ * When ||W||_F is 0 the result is 0 if R equals W and +inf otherwise. */
+size_t wl_rel_frob_workspace_bytes(int64_t n);
+wl_status wl_relative_frobenius_error(const void *W, const void *R, int64_t n, double *result,
+                                      void *ws, size_t ws_bytes, void *hip_stream);
 
 /* Kernel regime for the projection calls: 0 chooses by token count (the
  * default), 1 forces the decode GEMV wherever it applies (V^T x computed by

@@ -514,4 +514,63 @@ wl_status wl_materialize_weff(const wl_theta *th, void *W_eff, void *hip_stream)
     return ok();
 }
 
+wl_status wl_bundle_size(const wl_theta *const *th, int32_t n_th, size_t *bundle_bytes, size_t *dense_bytes) {
+    if (!th || n_th < 1) return fail(WL_ERR_INVALID_ARG, "no thetas");
+    if (!bundle_bytes || !dense_bytes) return fail(WL_ERR_INVALID_ARG, "bundle_bytes or dense_bytes is NULL");
+    size_t bundle = 0, dense = 0;
+    for (int32_t j = 0; j < n_th; ++j) {
+        const wl_theta *t = th[j];
+        char name[32];
+        snprintf(name, sizeof name, "theta %d", j);
+        const wl_status st = check_theta(t, name);
+        if (st != WL_OK) return st;
+        bool seen = false;
+        for (int32_t i = 0; i < j; ++i)
+            if (th[i]->W0 == t->W0) {
+                if (th[i]->d_in != t->d_in || th[i]->d_out != t->d_out)
+                    return fail(WL_ERR_INVALID_ARG, "thetas %d and %d share W0 but not its shape", i, j);
+                seen = true;
+                break;
+            }
+        const size_t w0 = (size_t)2 * t->d_out * t->d_in;
+        if (!seen) bundle += w0;
+        bundle += (t->s ? (size_t)4 * t->d_out : 0) + (size_t)2 * t->r * ((size_t)t->d_out + t->d_in);
+        dense += w0;
+    }
+    *bundle_bytes = bundle;
+    *dense_bytes = dense;
+    return ok();
+}
+
+size_t wl_rel_frob_workspace_bytes(int64_t n) {
+    if (n < 1) return 0;
+    return round_up((size_t)wl::frob_workgroups(n) * 2 * sizeof(double), kAlign);
+}
+
+wl_status wl_relative_frobenius_error(const void *W, const void *R, int64_t n, double *result, void *ws,
+                                      size_t ws_bytes, void *hip_stream) {
+    if (n < 1 || n >= ((int64_t)1 << 40)) return fail(WL_ERR_INVALID_ARG, "n=%lld is out of range", (long long)n);
+    if (!W || !R || !result || !ws) return fail(WL_ERR_INVALID_ARG, "W, R, result or ws is NULL");
+    if (!aligned(W, 16) || !aligned(R, 16)) return fail(WL_ERR_INVALID_ARG, "W or R is not 16-byte aligned");
+    if (!aligned(result, 8)) return fail(WL_ERR_INVALID_ARG, "result is not 8-byte aligned");
+    if (!aligned(ws, kAlign)) return fail(WL_ERR_INVALID_ARG, "the workspace is not 256-byte aligned");
+    const size_t need = wl_rel_frob_workspace_bytes(n);
+    if (ws_bytes < need) return fail(WL_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+    const size_t mb = (size_t)n * 2;
+    const Range wr{W, mb}, rr{R, mb};
+    if (overlaps({result, sizeof(double)}, wr) || overlaps({result, sizeof(double)}, rr) ||
+        overlaps({ws, need}, wr) || overlaps({ws, need}, rr) || overlaps({ws, need}, {result, sizeof(double)}))
+        return fail(WL_ERR_INVALID_ARG, "result or workspace overlaps an input");
+    wl::FrobJob job{};
+    job.W = static_cast<const uint16_t *>(W);
+    job.R = static_cast<const uint16_t *>(R);
+    job.n = n;
+    job.part = static_cast<double *>(ws);
+    job.n_wg = wl::frob_workgroups(n);
+    job.out = result;
+    const hipError_t e = wl::launch_frob(job, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(WL_ERR_HIP, "relative Frobenius error launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

@@ -168,4 +168,19 @@ struct Weff {
 };
 hipError_t launch_weff(const Weff &w, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// Relative Frobenius error of bf16 R against bf16 W (n elements each): fp64
+// partial sums per workgroup into part[2 * n_wg], then one workgroup writes
+// out[0] = ||W - R|| / ||W||.
+constexpr int kFrobMaxWorkgroups = 1024;
+struct FrobJob {
+    const uint16_t *W, *R;
+    int64_t n;
+    double *part;
+    int n_wg;
+    double *out;
+};
+int frob_workgroups(int64_t n);
+hipError_t launch_frob(const FrobJob &job, hipStream_t stream);
+
 }  // namespace wl

@@ -58,6 +58,12 @@ def _load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.wl_last_error.restype = ctypes.c_char_p
     lib.wl_abi_version.argtypes = []
     lib.wl_abi_version.restype = i32
+    lib.wl_bundle_size.argtypes = [ctypes.POINTER(P), i32, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.wl_bundle_size.restype = ctypes.c_int
+    lib.wl_rel_frob_workspace_bytes.argtypes = [ctypes.c_int64]
+    lib.wl_rel_frob_workspace_bytes.restype = sz
+    lib.wl_relative_frobenius_error.argtypes = [vp, vp, ctypes.c_int64, vp, vp, sz, vp]
+    lib.wl_relative_frobenius_error.restype = ctypes.c_int
     return lib
 
 
@@ -187,6 +193,32 @@ def wl_materialize_weff(th: dict, W_eff: torch.Tensor | None = None):
         W_eff = torch.empty(int(th["d_out"]), int(th["d_in"]), dtype=torch.bfloat16, device=dev)
     _check(lib.wl_materialize_weff(ctypes.byref(st), _ptr(W_eff), _stream(dev)))
     return W_eff
+
+
+def bundle_size(thetas: list) -> tuple:
+    """(bundle bytes, dense bytes) of a set of thetas: each distinct W0 counted once,
+    s, U and V per theta, against the bf16 dense weights they stand for."""
+    structs = [make_theta(t) for t in thetas]
+    arr = (ctypes.POINTER(Theta) * len(structs))(*[ctypes.pointer(st) for st in structs])
+    b, d = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib.wl_bundle_size(arr, len(structs), ctypes.byref(b), ctypes.byref(d)))
+    return int(b.value), int(d.value)
+
+
+def relative_frobenius_error(W: torch.Tensor, R: torch.Tensor) -> float:
+    """||W - R||_F / ||W||_F of two bf16 device tensors of equal size (waits for the
+    result)."""
+    for name, t in (("W", W), ("R", R)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor")
+    if W.numel() != R.numel():
+        raise ValueError("W and R must have the same number of elements")
+    n = W.numel()
+    out = torch.empty(1, dtype=torch.float64, device=W.device)
+    ws = torch.empty(max(int(lib.wl_rel_frob_workspace_bytes(n)), 256), dtype=torch.uint8, device=W.device)
+    _check(lib.wl_relative_frobenius_error(_ptr(W), _ptr(R), n, _ptr(out), _ptr(ws),
+                                            ws.numel(), _stream(W.device)))
+    return float(out.item())
 
 
 REGIME_AUTO, REGIME_GEMV, REGIME_MFMA, REGIME_GEMV_TWO_LAUNCH, REGIME_SKINNY = 0, 1, 2, 3, 4

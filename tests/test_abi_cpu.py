@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol(wl):
 
 
 def test_abi_version_and_status_strings(wl):
-    assert wl.abi_version() == 1
+    assert wl.abi_version() == 2
     assert wl.lib.wl_status_str(0) == b"ok"
     assert wl.lib.wl_status_str(4) == b"workspace too small"
     assert wl.lib.wl_status_str(99) == b"unknown status"
@@ -194,3 +194,63 @@ def test_library_resolves_its_own_symbols(wl):
     out = subprocess.run(["nm", "-u", "-C", wl.LIBRARY], capture_output=True, text=True, check=True).stdout
     own = [line for line in out.splitlines() if "wl::" in line]
     assert not own, f"unresolved library symbols: {own}"
+
+
+def bundle(wl, thetas):
+    arr = (ctypes.POINTER(wl.Theta) * len(thetas))(*[ctypes.pointer(t) for t in thetas])
+    b, d = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = wl.lib.wl_bundle_size(arr, len(thetas), ctypes.byref(b), ctypes.byref(d))
+    return st, b.value, d.value
+
+
+# Gemma-3-1B-shaped families (d_in, d_out): q, k, v, o, gate, up, down.
+FAMILIES = ((1152, 1024), (1152, 256), (1152, 256), (1024, 1152), (1152, 6912), (1152, 6912), (6912, 1152))
+
+
+def layer_thetas(wl, r, n_layers, shared):
+    # Fake, distinct 256-byte aligned W0 addresses; with `shared` every layer uses
+    # the same W0 per family (one band of n_layers layers).
+    out = []
+    for layer in range(n_layers):
+        for f, (d_in, d_out) in enumerate(FAMILIES):
+            w0 = A + 0x100 * (f if shared else layer * len(FAMILIES) + f)
+            out.append(wl.Theta(w0, B, C, D, d_in, d_out, r))
+    return out
+
+
+@pytest.mark.parametrize("r,ratio", [(4, 0.0445), (16, 0.0585), (32, 0.0772)])
+def test_bundle_ratio_of_shared_w0_layers(wl, r, ratio):
+    # 26 layers sharing one W0 per family against 26 dense layers: the ratios
+    # derived for the batched-decode shapes (theta bundle over original weights).
+    st, b, d = bundle(wl, layer_thetas(wl, r, 26, shared=True))
+    assert st == 0
+    assert d == 26 * sum(2 * i * o for i, o in FAMILIES)
+    assert round(b / d, 4) == ratio
+
+
+def test_bundle_of_own_w0_layers_exceeds_dense(wl):
+    # One W0 per layer: the bundle is the dense size plus s, U and V (1.006 to 1.039).
+    for r, lo, hi in ((4, 1.005, 1.007), (32, 1.038, 1.040)):
+        st, b, d = bundle(wl, layer_thetas(wl, r, 26, shared=False))
+        assert st == 0 and lo < b / d < hi
+
+
+def test_bundle_checks(wl):
+    t = [wl.Theta(A, None, B, C, 64, 32, 4), wl.Theta(A, None, B, C, 64, 48, 4)]
+    assert bundle(wl, t)[0] == 1                      # shared W0 with another shape
+    assert bundle(wl, [wl.Theta(A, None, B, C, 60, 32, 4)])[0] == 1
+    st, b, d = bundle(wl, [wl.Theta(A, None, B, C, 64, 32, 0)])
+    assert (st, b, d) == (0, 2 * 64 * 32, 2 * 64 * 32)   # r = 0, no s: the bundle is W0 itself
+
+
+def test_rel_frob_checks(wl):
+    f = wl.lib.wl_relative_frobenius_error
+    need = wl.lib.wl_rel_frob_workspace_bytes(1 << 20)
+    assert need >= 16 and need % 256 == 0
+    assert wl.lib.wl_rel_frob_workspace_bytes(0) == 0
+    assert f(None, B, 64, C, D, need, None) == 1
+    assert f(A + 2, B, 64, C, D, need, None) == 1                # misaligned W
+    assert f(A, B, 0, C, D, need, None) == 1                     # empty
+    assert f(A, B, 64, C + 4, D, need, None) == 1                # misaligned result
+    assert f(A, B, 64, C, D, 0, None) == 4                       # workspace too small
+    assert f(A, B, 64, A + 8, D, need, None) == 1                # result on top of W
