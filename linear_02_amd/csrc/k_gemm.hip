@@ -92,7 +92,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
     constexpr int BM = C::BM, BN = C::BN, KP = C::KP, NT = C::kThreads;
     __shared__ u32x4 lds[C::LDS_PIECES];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
 
     // Tile numbering: XCD x (blockIdx % 8) takes a contiguous band of logical tiles.
@@ -102,13 +102,16 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
     else
         for (int c = 0; c < g.n_ch; ++c) n_nt += (g.ch[c].d_out + BN - 1) / BN;
     const int n_mt = (g.T + BM - 1) / BM;
-    const int total = n_nt * n_mt;
+    const int tiles = n_nt * n_mt, total = tiles * g.ksplit;
     int tile;
     {
         const int per = (total + 7) / 8, x = blockIdx.x & 7, slot = blockIdx.x >> 3;
         const int full = total - 8 * (per - 1);   // XCDs 0..full-1 hold `per` tiles, the rest per-1
         tile = x < full ? x * per + slot : full * per + (x - full) * (per - 1) + slot;
     }
+    // Split of the input axis (split slowest, so that an XCD's band mostly shares one).
+    const int split = tile / tiles;
+    tile -= split * tiles;
     // Within the band: token tiles fastest (consecutive tiles share W0 rows), or
     // output tiles fastest (they share x rows) when x is the larger operand, so
     // that each XCD re-reads the smaller one.
@@ -128,7 +131,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
     const int d_out = C0.d_out;
     const int m0 = mt * BM;
     const int d_in = g.d_in, nch = d_in >> 3;
-    const int nk = (d_in + BK - 1) / BK;
+    const int nk_all = (d_in + BK - 1) / BK;
+    // This split's steps [kt0, nk) (the split plan counts 64-wide steps; the split tile has BK = 64).
+    const int kt0 = g.ksplit > 1 ? split * g.kb_per_split : 0;
+    const int nk = g.ksplit > 1 ? min(nk_all, kt0 + g.kb_per_split) : nk_all;
 
     const u32x4 *xg = reinterpret_cast<const u32x4 *>(g.x);
     const Child *ch[P];
@@ -144,31 +150,6 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[p][i][j][e] = 0.f;
-
-    // The ring: the 64 lanes of one load write 64 consecutive 16-byte LDS slots,
-    // so each lane fetches the global piece that belongs in its (swizzled) slot.
-    const u32x4 *zero = reinterpret_cast<const u32x4 *>(kZeroPiece);
-    auto issue = [&](int kt, int sl) {
-        u32x4 *st = lds + sl * C::STAGE_PIECES;
-#pragma unroll
-        for (int h = 0; h < C::A_PER; ++h) {
-            const int q = h * NT + tid, row = q / KP, kc = (q % KP) ^ swz_key<KP>(row), gk = kt * KP + kc;
-            const u32x4 *src = (gk < nch && m0 + row < g.T) ? xg + (size_t)(m0 + row) * nch + gk : zero;
-            lds_dma16(src, st + h * NT + wave * kWave);
-        }
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const u32x4 *wgp = reinterpret_cast<const u32x4 *>(ch[p]->W0);
-            u32x4 *bst = st + C::A_PIECES + p * C::B_PIECES;
-#pragma unroll
-            for (int h = 0; h < C::B_PER; ++h) {
-                const int q = h * NT + tid, row = q / KP, kc = (q % KP) ^ swz_key<KP>(row), gk = kt * KP + kc;
-                const u32x4 *src = (gk < nch && n0 + row < d_out) ? wgp + (size_t)(n0 + row) * nch + gk : zero;
-                lds_dma16(src, bst + h * NT + wave * kWave);
-            }
-        }
-    };
-
 
     // Full steps (the whole 64-wide K block inside d_in) take precomputed per-lane
     // piece offsets: tile rows past T or d_out read the last valid row instead (their
@@ -191,6 +172,34 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
             b_off[p][h] = min(n0 + row, dout_p - 1) * nch + kc;
         }
     }
+    // The ring: the 64 lanes of one load write 64 consecutive 16-byte LDS slots,
+    // so each lane fetches the global piece that belongs in its (swizzled) slot.
+    // This is the checked form for a partial last step; it reads only values
+    // already in registers (a kernel-argument load inside the loop would make
+    // every LDS wait a full drain).
+    const u32x4 *zero = reinterpret_cast<const u32x4 *>(kZeroPiece);
+    int dout_of[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) dout_of[p] = ch[p]->d_out;
+    auto issue = [&](int kt, int sl) {
+        u32x4 *st = lds + sl * C::STAGE_PIECES;
+#pragma unroll
+        for (int h = 0; h < C::A_PER; ++h) {
+            const int q = h * NT + tid, row = q / KP, kc = (q % KP) ^ swz_key<KP>(row), gk = kt * KP + kc;
+            const u32x4 *src = (gk < nch && m0 + row < g.T) ? xg + (size_t)(m0 + row) * nch + gk : zero;
+            lds_dma16(src, st + h * NT + wave * kWave);
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            u32x4 *bst = st + C::A_PIECES + p * C::B_PIECES;
+#pragma unroll
+            for (int h = 0; h < C::B_PER; ++h) {
+                const int q = h * NT + tid, row = q / KP, kc = (q % KP) ^ swz_key<KP>(row), gk = kt * KP + kc;
+                const u32x4 *src = (gk < nch && n0 + row < dout_of[p]) ? wg[p] + (size_t)(n0 + row) * nch + gk : zero;
+                lds_dma16(src, bst + h * NT + wave * kWave);
+            }
+        }
+    };
     auto issue_full = [&](int kt, int sl) {
         u32x4 *st = lds + sl * C::STAGE_PIECES;
         const u32x4 *xk = xg + kt * KP;
@@ -254,16 +263,17 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
 
     // One barrier per step: after it, stage kt has landed for every wave and every
     // wave has finished step kt - 1, so that step's slot takes stage kt + D - 1.
-    for (int s0 = 0; s0 < D - 1 && s0 < nk; ++s0) issue_any(s0, s0);
-    for (int kt = 0; kt < nk; ++kt) {
+    // Ring slots count from the split's first step.
+    for (int s0 = 0; s0 < D - 1 && kt0 + s0 < nk; ++s0) issue_any(kt0 + s0, s0);
+    for (int kt = kt0; kt < nk; ++kt) {
         // This wave's loads of stage kt are done; up to D - 2 later stages stay in flight.
         const int ahead = min(D - 2, nk - 1 - kt);
         if (ahead >= 2) wait_vm<2 * C::PER_STAGE>();
         else if (ahead == 1) wait_vm<C::PER_STAGE>();
         else wait_vm<0>();
         barrier();
-        if (kt + D - 1 < nk) issue_any(kt + D - 1, (kt + D - 1) % D);
-        compute(lds + (kt % D) * C::STAGE_PIECES);
+        if (kt + D - 1 < nk) issue_any(kt + D - 1, (kt - kt0 + D - 1) % D);
+        compute(lds + ((kt - kt0) % D) * C::STAGE_PIECES);
     }
 
     // ---- epilogue ----
@@ -279,7 +289,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
 #pragma unroll
             for (int i = 0; i < TM; ++i) acc[p][i][j] *= sv;
         }
-        if constexpr (NV > 0) {
+        // The rank term is added once: by split 0 when the input axis is split.
+        if constexpr (NV > 0) if (split == 0) {
             const int r = Cp.r, S = Cp.vtx_splits;
             const size_t ss = (size_t)g.T * r;        // split stride of the partials
             for (int k0 = 0; k0 < r; k0 += 16) {
@@ -352,6 +363,24 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
         }
     }
 
+    if (g.ksplit > 1) {
+        // Split partials, fp32 [split][T][d_out] (single child, no pair); the
+        // reduction launch adds them in split order and rounds once.
+        float *part = g.part + (size_t)split * g.T * d_out;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int o = n0 + (wn * TN + j) * 32 + fr;
+            if (o >= d_out) continue;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = m0 + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * fk + (e & 3);
+                    if (t < g.T) part[(size_t)t * d_out + o] = acc[0][i][j][e];
+                }
+        }
+        return;
+    }
     const int col0 = g.pair ? 0 : C0.col0;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -378,9 +407,36 @@ hipError_t launch_cfg(const Gemm &g, hipStream_t stream) {
         n_nt = (g.ch[0].d_out + C::BN - 1) / C::BN;
     else
         for (int c = 0; c < g.n_ch; ++c) n_nt += (g.ch[c].d_out + C::BN - 1) / C::BN;
-    const int total = n_nt * ((g.T + C::BM - 1) / C::BM);
+    const int total = n_nt * ((g.T + C::BM - 1) / C::BM) * g.ksplit;
     hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BK, P, D, NV>), dim3(total), dim3(C::kThreads), 0, stream, g);
     return hipGetLastError();
+}
+
+// y[t][col0 + o] = bf16( sum over splits q, in order, of part[q][t][o] ); four
+// consecutive outputs per thread (8-byte stores when the row offsets allow).
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float *part, int S, int T, int d_out, uint16_t *y,
+                                                           int ldy, int col0) {
+    const int nq = (d_out + 3) >> 2;
+    const int64_t n = (int64_t)T * nq;
+    const size_t ss = (size_t)T * d_out;
+    const bool vec = ((d_out | ldy | col0) & 3) == 0;
+    for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < n; it += (int64_t)gridDim.x * 256) {
+        const int t = (int)(it / nq), o = (int)(it - (int64_t)t * nq) * 4;
+        const float *src = part + (size_t)t * d_out + o;
+        uint16_t *dst = y + (size_t)t * ldy + col0 + o;
+        if (vec) {
+            f32x4 a = ldg(reinterpret_cast<const f32x4 *>(src));
+            for (int q = 1; q < S; ++q) a += ldg(reinterpret_cast<const f32x4 *>(src + q * ss));
+            *reinterpret_cast<u32x2 *>(dst) = u32x2{(uint32_t)f_bf16(a.x) | ((uint32_t)f_bf16(a.y) << 16),
+                                                    (uint32_t)f_bf16(a.z) | ((uint32_t)f_bf16(a.w) << 16)};
+        } else {
+            for (int e = 0; e < 4 && o + e < d_out; ++e) {
+                float a = src[e];
+                for (int q = 1; q < S; ++q) a += src[q * ss + e];
+                dst[e] = f_bf16(a);
+            }
+        }
+    }
 }
 
 template <int WM, int WN, int TM, int TN, int BK, int D, int P>
@@ -414,6 +470,10 @@ hipError_t launch_nv(const Gemm &g, hipStream_t stream) {
 #ifndef WL_GEMM_TILE_SMALL_PAIR
 #define WL_GEMM_TILE_SMALL_PAIR 2, 2, 2, 1, 64, 2
 #endif
+// Tile of the split-input-axis GEMM (long inputs, few output tiles).
+#ifndef WL_GEMM_TILE_SPLIT
+#define WL_GEMM_TILE_SPLIT 4, 2, 2, 2, 64, 3
+#endif
 
 namespace {
 
@@ -433,13 +493,49 @@ int tiles_of(const Gemm &g) {
     return n_nt * ((g.T + BM - 1) / BM);
 }
 
+constexpr int kSplitMinSteps = 24;   // 64-wide input steps per split, at least
+constexpr int kComputeUnits = 256;
+
+template <int WM, int WN, int TM, int TN, int BK, int D>
+constexpr int tile_bk() { return BK; }
+static_assert(tile_bk<WL_GEMM_TILE_SPLIT>() == 64, "the split plan counts 64-wide steps");
+
 }  // namespace
+
+GemmSplit gemm_split_plan(int T, int d_in, int rows, int n_ch, int pair) {
+    const int nk = (d_in + 63) / 64;
+    GemmSplit p{1, nk};
+    if (pair || n_ch != 1 || T <= 0 || rows <= 0) return p;
+    Gemm g{};
+    g.n_ch = 1;
+    g.T = T;
+    g.ch[0].d_out = rows;
+    // Split only where every unsplit tile choice leaves compute units without work.
+    if (tiles_of<WL_GEMM_TILE_BIG>(g) >= kFillTiles || tiles_of<WL_GEMM_TILE>(g) >= kFillTiles) return p;
+    const int tiles = tiles_of<WL_GEMM_TILE_SPLIT>(g);
+    int S = kComputeUnits / tiles;
+    if (S > nk / kSplitMinSteps) S = nk / kSplitMinSteps;
+    if (S < 2) return p;
+    p.kb_per_split = (nk + S - 1) / S;
+    p.ksplit = (nk + p.kb_per_split - 1) / p.kb_per_split;
+    return p;
+}
 
 hipError_t launch_gemm(const Gemm &g_in, hipStream_t stream) {
     Gemm g = g_in;
     int rows = 0;
     for (int c = 0; c < (g.pair ? 1 : g.n_ch); ++c) rows += g.ch[c].d_out;
     g.col_fast = g.T > rows * (g.pair ? 2 : 1);   // x ([T][d_in]) larger than the W0 rows it meets
+    if (g.ksplit > 1) {
+        const hipError_t e = launch_nv<WL_GEMM_TILE_SPLIT, 1>(g, stream);
+        if (e != hipSuccess) return e;
+        const int64_t n = (int64_t)g.T * ((g.ch[0].d_out + 3) / 4);
+        const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+        hipLaunchKernelGGL(split_reduce_kernel, dim3(blocks), dim3(256), 0, stream, g.part, g.ksplit, g.T,
+                           g.ch[0].d_out, g.y, g.ldy, g.ch[0].col0);
+        return hipGetLastError();
+    }
+    g.ksplit = 1;
     if (g.pair) {
         if (tiles_of<WL_GEMM_TILE_BIG_PAIR>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_BIG_PAIR, 2>(g, stream);
         if (tiles_of<WL_GEMM_TILE_PAIR>(g) >= kFillTiles) return launch_nv<WL_GEMM_TILE_PAIR, 2>(g, stream);

@@ -121,6 +121,8 @@ Kind choose(int T, int d_in, int sum_r) {
 //   skinny vpart      fp32 [n_vsl][n_ch][T][kMaxRank] V^T x slice partials
 //   mm_vtx            fp32 [S][T][r_c] per child: V^T x split partials of the
 //                     matrix-core regime (the largest of the call's projections)
+//   mm_part           fp32 [ksplit][T][d_out]: input-axis split partials of the
+//                     matrix-core regime (the largest of the call's projections)
 //   h                 bf16 [T][d_ff] (MLP only)
 
 constexpr size_t kReservedBytes = 256;
@@ -129,6 +131,7 @@ struct Layout {
     size_t gemv_partial = 0;
     size_t sk_part = 0, sk_vpart = 0;
     size_t mm_vtx = 0;
+    size_t mm_part = 0;
     size_t h = 0;
     size_t total = 0;
 };
@@ -185,6 +188,14 @@ Layout layout(int op, const wl_theta *const *th, int T) {
     }
     L.mm_vtx = off;
     off = round_up(off + mm, kAlign);
+    size_t mp = 0;
+    for (int j = 0; j < n; ++j) {
+        const wl::GemmSplit sp = wl::gemm_split_plan(T, ps[j].d_in, ps[j].rows, ps[j].n_ch, ps[j].P == 2);
+        const size_t b = sp.ksplit > 1 ? (size_t)sp.ksplit * T * ps[j].rows * 4 : 0;
+        mp = b > mp ? b : mp;
+    }
+    L.mm_part = off;
+    off = round_up(off + mp, kAlign);
     if (op == WL_OP_MLP) {
         L.h = off;
         off = round_up(off + (size_t)T * th[0]->d_out * 2, kAlign);
@@ -334,6 +345,10 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
         g.T = T;
         g.x = static_cast<const uint16_t *>(x);
         g.y = static_cast<uint16_t *>(y);
+        const wl::GemmSplit sp = wl::gemm_split_plan(T, d_in, rows, n_ch, pair);
+        g.ksplit = sp.ksplit;
+        g.kb_per_split = sp.kb_per_split;
+        g.part = reinterpret_cast<float *>(ws + L.mm_part);
         e = wl::launch_gemm(g, stream);
     }
     if (e != hipSuccess) return fail(WL_ERR_HIP, "projection launch failed: %s", hipGetErrorString(e));

@@ -154,7 +154,20 @@ struct Gemm {
     const uint16_t *x;    // bf16 [T][d_in]
     uint16_t *y;          // bf16 [T][ldy]
     int col_fast;         // tile order within an XCD's band (set by launch_gemm)
+    // Split of the input axis (single child, no pair): ksplit workgroups per
+    // output tile, each over kb_per_split 64-wide steps, writing fp32 partials
+    // part[ksplit][T][d_out]; a second launch adds them in order into y.
+    // ksplit = 1: no split (part unused).
+    int ksplit;
+    int kb_per_split;
+    float *part;
 };
+struct GemmSplit {
+    int ksplit, kb_per_split;
+};
+// The split used for a GEMM-regime projection of `rows` outputs (n_ch children,
+// pair or not) at T tokens; the same plan sizes the workspace.
+GemmSplit gemm_split_plan(int T, int d_in, int rows, int n_ch, int pair);
 hipError_t launch_gemm(const Gemm &g, hipStream_t stream);
 
 // ---------------------------------------------------------------------------

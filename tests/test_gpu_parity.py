@@ -75,6 +75,8 @@ LINEAR_CASES = [
     (6912, 1152, 32, 17),     # long input axis, many splits, ragged tokens
     (1024, 1152, 4, 64),      # two token blocks
     (136, 129, 17, 12),       # ragged rows and input axis
+    (3080, 136, 8, 70),       # matrix cores: input axis split in two, partial last step
+    (3080, 131, 8, 70),       # the same with an odd output count (scalar reduction)
 ]
 
 
