@@ -18,6 +18,8 @@ reconstruction" page (reconstruction equation and its per-element expansion):
 Activations x[t, i] are bf16 [T][d_in]. Values are drawn in fp32 from a normal
 distribution (the second argument is the standard deviation) and rounded to
 bf16 with round-to-nearest-even by torch's dtype conversion; s stays fp32.
+With ``dtype=torch.float32`` (the fp32 variant of every operation) the same
+draws are kept in fp32 unrounded.
 
 The pages print no checkpoint values, so these draws stand in for the Gemma
 checkpoints their measurements use.
@@ -55,25 +57,27 @@ def _normal(gen: torch.Generator, shape, std: float, mean: float = 0.0) -> torch
 
 def theta(gen: torch.Generator, d_in: int, d_out: int, r: int, *,
           w0_std: float = 0.02, uv_std: float = 0.01, s_std: float = 0.01,
-          W0: torch.Tensor | None = None) -> dict:
-    """Draw one theta bundle (CPU tensors). Draw order: W0 (unless given), s, U, V."""
+          W0: torch.Tensor | None = None, dtype: torch.dtype = torch.bfloat16) -> dict:
+    """Draw one theta bundle (CPU tensors). Draw order: W0 (unless given), s, U, V.
+    W0, U and V are ``dtype`` (bf16 or fp32); s is fp32."""
     if W0 is None:
-        W0 = _normal(gen, (d_out, d_in), w0_std).to(torch.bfloat16)
+        W0 = _normal(gen, (d_out, d_in), w0_std).to(dtype)
     else:
-        assert tuple(W0.shape) == (d_out, d_in) and W0.dtype == torch.bfloat16
+        assert tuple(W0.shape) == (d_out, d_in) and W0.dtype == dtype
     s = _normal(gen, (d_out,), s_std, mean=1.0)
-    U = _normal(gen, (d_out, r), uv_std).to(torch.bfloat16)
-    V = _normal(gen, (d_in, r), uv_std).to(torch.bfloat16)
+    U = _normal(gen, (d_out, r), uv_std).to(dtype)
+    V = _normal(gen, (d_in, r), uv_std).to(dtype)
     return dict(W0=W0, s=s, U=U, V=V, d_in=d_in, d_out=d_out, r=r)
 
 
-def activations(gen: torch.Generator, T: int, d: int, std: float = 1.0) -> torch.Tensor:
-    """x ~ N(0, std) rounded to bf16, shape [T][d]."""
-    return _normal(gen, (T, d), std).to(torch.bfloat16)
+def activations(gen: torch.Generator, T: int, d: int, std: float = 1.0,
+                dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """x ~ N(0, std) as ``dtype`` (bf16: rounded), shape [T][d]."""
+    return _normal(gen, (T, d), std).to(dtype)
 
 
 def layer(gen: torch.Generator, dims: dict, r: int, *, w0_std: float = 0.02,
-          shared_W0: dict | None = None) -> dict:
+          shared_W0: dict | None = None, dtype: torch.dtype = torch.bfloat16) -> dict:
     """One decoder layer's seven theta bundles, drawn in the fixed family order.
 
     ``shared_W0`` maps family -> an already-drawn W0 (band sharing: one W0 per
@@ -84,17 +88,17 @@ def layer(gen: torch.Generator, dims: dict, r: int, *, w0_std: float = 0.02,
     for fam in FAMILIES:
         d_in, d_out = shapes[fam]
         w = None if shared_W0 is None else shared_W0.get(fam)
-        out[fam] = theta(gen, d_in, d_out, r, w0_std=w0_std, W0=w)
+        out[fam] = theta(gen, d_in, d_out, r, w0_std=w0_std, W0=w, dtype=dtype)
     return out
 
 
-def layer_inputs(gen: torch.Generator, dims: dict, T: int) -> dict:
+def layer_inputs(gen: torch.Generator, dims: dict, T: int, dtype: torch.dtype = torch.bfloat16) -> dict:
     """The three distinct projection inputs of a layer: attention input (feeds
     Q/K/V), attention output (feeds O) and MLP input (feeds gate/up)."""
     return dict(
-        x_attn=activations(gen, T, dims["d_model"]),
-        x_o=activations(gen, T, dims["q"]),
-        x_mlp=activations(gen, T, dims["d_model"]),
+        x_attn=activations(gen, T, dims["d_model"], dtype=dtype),
+        x_o=activations(gen, T, dims["q"], dtype=dtype),
+        x_mlp=activations(gen, T, dims["d_model"], dtype=dtype),
     )
 
 

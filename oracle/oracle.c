@@ -19,8 +19,10 @@
  *       y[t,o] = s[o] * sum_i W0[o,i] * x[t,i]  +  sum_k U[o,k] * sum_i V[i,k] * x[t,i]
  *
  * Layouts (row-major, contiguous): W0 [d_out][d_in], s [d_out], U [d_out][r],
- * V [d_in][r], x [T][d_in], y [T][d_out]. bf16 tensors are passed as their
- * 16-bit patterns.
+ * V [d_in][r], x [T][d_in], y [T][d_out]. W0, U, V and x share one element
+ * type per call: bf16 (passed as 16-bit patterns) or IEEE binary32 (the
+ * "also supports float32" remark of the custom-op description on the
+ * "In-kernel reconstruction" page); s is always binary32.
  */
 #include <math.h>
 #include <stdint.h>
@@ -31,12 +33,15 @@
  * introduction: a shared block W0 per band, a per-row scale s and a low-rank
  * delta U, V of rank r). s may be NULL, meaning every s[o] is 1. U and V may be
  * NULL only when r == 0. */
+enum { ORC_BF16 = 0, ORC_F32 = 1 };
+
 typedef struct {
-    const uint16_t *W0;
+    const void *W0;
     const float *s;
-    const uint16_t *U;
-    const uint16_t *V;
+    const void *U;
+    const void *V;
     int64_t d_in, d_out, r;
+    int64_t dtype;          /* ORC_BF16 or ORC_F32: W0, U, V and the call's x (and y's rounding) */
 } orc_theta;
 
 /* The exact value of a bf16 bit pattern: bf16 is the upper half of an IEEE
@@ -82,6 +87,14 @@ uint16_t orc_bf16_rne(double v)
 
 double orc_bf16_value(uint16_t bits) { return bf16_value(bits); }
 
+/* Element j of a tensor of the given element type, exactly, as a double. */
+static double elem(const void *p, int64_t dtype, int64_t j)
+{
+    if (dtype == ORC_F32)
+        return (double)((const float *)p)[j];
+    return bf16_value(((const uint16_t *)p)[j]);
+}
+
 /* tanh-approximated GELU (Hendrycks & Gimpel, 2016):
  *   gelu(z) = 0.5 * z * (1 + tanh(sqrt(2/pi) * (z + 0.044715 * z^3)))
  * The pages name an activation between gate/up and down ("In-kernel
@@ -102,30 +115,30 @@ double orc_gelu_tanh(double z)
  *   bound[t,o] = |s[o]| * sum_i |W0[o,i] * x[t,i]| + sum_k |U[o,k] * vtx[k]|
  * y and bound are [T][d_out], fp64, unrounded. bound may be NULL.
  * Returns 0, or -1 if scratch memory cannot be had. */
-int orc_linear(const orc_theta *th, int64_t T, const uint16_t *x, double *y, double *bound)
+int orc_linear(const orc_theta *th, int64_t T, const void *x, double *y, double *bound)
 {
-    const int64_t d_in = th->d_in, d_out = th->d_out, r = th->r;
+    const int64_t d_in = th->d_in, d_out = th->d_out, r = th->r, dt = th->dtype;
     double *vtx = (double *)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
     if (!vtx)
         return -1;
     for (int64_t t = 0; t < T; ++t) {
-        const uint16_t *xt = x + t * d_in;
+        const int64_t x0 = t * d_in;   /* token t's row of x */
         for (int64_t k = 0; k < r; ++k) {
             double acc = 0.0;
             for (int64_t i = 0; i < d_in; ++i)
-                acc += bf16_value(th->V[i * r + k]) * bf16_value(xt[i]);
+                acc += elem(th->V, dt, i * r + k) * elem(x, dt, x0 + i);
             vtx[k] = acc;
         }
         for (int64_t o = 0; o < d_out; ++o) {
             double m = 0.0, m_abs = 0.0;
             for (int64_t i = 0; i < d_in; ++i) {
-                double p = bf16_value(th->W0[o * d_in + i]) * bf16_value(xt[i]);
+                double p = elem(th->W0, dt, o * d_in + i) * elem(x, dt, x0 + i);
                 m += p;
                 m_abs += fabs(p);
             }
             double delta = 0.0, delta_abs = 0.0;
             for (int64_t k = 0; k < r; ++k) {
-                double p = bf16_value(th->U[o * r + k]) * vtx[k];
+                double p = elem(th->U, dt, o * r + k) * vtx[k];
                 delta += p;
                 delta_abs += fabs(p);
             }
@@ -141,11 +154,14 @@ int orc_linear(const orc_theta *th, int64_t T, const uint16_t *x, double *y, dou
 
 /* "In-kernel reconstruction", Q/K/V fusion: the three attention projections
  * share one input x; the fused result is the three projections' outputs side
- * by side, columns Q | K | V. y and bound are [T][dq + dk + dv]. */
+ * by side, columns Q | K | V. y and bound are [T][dq + dk + dv]. The three
+ * thetas must share one element type (else -1). */
 int orc_qkv(const orc_theta *q, const orc_theta *k, const orc_theta *v, int64_t T,
-            const uint16_t *x, double *y, double *bound)
+            const void *x, double *y, double *bound)
 {
     const orc_theta *child[3] = {q, k, v};
+    if (k->dtype != q->dtype || v->dtype != q->dtype)
+        return -1;
     int64_t width = q->d_out + k->d_out + v->d_out;
     int64_t col0 = 0;
     for (int c = 0; c < 3; ++c) {
@@ -174,37 +190,47 @@ int orc_qkv(const orc_theta *q, const orc_theta *k, const orc_theta *v, int64_t 
  * up, activation and down in one operation:
  *   g = linear(gate, x),  u = linear(up, x)
  *   h = gelu_tanh(g) * u
- *   y = linear(down, bf16(h))
- * The intermediate h is rounded once to bf16 (round-to-nearest-even) before
- * the down projection: down is a bf16-input projection like every other, and
- * the pages' three-call fallback casts each call's result to the activation
- * dtype ("In-kernel reconstruction", the custom-op path: accumulate in float32,
- * cast back to the output dtype). bound is that of the down projection with
- * x := bf16(h). h_bits (optional, [T][d_ff]) receives the rounded h. */
+ *   y = linear(down, round(h))
+ * The intermediate h is rounded once to the call's element type (bf16 or
+ * binary32, round-to-nearest-even) before the down projection: down is a
+ * projection like every other, and the pages' three-call fallback casts each
+ * call's result to the activation dtype ("In-kernel reconstruction", the
+ * custom-op path: accumulate in float32, cast back to the output dtype). bound
+ * is that of the down projection with x := round(h). h_out (optional,
+ * [T][d_ff]) receives the rounded h: bf16 patterns or binary32 values. The
+ * three thetas must share one element type (else -1). */
 int orc_mlp(const orc_theta *gate, const orc_theta *up, const orc_theta *down, int64_t T,
-            const uint16_t *x, double *y, double *bound, uint16_t *h_bits)
+            const void *x, double *y, double *bound, void *h_out)
 {
-    int64_t d_ff = gate->d_out;
+    int64_t d_ff = gate->d_out, dt = gate->dtype;
+    if (up->dtype != dt || down->dtype != dt)
+        return -1;
     size_t n = (size_t)(T * d_ff > 0 ? T * d_ff : 1);
+    size_t esz = dt == ORC_F32 ? sizeof(float) : sizeof(uint16_t);
     double *g = (double *)malloc(sizeof(double) * n);
     double *u = (double *)malloc(sizeof(double) * n);
-    uint16_t *hb = (uint16_t *)malloc(sizeof(uint16_t) * n);
+    void *hr = malloc(esz * n);
     int rc = -1;
-    if (!g || !u || !hb)
+    if (!g || !u || !hr)
         goto done;
     if (orc_linear(gate, T, x, g, NULL) != 0 || orc_linear(up, T, x, u, NULL) != 0)
         goto done;
-    for (int64_t j = 0; j < T * d_ff; ++j)
-        hb[j] = orc_bf16_rne(orc_gelu_tanh(g[j]) * u[j]);
-    if (orc_linear(down, T, hb, y, bound) != 0)
+    for (int64_t j = 0; j < T * d_ff; ++j) {
+        double h = orc_gelu_tanh(g[j]) * u[j];
+        if (dt == ORC_F32)
+            ((float *)hr)[j] = (float)h;   /* C conversion: round to nearest, ties to even */
+        else
+            ((uint16_t *)hr)[j] = orc_bf16_rne(h);
+    }
+    if (orc_linear(down, T, hr, y, bound) != 0)
         goto done;
-    if (h_bits)
-        memcpy(h_bits, hb, sizeof(uint16_t) * (size_t)(T * d_ff));
+    if (h_out)
+        memcpy(h_out, hr, esz * (size_t)(T * d_ff));
     rc = 0;
 done:
     free(g);
     free(u);
-    free(hb);
+    free(hr);
     return rc;
 }
 
@@ -217,14 +243,14 @@ done:
  * sum_k |U[o,k]*V[i,k]|. bound may be NULL. */
 int orc_weff(const orc_theta *th, double *W_eff, double *bound)
 {
-    const int64_t d_in = th->d_in, d_out = th->d_out, r = th->r;
+    const int64_t d_in = th->d_in, d_out = th->d_out, r = th->r, dt = th->dtype;
     for (int64_t o = 0; o < d_out; ++o) {
         double so = th->s ? (double)th->s[o] : 1.0;
         for (int64_t i = 0; i < d_in; ++i) {
-            double base = so * bf16_value(th->W0[o * d_in + i]);
+            double base = so * elem(th->W0, dt, o * d_in + i);
             double delta = 0.0, delta_abs = 0.0;
             for (int64_t k = 0; k < r; ++k) {
-                double p = bf16_value(th->U[o * r + k]) * bf16_value(th->V[i * r + k]);
+                double p = elem(th->U, dt, o * r + k) * elem(th->V, dt, i * r + k);
                 delta += p;
                 delta_abs += fabs(p);
             }

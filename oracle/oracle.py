@@ -5,8 +5,10 @@ CPU-baseline leg may import this module. It marshals arrays into the C oracle
 and back; it computes nothing of the method itself.
 
 Thetas are dicts as produced by ``linear_02_amd.inputs.theta``: W0, U, V bf16
-tensors, s an fp32 tensor or None, plus d_in, d_out, r. Results are float64
-numpy arrays.
+(or fp32) tensors, s an fp32 tensor or None, plus d_in, d_out, r. The element
+type of W0 selects the oracle's: bf16 tensors travel as their 16-bit patterns,
+fp32 ones as binary32 values, and x must have the same type. Results are
+float64 numpy arrays.
 """
 from __future__ import annotations
 
@@ -31,10 +33,33 @@ def build(source: str = SOURCE, out: str = LIBRARY) -> str:
     return out
 
 
+BF16, F32 = 0, 1
+
+
 class _Theta(ctypes.Structure):
     _fields_ = [("W0", ctypes.c_void_p), ("s", ctypes.c_void_p), ("U", ctypes.c_void_p),
                 ("V", ctypes.c_void_p), ("d_in", ctypes.c_int64), ("d_out", ctypes.c_int64),
-                ("r", ctypes.c_int64)]
+                ("r", ctypes.c_int64), ("dtype", ctypes.c_int64)]
+
+
+def _dtype_of(t) -> int:
+    """Element type code of a tensor: F32 for float32, BF16 for bf16 (or uint16 patterns)."""
+    if isinstance(t, np.ndarray):
+        return F32 if t.dtype == np.float32 else BF16
+    import torch
+    return F32 if t.dtype == torch.float32 else BF16
+
+
+def _elems(t, dtype: int) -> np.ndarray:
+    """Tensor -> contiguous array of the oracle's element type ``dtype``."""
+    if dtype == BF16:
+        return _bits(t)
+    if isinstance(t, np.ndarray):
+        assert t.dtype == np.float32, t.dtype
+        return np.ascontiguousarray(t)
+    import torch
+    assert t.dtype == torch.float32, t.dtype
+    return np.ascontiguousarray(t.detach().cpu().contiguous().numpy())
 
 
 def _bits(t) -> np.ndarray:
@@ -90,10 +115,11 @@ class Oracle:
     # -- marshalling ----------------------------------------------------------------
     @staticmethod
     def _theta(th: dict):
-        keep = dict(W0=_bits(th["W0"]), s=_f32(th.get("s")))
+        dt = _dtype_of(th["W0"])
+        keep = dict(W0=_elems(th["W0"], dt), s=_f32(th.get("s")))
         r = int(th["r"])
-        keep["U"] = _bits(th["U"]) if r > 0 else None
-        keep["V"] = _bits(th["V"]) if r > 0 else None
+        keep["U"] = _elems(th["U"], dt) if r > 0 else None
+        keep["V"] = _elems(th["V"], dt) if r > 0 else None
         d_in, d_out = int(th["d_in"]), int(th["d_out"])
         assert keep["W0"].size == d_out * d_in
         if keep["s"] is not None:
@@ -101,14 +127,14 @@ class Oracle:
         if r > 0:
             assert keep["U"].size == d_out * r and keep["V"].size == d_in * r
         st = _Theta(_ptr(keep["W0"]), _ptr(keep["s"]), _ptr(keep["U"]), _ptr(keep["V"]),
-                    d_in, d_out, r)
+                    d_in, d_out, r, dt)
         return st, keep
 
     # -- operations -----------------------------------------------------------------
     def linear(self, th: dict, x) -> tuple[np.ndarray, np.ndarray]:
         """(y, bound), both float64 [T][d_out]."""
         st, keep = self._theta(th)
-        xb = _bits(x).reshape(-1, int(th["d_in"]))
+        xb = _elems(x, st.dtype).reshape(-1, int(th["d_in"]))
         T = xb.shape[0]
         y = np.empty((T, int(th["d_out"])), np.float64)
         b = np.empty_like(y)
@@ -121,7 +147,7 @@ class Oracle:
         sq, kq = self._theta(q)
         sk, kk = self._theta(k)
         sv, kv = self._theta(v)
-        xb = _bits(x).reshape(-1, int(q["d_in"]))
+        xb = _elems(x, sq.dtype).reshape(-1, int(q["d_in"]))
         T = xb.shape[0]
         width = int(q["d_out"]) + int(k["d_out"]) + int(v["d_out"])
         y = np.empty((T, width), np.float64)
@@ -132,15 +158,16 @@ class Oracle:
         return y, b
 
     def mlp(self, gate: dict, up: dict, down: dict, x):
-        """(y, bound, h_bits): y, bound float64 [T][d_model]; h_bits uint16 [T][d_ff]."""
+        """(y, bound, h): y, bound float64 [T][d_model]; h the rounded intermediate
+        [T][d_ff], uint16 bf16 patterns (bf16 thetas) or float32 values (fp32 ones)."""
         sg, kg = self._theta(gate)
         su, ku = self._theta(up)
         sd, kd = self._theta(down)
-        xb = _bits(x).reshape(-1, int(gate["d_in"]))
+        xb = _elems(x, sg.dtype).reshape(-1, int(gate["d_in"]))
         T = xb.shape[0]
         y = np.empty((T, int(down["d_out"])), np.float64)
         b = np.empty_like(y)
-        h = np.empty((T, int(gate["d_out"])), np.uint16)
+        h = np.empty((T, int(gate["d_out"])), np.float32 if sg.dtype == F32 else np.uint16)
         rc = self.lib.orc_mlp(ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), T,
                               _ptr(xb), _ptr(y), _ptr(b), _ptr(h))
         assert rc == 0

@@ -15,7 +15,10 @@ disagrees with something the pages or the mathematics fix:
   reconstruction paths and the precompute-outside path are math-identical);
 * closed forms and invariants: unit-vector inputs, rank-1 factors, linearity,
   the role of s, rank splitting, relative Frobenius error closed forms, GELU
-  identities and its sigmoid form evaluated in 50-digit decimal arithmetic.
+  identities and its sigmoid form evaluated in 50-digit decimal arithmetic;
+* for the fp32 variant: exact rational brute force on integers that bf16
+  cannot hold, numpy float64 products of full-precision binary32 data, and the
+  binary32 rounding of the MLP intermediate.
 
 The same pins run against deliberately broken copies of the oracle
 (test_oracle_mutants.py) to show that each plausible mistake fails one of them.
@@ -410,11 +413,83 @@ def pin_mlp_h_is_rounded_gelu_product(orc):
     assert np.max(np.abs(y - hd @ dense(down).T) / b) < 1e-13
 
 
+# -- the fp32 variant ------------------------------------------------------------------------
+
+def pin_f32_bruteforce_exact(orc):
+    """fp32 thetas with integers up to 2^11 (exact in binary32, not in bf16's 8-bit
+    significand): every output and W_eff entry equals exact rational arithmetic."""
+    for seed, (d_in, d_out, r, T) in enumerate([(5, 3, 1, 1), (9, 7, 2, 2), (16, 12, 4, 3)]):
+        gen = torch.Generator().manual_seed(300 + seed)
+        th = dict(W0=inputs.int_tensor(gen, (d_out, d_in), -2048, 2048, dtype=torch.float32),
+                  s=inputs.choice_tensor(gen, (d_out,), (0.5, 1.0, -3.0, 1.25)),
+                  U=inputs.int_tensor(gen, (d_out, r), -300, 300, dtype=torch.float32),
+                  V=inputs.int_tensor(gen, (d_in, r), -300, 300, dtype=torch.float32),
+                  d_in=d_in, d_out=d_out, r=r)
+        x = inputs.int_tensor(gen, (T, d_in), -1000, 1000, dtype=torch.float32)
+        y, b = orc.linear(th, x)
+        want = _exact_apply(_exact_weff(th), _f64(x))
+        for t_ in range(T):
+            for o in range(d_out):
+                assert Fraction(float(y[t_, o])) == want[t_][o], (seed, t_, o)
+        w, _ = orc.weff(th)
+        ew = _exact_weff(th)
+        assert all(Fraction(float(w[o, i])) == ew[o][i] for o in range(d_out) for i in range(d_in))
+
+
+def pin_f32_random_matmuls(orc):
+    """Random fp32 data (full 24-bit significands): the projection equals numpy's
+    float64 products of the same values, W_eff equals diag(s) W0 + U V^T, doubling x
+    doubles y exactly, and Q/K/V columns are the three projections."""
+    gen = torch.Generator().manual_seed(310)
+    d_in, d_out, r, T = 56, 33, 5, 4
+    th = inputs.theta(gen, d_in, d_out, r, dtype=torch.float32)
+    x = inputs.activations(gen, T, d_in, dtype=torch.float32)
+    y, b = orc.linear(th, x)
+    X, W0, U, V, s = _f64(x), _f64(th["W0"]), _f64(th["U"]), _f64(th["V"]), _s_vec(th)
+    assert np.max(np.abs(y - (s[None, :] * (X @ W0.T) + (X @ V) @ U.T)) / b) < 1e-13
+    y2, _ = orc.linear(th, x * 2)
+    assert np.array_equal(y2, 2 * y)
+    w, bw = orc.weff(th)
+    assert np.max(np.abs(w - (np.diag(s) @ W0 + U @ V.T)) / np.maximum(bw, 1e-300)) < 1e-15
+    k, v = inputs.theta(gen, d_in, 9, 3, dtype=torch.float32), inputs.theta(gen, d_in, 4, 2, dtype=torch.float32)
+    yq, _ = orc.qkv(th, k, v, x)
+    assert np.array_equal(yq, np.concatenate([y, orc.linear(k, x)[0], orc.linear(v, x)[0]], axis=1))
+
+
+def pin_f32_mlp_h(orc):
+    """fp32 MLP: h is the binary32 value nearest gelu(g) * u (gelu through the decimal
+    sigmoid form, g and u from numpy products), not a bf16 value, and y is the down
+    projection of that h."""
+    gen = torch.Generator().manual_seed(320)
+    d, ff, r, T = 24, 20, 4, 2
+    gate, up, down = (inputs.theta(gen, d, ff, r, dtype=torch.float32),
+                      inputs.theta(gen, d, ff, r, dtype=torch.float32),
+                      inputs.theta(gen, ff, d, r, dtype=torch.float32))
+    x = inputs.activations(gen, T, d, dtype=torch.float32)
+    y, b, h = orc.mlp(gate, up, down, x)
+    assert h.dtype == np.float32
+    X = _f64(x)
+
+    def dense(th):
+        return np.diag(_s_vec(th)) @ _f64(th["W0"]) + _f64(th["U"]) @ _f64(th["V"]).T
+    g, u = X @ dense(gate).T, X @ dense(up).T
+    beyond_bf16 = 0
+    for t_ in range(T):
+        for j in range(ff):
+            hv = float(_gelu_sigmoid_decimal(float(g[t_, j]))) * u[t_, j]
+            got = float(h[t_, j])
+            assert abs(got - hv) <= abs(hv) * 2.0 ** -24 * 1.0001 + 1e-45, (t_, j, got, hv)
+            beyond_bf16 += int(np.float32(got).view(np.uint32)) & 0xFFFF != 0
+    assert beyond_bf16 > T * ff // 2
+    assert np.max(np.abs(y - h.astype(np.float64) @ dense(down).T) / b) < 1e-13
+
+
 PINS = [pin_worked_example, pin_bf16_rne_table, pin_bf16_rne_matches_torch,
         pin_passthrough_integer_exact, pin_passthrough_random_matmul, pin_bruteforce_exact,
         pin_qkv_bruteforce, pin_unit_vectors, pin_rank1_closed_form, pin_linearity, pin_s_role,
         pin_rank_split, pin_weff_forms, pin_rel_frob_closed_forms, pin_gelu,
-        pin_mlp_exact_integer, pin_mlp_zero_gate, pin_mlp_h_is_rounded_gelu_product]
+        pin_mlp_exact_integer, pin_mlp_zero_gate, pin_mlp_h_is_rounded_gelu_product,
+        pin_f32_bruteforce_exact, pin_f32_random_matmuls, pin_f32_mlp_h]
 
 
 def report(lib_path: str) -> None:

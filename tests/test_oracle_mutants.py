@@ -15,18 +15,18 @@ from oracle import oracle as oracle_mod
 
 # (name, text to replace, replacement, which occurrence (0-based))
 MUTANTS = [
-    ("V transposed in vtx", "acc += bf16_value(th->V[i * r + k])", "acc += bf16_value(th->V[k * d_in + i])", 0),
-    ("U transposed", "bf16_value(th->U[o * r + k]) * vtx[k]", "bf16_value(th->U[k * d_out + o]) * vtx[k]", 0),
-    ("W0 transposed", "bf16_value(th->W0[o * d_in + i]) * bf16_value(xt[i])", "bf16_value(th->W0[i * d_out + o]) * bf16_value(xt[i])", 0),
-    ("x stride d_out", "const uint16_t *xt = x + t * d_in;", "const uint16_t *xt = x + t * d_out;", 0),
+    ("V transposed in vtx", "acc += elem(th->V, dt, i * r + k)", "acc += elem(th->V, dt, k * d_in + i)", 0),
+    ("U transposed", "elem(th->U, dt, o * r + k) * vtx[k]", "elem(th->U, dt, k * d_out + o) * vtx[k]", 0),
+    ("W0 transposed", "elem(th->W0, dt, o * d_in + i) * elem(x, dt, x0 + i)", "elem(th->W0, dt, i * d_out + o) * elem(x, dt, x0 + i)", 0),
+    ("x stride d_out", "const int64_t x0 = t * d_in;", "const int64_t x0 = t * d_out;", 0),
     ("s also scales delta", "y[t * d_out + o] = so * m + delta;", "y[t * d_out + o] = so * (m + delta);", 0),
     ("delta sign", "y[t * d_out + o] = so * m + delta;", "y[t * d_out + o] = so * m - delta;", 0),
     ("s dropped", "y[t * d_out + o] = so * m + delta;", "y[t * d_out + o] = m + delta;", 0),
     ("delta dropped", "y[t * d_out + o] = so * m + delta;", "y[t * d_out + o] = so * m;", 0),
-    ("last rank term dropped", "for (int64_t k = 0; k < r; ++k) {\n                double p = bf16_value(th->U[o * r + k]) * vtx[k];",
-     "for (int64_t k = 0; k < r - 1; ++k) {\n                double p = bf16_value(th->U[o * r + k]) * vtx[k];", 0),
-    ("last column dropped", "for (int64_t i = 0; i < d_in; ++i) {\n                double p = bf16_value(th->W0",
-     "for (int64_t i = 0; i < d_in - 1; ++i) {\n                double p = bf16_value(th->W0", 0),
+    ("last rank term dropped", "for (int64_t k = 0; k < r; ++k) {\n                double p = elem(th->U, dt, o * r + k) * vtx[k];",
+     "for (int64_t k = 0; k < r - 1; ++k) {\n                double p = elem(th->U, dt, o * r + k) * vtx[k];", 0),
+    ("last column dropped", "for (int64_t i = 0; i < d_in; ++i) {\n                double p = elem(th->W0",
+     "for (int64_t i = 0; i < d_in - 1; ++i) {\n                double p = elem(th->W0", 0),
     ("vtx over last input dropped", "for (int64_t i = 0; i < d_in; ++i)\n                acc +=",
      "for (int64_t i = 1; i < d_in; ++i)\n                acc +=", 0),
     ("s default 0", "double so = th->s ? (double)th->s[o] : 1.0;\n            y[", "double so = th->s ? (double)th->s[o] : 0.0;\n            y[", 0),
@@ -36,8 +36,8 @@ MUTANTS = [
     ("gelu sqrt(pi/2)", "sqrt(2.0 / M_PI)", "sqrt(M_PI / 2.0)", 0),
     ("gelu drops z", "return 0.5 * z * (1.0 + tanh(a));", "return 0.5 * (1.0 + tanh(a));", 0),
     ("gelu of product", "orc_gelu_tanh(g[j]) * u[j]", "orc_gelu_tanh(g[j] * u[j])", 0),
-    ("h not rounded to nearest", "hb[j] = orc_bf16_rne(orc_gelu_tanh(g[j]) * u[j]);",
-     "hb[j] = (uint16_t)(orc_bf16_rne(orc_gelu_tanh(g[j]) * u[j]) + 1);", 0),
+    ("h not rounded to nearest", "((uint16_t *)hr)[j] = orc_bf16_rne(h);",
+     "((uint16_t *)hr)[j] = (uint16_t)(orc_bf16_rne(h) + 1);", 0),
     ("up reads gate", "orc_linear(up, T, x, u, NULL)", "orc_linear(gate, T, x, u, NULL)", 0),
     ("rounding ties away from zero", "double n = nearbyint(ldexp(a, -q));", "double n = round(ldexp(a, -q));", 0),
     ("rounding truncates", "double n = nearbyint(ldexp(a, -q));", "double n = trunc(ldexp(a, -q));", 0),
@@ -45,10 +45,15 @@ MUTANTS = [
     ("subnormal quantum", "q = -133;", "q = -134;", 0),
     ("overflow saturates", "return sign | 0x7F80;             /* rounds past", "return sign | 0x7F7F;             /* rounds past", 0),
     ("qkv column offset", "col0 += n;", "col0 += q->d_out;", 0),
-    ("weff V transposed", "bf16_value(th->V[i * r + k]);\n                delta +=", "bf16_value(th->V[k * d_in + i]);\n                delta +=", 0),
-    ("weff unscaled", "double base = so * bf16_value(th->W0[o * d_in + i]);", "double base = bf16_value(th->W0[o * d_in + i]);", 0),
+    ("weff V transposed", "elem(th->V, dt, i * r + k);\n                delta +=", "elem(th->V, dt, k * d_in + i);\n                delta +=", 0),
+    ("weff unscaled", "double base = so * elem(th->W0, dt, o * d_in + i);", "double base = elem(th->W0, dt, o * d_in + i);", 0),
     ("rel frob squared", "return sqrt(num) / sqrt(den);", "return num / den;", 0),
     ("rel frob zero norm", "return num == 0.0 ? 0.0 : INFINITY;", "return 0.0;", 0),
+    ("f32 read as bf16", "return (double)((const float *)p)[j];",
+     "return bf16_value((uint16_t)(((const uint32_t *)p)[j] >> 16));", 0),
+    ("f32 h rounded to bf16", "((float *)hr)[j] = (float)h;", "((float *)hr)[j] = (float)bf16_value(orc_bf16_rne(h));", 0),
+    ("f32 h rounded down", "((float *)hr)[j] = (float)h;", "((float *)hr)[j] = (float)(h * (1.0 - 0x1p-24));", 0),
+    ("f32 x read with the theta's W0 type only", "elem(x, dt, x0 + i);\n            vtx[k]", "elem(x, ORC_BF16, x0 + i);\n            vtx[k]", 0),
 ]
 
 
