@@ -57,6 +57,7 @@ if REPO not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix cores
+MFMA_F32_PEAK_TFS = 157.3      # MI355X dense fp32 matrix cores
 METRIC = "tokens/s + achieved HBM GB/s (T=1) / MFMA TFLOP/s (T=2048) per rank"
 WORKLOADS = ("layer-decode", "single", "batched-decode", "prefill", "large", "copy")
 DEFAULT_STEPS = {"layer-decode": 2600, "single": 4000, "batched-decode": 200, "prefill": 260, "large": 40}
@@ -78,15 +79,22 @@ def parse_args():
                    help="write the dominant call's HBM traffic from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
                         "counter files (of a --dominant-only run and of --workload copy) and exit")
     p.add_argument("--traffic-calls", type=int, default=0, help="dominant calls in the counted run")
+    p.add_argument("--dtype", choices=("bf16", "f32"), default="bf16",
+                   help="element type of W0, U, V, x, y (f32: the fp32 variant of every operation)")
     return p.parse_args()
 
 
 # -- algorithmic work (counted once per call; what the method must move or compute) ----------
 
+def elem_bytes(th: dict) -> int:
+    """Bytes per element of a theta's W0, U, V (and of its call's x, y)."""
+    return th["W0"].element_size()
+
+
 def theta_bytes(th: dict) -> int:
     """W0 + s + U + V bytes of one theta."""
-    d_in, d_out, r = th["d_in"], th["d_out"], th["r"]
-    return 2 * d_out * d_in + (4 * d_out if th.get("s") is not None else 0) + 2 * r * (d_out + d_in)
+    d_in, d_out, r, e = th["d_in"], th["d_out"], th["r"], elem_bytes(th)
+    return e * d_out * d_in + (4 * d_out if th.get("s") is not None else 0) + e * r * (d_out + d_in)
 
 
 def theta_flops(th: dict, T: int) -> int:
@@ -96,7 +104,8 @@ def theta_flops(th: dict, T: int) -> int:
 
 
 def call_bytes(thetas, T: int, d_x: int, d_y: int) -> int:
-    return sum(theta_bytes(t) for t in thetas) + 2 * T * d_x + 2 * T * d_y
+    e = elem_bytes(thetas[0])
+    return sum(theta_bytes(t) for t in thetas) + e * T * d_x + e * T * d_y
 
 
 def layer_work(lay: dict, dims: dict, T: int):
@@ -121,7 +130,9 @@ def mlp_work(lay: dict, dims: dict, T: int):
 _COMMON_SOURCES = ("wl_abi.cpp", "wl_kernels.h", "wl_device.h")
 
 
-def _regime_sources(tokens: int) -> tuple:
+def _regime_sources(tokens: int, dtype: str = "bf16") -> tuple:
+    if dtype == "f32":
+        return ("k_f32.hip",)
     if tokens <= 8:
         return ("k_gemv.hip", "k_vtx.hip")
     if tokens <= 64:
@@ -129,11 +140,11 @@ def _regime_sources(tokens: int) -> tuple:
     return ("k_gemm.hip", "k_vtxmm.hip")
 
 
-def source_digest(tokens: int) -> str:
+def source_digest(tokens: int, dtype: str = "bf16") -> str:
     """Digest of the sources of the kernels that run at this token count, to tell
     whether stored counter data still applies."""
     h = hashlib.sha256()
-    for name in sorted(_COMMON_SOURCES + _regime_sources(tokens)):
+    for name in sorted(_COMMON_SOURCES + _regime_sources(tokens, dtype)):
         with open(os.path.join(REPO, "linear_02_amd", "csrc", name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -141,8 +152,10 @@ def source_digest(tokens: int) -> str:
 
 def traffic_key(args, workload: str) -> str:
     """Name of a workload's traffic record: one W0 shared by all layers (--shared-w0)
-    moves other bytes than one W0 per layer, so it has a record of its own."""
-    return workload + "-G1" if getattr(args, "shared_w0", False) else workload
+    moves other bytes than one W0 per layer, and the fp32 variant other bytes than
+    bf16, so each has a record of its own."""
+    key = workload + "-G1" if getattr(args, "shared_w0", False) else workload
+    return key + "-f32" if getattr(args, "dtype", "bf16") == "f32" else key
 
 
 def stored_traffic(workload: str, rank: int, tokens: int):
@@ -158,7 +171,7 @@ def stored_traffic(workload: str, rank: int, tokens: int):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("sources") != source_digest(tokens):
+    if kv.get("sources") != source_digest(tokens, "f32" if workload.endswith("-f32") else "bf16"):
         return None
     try:
         return float(kv["bytes_per_call"])
@@ -250,8 +263,9 @@ def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_
     dev = torch.device("cuda:0")
     gen = torch.Generator().manual_seed(seed)
     t_gen = time.perf_counter()
-    host_layers = inputs.layers(gen, dims, r, n_layers, G, w0_std=w0_std)
-    acts = inputs.layer_inputs(gen, dims, T)
+    dt = torch.float32 if args.dtype == "f32" else torch.bfloat16
+    host_layers = inputs.layers(gen, dims, r, n_layers, G, w0_std=w0_std, dtype=dt)
+    acts = inputs.layer_inputs(gen, dims, T, dtype=dt)
     layers = [{f: wl.theta_to(lay[f], dev) for f in inputs.FAMILIES} for lay in host_layers]
     # W0 blocks shared between layers stay shared on the device.
     if G < n_layers:
@@ -264,9 +278,9 @@ def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_
     t_gen = time.perf_counter() - t_gen
 
     d, width = dims["d_model"], dims["q"] + 2 * dims["kv"]
-    y_qkv = torch.empty(T, width, dtype=torch.bfloat16, device=dev)
-    y_o = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
-    y_mlp = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    y_qkv = torch.empty(T, width, dtype=dt, device=dev)
+    y_o = torch.empty(T, d, dtype=dt, device=dev)
+    y_mlp = torch.empty(T, d, dtype=dt, device=dev)
     l0 = layers[0]
     ws_bytes = max(wl.workspace_bytes(wl.OP_QKV, [l0["q"], l0["k"], l0["v"]], T),
                    wl.workspace_bytes(wl.OP_LINEAR, [l0["o"]], T),
@@ -338,9 +352,10 @@ def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_
                 "kernel": "wl_mlp_fused (all of its kernels, back to back)", "bytes_per_launch": mlp_b,
                 "us_per_launch": mlp_ms * 1e3}
     else:
+        peak = MFMA_F32_PEAK_TFS if args.dtype == "f32" else MFMA_BF16_PEAK_TFS
         achieved = mlp_f / (mlp_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_BF16_PEAK_TFS, "traffic": stored_traffic(traffic_key(args, workload), r, T),
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": stored_traffic(traffic_key(args, workload), r, T),
                 "kernel": "wl_mlp_fused (all of its kernels, back to back)", "flops_per_launch": mlp_f,
                 "us_per_launch": mlp_ms * 1e3}
 
@@ -364,7 +379,8 @@ def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_
         "value": K * tokens_per_step / (ms_total * 1e-3),
         "unit": "tokens/s",
         "steps": K, "warmup": W, "ms_per_step": ms_per_step,
-        "config": {"workload": workload_name(workload, dims, r, T, n_layers, G),
+        "config": {"workload": workload_name(workload, dims, r, T, n_layers, G)
+                   + (", fp32 weights and activations" if args.dtype == "f32" else ""),
                    "T": T, "rank": r, "layers": n_layers, "G": G, "d_model": d, "q": dims["q"],
                    "kv": dims["kv"], "d_ff": dims["ff"], "parallelism": "single-gpu"},
         "roofline": roof,
@@ -395,9 +411,10 @@ def materialize_and_dense(torch, wl, layers, xa, dims, T, ws):
     dense = {f: dict(W0=weff[f], s=None, U=None, V=None, d_in=lay[f]["d_in"], d_out=lay[f]["d_out"], r=0)
              for f in lay}
     d, width = dims["d_model"], dims["q"] + 2 * dims["kv"]
-    y_qkv = torch.empty(T, width, dtype=torch.bfloat16, device=dev)
-    y_o = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
-    y_mlp = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    dt = lay["q"]["W0"].dtype
+    y_qkv = torch.empty(T, width, dtype=dt, device=dev)
+    y_o = torch.empty(T, d, dtype=dt, device=dev)
+    y_mlp = torch.empty(T, d, dtype=dt, device=dev)
 
     def dense_layer():
         wl.wl_qkv_fused(dense["q"], dense["k"], dense["v"], xa["x_attn"], y=y_qkv, ws=ws)
@@ -408,8 +425,9 @@ def materialize_and_dense(torch, wl, layers, xa, dims, T, ws):
     gd = GraphSet(torch, [dense_layer])
     m_ms = time_calls(torch, gm, 20)
     d_ms = time_calls(torch, gd, 20)
-    w_bytes = sum(2 * 2 * lay[f]["d_out"] * lay[f]["d_in"] + 4 * lay[f]["d_out"]
-                  + 2 * lay[f]["r"] * (lay[f]["d_in"] + lay[f]["d_out"]) for f in lay)
+    e = lay["q"]["W0"].element_size()
+    w_bytes = sum(2 * e * lay[f]["d_out"] * lay[f]["d_in"] + 4 * lay[f]["d_out"]
+                  + e * lay[f]["r"] * (lay[f]["d_in"] + lay[f]["d_out"]) for f in lay)
     return {"materialize_weff": {"us_per_layer": m_ms * 1e3, "hbm_gbs": w_bytes / (m_ms * 1e-3) / 1e9,
                                  "bytes_per_layer": w_bytes},
             "dense_on_weff": {"us_per_layer": d_ms * 1e3}}
@@ -532,7 +550,7 @@ def write_traffic(args) -> int:
                 f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {rel(cfetch_csv)} -o p -- python3 bench.py --workload copy --steps 4\n"
                 f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {rel(cwrite_csv)} -o p -- python3 bench.py --workload copy --steps 4\n"
                 f"#   {run} --traffic-calls {calls} --traffic-from {' '.join(os.path.relpath(os.path.abspath(c), REPO) for c in args.traffic_from)}\n")
-        f.write(f"sources = {source_digest(T)}\n")
+        f.write(f"sources = {source_digest(T, args.dtype)}\n")
         f.write(f"calls = {calls}\n")
         f.write(f"fetch_kib_total = {f_kib:.1f}\nwrite_kib_total = {w_kib:.1f}\n")
         f.write(f"copy_fetch_scale = {kf:.4f}\ncopy_write_scale = {kw:.4f}\n")
@@ -564,6 +582,9 @@ def main() -> int:
         print(json.dumps(run_copy(args, torch)))
         return 0
     orc = oracle_mod.default()
+    if wk == "single" and args.dtype != "bf16":
+        print("--workload single runs bf16 only", file=sys.stderr)
+        return 2
     if wk == "single":
         res = run_single(args, torch, np, wl, inputs, orc)
     elif wk == "layer-decode":
@@ -587,7 +608,7 @@ def main() -> int:
         return 0
     out = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,
            "steps": res.pop("steps"), "warmup": res.pop("warmup"), "ms_per_step": res.pop("ms_per_step"),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
            "data": "synthetic"}
     out.update(res)
     print(json.dumps(out))

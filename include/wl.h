@@ -17,12 +17,18 @@
  *            no per-call state (its only global state is the regime switch
  *            below).
  * Layout.    All tensors are row-major and contiguous:
- *              W0 bf16 [d_out][d_in]   s fp32 [d_out]
- *              U  bf16 [d_out][r]      V bf16 [d_in][r]
- *              x  bf16 [T][d_in]       y bf16 [T][d_out]
+ *              W0 [d_out][d_in]   s fp32 [d_out]
+ *              U  [d_out][r]      V [d_in][r]
+ *              x  [T][d_in]       y [T][d_out]
  *            (the index roles of the per-element expansion; the GEMM form on
  *            the same page, "The GEMM path", multiplies x by W0 transposed, by
  *            V, and the result by U transposed).
+ * Dtypes.    A theta's `dtype` sets the element type of its W0, U, V and of
+ *            the call's x, y (and of the MLP's h and of W_eff): WL_DTYPE_BF16
+ *            or WL_DTYPE_F32 (the custom op "also supports float32", "In-kernel
+ *            reconstruction", the custom-op path). s is fp32 in both. The
+ *            thetas of one fused call share one dtype. A zero-filled theta is
+ *            bf16.
  * Alignment. W0, U, V, x, y and W_eff must be 16-byte aligned, s 4-byte
  *            aligned, the workspace 256-byte aligned. d_in must be a multiple
  *            of 8 (rows are read in 16-byte pieces).
@@ -30,11 +36,12 @@
  *            returns WL_OK, and x, y may then be NULL). Sizes are int32 and
  *            every tensor must hold fewer than 2^31 elements.
  * Numerics.  Products accumulate in fp32; the epilogue s[o]*m + U[o,:].vtx is
- *            fp32; y is rounded once to bf16, round-to-nearest-even ("In-kernel
+ *            fp32; a bf16 y is rounded once, round-to-nearest-even ("In-kernel
  *            reconstruction", "The custom-op path": every implementation
- *            accumulates in float32 and casts back to the output dtype). The
- *            matrix-core regime feeds vtx = V^T x to the matrix cores as a bf16
- *            head plus a bf16 remainder. Results are deterministic from run to
+ *            accumulates in float32 and casts back to the output dtype); an
+ *            fp32 y is the fp32 result. The bf16 matrix-core regime feeds
+ *            vtx = V^T x to the matrix cores as a bf16 head plus a bf16
+ *            remainder. Results are deterministic from run to
  *            run (no floating-point atomics) but not bit-exact against other
  *            summation orders ("Serve and generate with weightless", "Set the
  *            fast path on NVIDIA": parity is logit parity, not bit equality).
@@ -51,7 +58,7 @@
  *              WL_ERR_INVALID_ARG  null or misaligned pointer, bad size or
  *                                  shape mismatch, output overlapping an input
  *                                  or the workspace
- *              WL_ERR_UNSUPPORTED  r > 64
+ *              WL_ERR_UNSUPPORTED  r > 64, or a dtype other than the two
  *              WL_ERR_WORKSPACE    ws_bytes below the required size
  *              WL_ERR_HIP          a kernel launch failed
  *            No call aborts, throws or prints (set the environment variable
@@ -71,7 +78,7 @@
 extern "C" {
 #endif
 
-#define WL_ABI_VERSION 2
+#define WL_ABI_VERSION 3
 
 typedef enum {
     WL_OK = 0,
@@ -85,12 +92,16 @@ typedef enum {
  * introduction: a shared block W0 per band of layers, a per-row scale s and a
  * low-rank delta U, V of rank r). Several thetas may point at the same W0
  * (band sharing). The library only reads through these pointers. */
+/* Element types of W0, U, V, x, y. */
+enum { WL_DTYPE_BF16 = 0, WL_DTYPE_F32 = 1 };
+
 typedef struct {
-    const void  *W0;   /* bf16 [d_out][d_in]                                   */
+    const void  *W0;   /* dtype [d_out][d_in]                                  */
     const float *s;    /* fp32 [d_out]; NULL means every s[o] is 1              */
-    const void  *U;    /* bf16 [d_out][r]; ignored (may be NULL) when r == 0    */
-    const void  *V;    /* bf16 [d_in][r];  ignored (may be NULL) when r == 0    */
+    const void  *U;    /* dtype [d_out][r]; ignored (may be NULL) when r == 0   */
+    const void  *V;    /* dtype [d_in][r];  ignored (may be NULL) when r == 0   */
     int32_t d_in, d_out, r;
+    int32_t dtype;     /* WL_DTYPE_BF16 (0) or WL_DTYPE_F32 (1)                 */
 } wl_theta;
 
 /* Operation codes for wl_workspace_bytes. */
@@ -107,8 +118,8 @@ size_t wl_workspace_bytes(int32_t op, const wl_theta *const *th, int32_t n_th, i
 /* The reconstruct-and-project linear ("In-kernel reconstruction",
  * introduction: reconstruction formula and per-element expansion).
  *   th    one theta bundle
- *   x     bf16 [T][th->d_in]
- *   y     bf16 [T][th->d_out] (written; must not overlap any input)
+ *   x     dtype [T][th->d_in]
+ *   y     dtype [T][th->d_out] (written; must not overlap any input)
  *   T     tokens (rows of x)
  *   ws    workspace, ws_bytes >= wl_workspace_bytes(WL_OP_LINEAR, &th, 1, T)
  * With th->r == 0 and th->s == NULL this is the dense product y = x W0^T: the
@@ -120,9 +131,9 @@ wl_status wl_linear(const wl_theta *th, const void *x, void *y, int32_t T,
 /* Q/K/V fusion ("In-kernel reconstruction", "Q/K/V fusion"): the three
  * attention projections that read the same x, computed in one pass over the
  * concatenated W0 rows, each child with its own V^T x (a block-diagonal U).
- *   q, k, v   thetas with equal d_in; ranks, scales and d_out may differ
- *   x         bf16 [T][d_in]
- *   y_qkv     bf16 [T][q->d_out + k->d_out + v->d_out], columns Q | K | V
+ *   q, k, v   thetas with equal d_in and dtype; ranks, scales and d_out may differ
+ *   x         dtype [T][d_in]
+ *   y_qkv     dtype [T][q->d_out + k->d_out + v->d_out], columns Q | K | V
  *   ws        ws_bytes >= wl_workspace_bytes(WL_OP_QKV, {q, k, v}, 3, T)
  * Each child's columns equal wl_linear of that child to within rounding. */
 wl_status wl_qkv_fused(const wl_theta *q, const wl_theta *k, const wl_theta *v,
@@ -132,11 +143,12 @@ wl_status wl_qkv_fused(const wl_theta *q, const wl_theta *k, const wl_theta *v,
 /* Fused MLP ("In-kernel reconstruction", "The custom-op path": the fused MLP
  * op runs gate, up, the activation and down as one operation):
  *   g = linear(gate, x), u = linear(up, x)       (fp32, not rounded)
- *   h = bf16_rne(gelu_tanh(g) * u)               (rounded once to bf16)
+ *   h = round(gelu_tanh(g) * u)                  (rounded once to the dtype:
+ *                                                 bf16 RNE, or the fp32 value)
  *   y = linear(down, h)
  * with gelu_tanh(z) = 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
  * Shapes: gate.d_in == up.d_in (= d_model), gate.d_out == up.d_out ==
- * down.d_in (= d_ff); x bf16 [T][d_model], y bf16 [T][down.d_out].
+ * down.d_in (= d_ff), one dtype; x dtype [T][d_model], y dtype [T][down.d_out].
  * h lives in the workspace:
  *   ws_bytes >= wl_workspace_bytes(WL_OP_MLP, {gate, up, down}, 3, T). */
 wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta *down,
@@ -145,8 +157,9 @@ wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta 
 
 /* The effective weight of the precompute-outside path ("Serve and generate
  * with weightless", "Set the fast path on NVIDIA"):
- *   W_eff[o,i] = bf16_rne( s[o] * W0[o,i] + sum_k U[o,k] * V[i,k] )
- * W_eff: bf16 [th->d_out][th->d_in], written; must not overlap any input.
+ *   W_eff[o,i] = round( s[o] * W0[o,i] + sum_k U[o,k] * V[i,k] )
+ * W_eff: th->dtype [th->d_out][th->d_in] (bf16: rounded once, RNE; fp32: the
+ * fp32 result), written; must not overlap any input.
  * Needs no workspace. */
 wl_status wl_materialize_weff(const wl_theta *th, void *W_eff, void *hip_stream);
 
@@ -154,10 +167,11 @@ wl_status wl_materialize_weff(const wl_theta *th, void *W_eff, void *hip_stream)
  * ("What weightless inference costs", "Compression": the ratio of the theta
  * bundle, W0 + s + U + V across every layer and family, to the original
  * projection weights). For th[0 .. n_th):
- *   *bundle_bytes = 2 d_out d_in once per distinct W0 pointer
- *                   + per theta: 4 d_out (when s is not NULL) + 2 r (d_out + d_in)
- *   *dense_bytes  = per theta: 2 d_out d_in (the bf16 weight it stands for)
- * Thetas that share a W0 pointer must share its shape (else
+ *   *bundle_bytes = e d_out d_in once per distinct W0 pointer
+ *                   + per theta: 4 d_out (when s is not NULL) + e r (d_out + d_in)
+ *   *dense_bytes  = per theta: e d_out d_in (the weight it stands for)
+ * with e = 2 for bf16 thetas and 4 for fp32 ones.
+ * Thetas that share a W0 pointer must share its shape and dtype (else
  * WL_ERR_INVALID_ARG). Host only: reads the structs, never the tensors. */
 wl_status wl_bundle_size(const wl_theta *const *th, int32_t n_th,
                          size_t *bundle_bytes, size_t *dense_bytes);

@@ -57,6 +57,8 @@ const int64_t kMaxElems = (int64_t)1 << 31;
 
 wl_status check_theta(const wl_theta *th, const char *name) {
     if (!th) return fail(WL_ERR_INVALID_ARG, "%s: theta is NULL", name);
+    if (th->dtype != WL_DTYPE_BF16 && th->dtype != WL_DTYPE_F32)
+        return fail(WL_ERR_UNSUPPORTED, "%s: dtype=%d is neither WL_DTYPE_BF16 nor WL_DTYPE_F32", name, th->dtype);
     if (th->d_in < 1 || th->d_out < 1)
         return fail(WL_ERR_INVALID_ARG, "%s: d_in=%d d_out=%d must be >= 1", name, th->d_in, th->d_out);
     if (th->d_in % 8)
@@ -77,11 +79,23 @@ wl_status check_theta(const wl_theta *th, const char *name) {
     return WL_OK;
 }
 
+// Bytes per element of W0, U, V and of the call's x, y (and h, W_eff).
+size_t elem_bytes(const wl_theta *th) { return th->dtype == WL_DTYPE_F32 ? 4 : 2; }
+
 void theta_ranges(const wl_theta *th, Range *out /* 4 */) {
-    out[0] = {th->W0, (size_t)th->d_out * th->d_in * 2};
+    const size_t es = elem_bytes(th);
+    out[0] = {th->W0, (size_t)th->d_out * th->d_in * es};
     out[1] = {th->s, th->s ? (size_t)th->d_out * 4 : 0};
-    out[2] = {th->r > 0 ? th->U : nullptr, (size_t)th->d_out * th->r * 2};
-    out[3] = {th->r > 0 ? th->V : nullptr, (size_t)th->d_in * th->r * 2};
+    out[2] = {th->r > 0 ? th->U : nullptr, (size_t)th->d_out * th->r * es};
+    out[3] = {th->r > 0 ? th->V : nullptr, (size_t)th->d_in * th->r * es};
+}
+
+// The thetas of one fused call must share their element type.
+wl_status check_same_dtype(const wl_theta *const *ths, int n, const char *op) {
+    for (int c = 1; c < n; ++c)
+        if (ths[c]->dtype != ths[0]->dtype)
+            return fail(WL_ERR_INVALID_ARG, "%s: the thetas' dtypes differ (%d and %d)", op, ths[0]->dtype, ths[c]->dtype);
+    return WL_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -132,6 +146,7 @@ struct Layout {
     size_t sk_part = 0, sk_vpart = 0;
     size_t mm_vtx = 0;
     size_t mm_part = 0;
+    size_t f32_part = 0, f32_vtx = 0;   // fp32 variant only
     size_t h = 0;
     size_t total = 0;
 };
@@ -161,7 +176,42 @@ int proj_shapes(int op, const wl_theta *const *th, ProjShape *out) {
     return 2;
 }
 
+// fp32 variant: V^T x slice partials [n_slices][T][r_c] and complete V^T x
+// [T][r_c] per child (the largest of the call's projections), MLP h fp32 [T][d_ff].
+Layout layout_f32(int op, const wl_theta *const *th, int T) {
+    Layout L;
+    size_t off = kReservedBytes;
+    ProjShape ps[2];
+    const int n = proj_shapes(op, th, ps);
+    size_t part = 0, vtx = 0;
+    int first = 0;
+    for (int j = 0; j < n; ++j) {
+        const int n_th = ps[j].P == 2 ? 2 : ps[j].n_ch;
+        size_t a = 0, b = 0;
+        for (int c = 0; c < n_th; ++c) {
+            const int r = th[first + c]->r;
+            if (r == 0) continue;
+            a += round_up((size_t)wl::f32_vtx_slices(ps[j].d_in) * T * r * 4, kAlign);
+            b += round_up((size_t)T * r * 4, kAlign);
+        }
+        part = a > part ? a : part;
+        vtx = b > vtx ? b : vtx;
+        first += n_th;
+    }
+    L.f32_part = off;
+    off = round_up(off + part, kAlign);
+    L.f32_vtx = off;
+    off = round_up(off + vtx, kAlign);
+    if (op == WL_OP_MLP) {
+        L.h = off;
+        off = round_up(off + (size_t)T * th[0]->d_out * 4, kAlign);
+    }
+    L.total = off;
+    return L;
+}
+
 Layout layout(int op, const wl_theta *const *th, int T) {
+    if (th[0]->dtype == WL_DTYPE_F32) return layout_f32(op, th, T);
     Layout L;
     size_t off = kReservedBytes;
     L.gemv_partial = off;
@@ -355,6 +405,62 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
     return WL_OK;
 }
 
+// One fp32 projection over shared x (children side by side in y, or the
+// gate/up pair into h): V^T x slices and their ordered sum, then the GEMV
+// (a few tokens) or the matrix-core GEMM.
+wl_status run_proj_f32(const wl_theta *const *ths, int n_ch, bool pair, int d_in, int T, const void *x, void *y,
+                       int ldy, char *ws, const Layout &L, hipStream_t stream) {
+    wl::F32Proj g{};
+    wl::F32Vtx vj{};
+    vj.x = static_cast<const float *>(x);
+    vj.d_in = d_in;
+    vj.T = T;
+    vj.slice_len = wl::kF32VtxSlice;
+    vj.n_slices = wl::f32_vtx_slices(d_in);
+    size_t poff = L.f32_part, voff = L.f32_vtx;
+    int col0 = 0;
+    for (int c = 0; c < n_ch; ++c) {
+        const wl_theta *t = ths[c];
+        wl::F32Child &C = g.ch[c];
+        C.W0 = static_cast<const float *>(t->W0);
+        C.s = t->s;
+        C.U = static_cast<const float *>(t->U);
+        C.vtx = nullptr;
+        C.r = t->r;
+        C.d_out = t->d_out;
+        C.col0 = pair ? 0 : col0;
+        if (!pair) col0 += t->d_out;
+        if (t->r == 0) continue;
+        float *part = reinterpret_cast<float *>(ws + poff);
+        poff += round_up((size_t)vj.n_slices * T * t->r * 4, kAlign);
+        float *vtx = reinterpret_cast<float *>(ws + voff);
+        voff += round_up((size_t)T * t->r * 4, kAlign);
+        C.vtx = vtx;
+        vj.V[vj.n_ch] = static_cast<const float *>(t->V);
+        vj.part[vj.n_ch] = part;
+        vj.vtx[vj.n_ch] = vtx;
+        vj.r[vj.n_ch] = t->r;
+        ++vj.n_ch;
+    }
+    hipError_t e = wl::launch_f32_vtx(vj, stream);
+    if (e != hipSuccess) return fail(WL_ERR_HIP, "fp32 V^T x launch failed: %s", hipGetErrorString(e));
+    g.n_ch = n_ch;
+    g.pair = pair;
+    g.d_in = d_in;
+    g.T = T;
+    g.ldy = ldy;
+    g.x = static_cast<const float *>(x);
+    g.y = static_cast<float *>(y);
+    const int regime = g_regime.load(std::memory_order_relaxed);
+    const bool gemv = T <= wl::kF32GemvMaxTok && regime != 2 && regime != 4;
+    if (getenv("WL_LOG"))
+        fprintf(stderr, "wl: fp32 proj n_ch=%d pair=%d d_in=%d T=%d -> %s\n", n_ch, (int)pair, d_in, T,
+                gemv ? "gemv" : "mfma");
+    e = gemv ? wl::launch_f32_gemv(g, stream) : wl::launch_f32_gemm(g, stream);
+    if (e != hipSuccess) return fail(WL_ERR_HIP, "fp32 projection launch failed: %s", hipGetErrorString(e));
+    return WL_OK;
+}
+
 wl_status check_io(const void *x, const void *y, int T, int d_in, int ldy) {
     if (T < 0) return fail(WL_ERR_INVALID_ARG, "T=%d is negative", T);
     if (T == 0) return WL_OK;
@@ -427,14 +533,19 @@ wl_status wl_linear(const wl_theta *th, const void *x, void *y, int32_t T, void 
     const wl_theta *ths[1] = {th};
     const Layout L = layout(WL_OP_LINEAR, ths, T);
     if ((st = check_ws(L.total, ws, ws_bytes)) != WL_OK) return st;
+    const size_t es = elem_bytes(th);
     Range in[6];
     theta_ranges(th, in);
-    in[4] = {x, (size_t)T * th->d_in * 2};
+    in[4] = {x, (size_t)T * th->d_in * es};
     in[5] = {ws, ws_bytes};
-    if ((st = check_overlap({y, (size_t)T * th->d_out * 2}, in, 6)) != WL_OK) return st;
+    if ((st = check_overlap({y, (size_t)T * th->d_out * es}, in, 6)) != WL_OK) return st;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     char *w = static_cast<char *>(ws);
+    if (th->dtype == WL_DTYPE_F32) {
+        if ((st = run_proj_f32(ths, 1, false, th->d_in, T, x, y, th->d_out, w, L, stream)) != WL_OK) return st;
+        return ok();
+    }
     const wl::Child ch = make_child(th, 0);
     if ((st = run_proj(&ch, 1, false, th->d_in, T, x, y, th->d_out, w, L, stream)) != WL_OK) return st;
     return ok();
@@ -447,6 +558,7 @@ wl_status wl_qkv_fused(const wl_theta *q, const wl_theta *k, const wl_theta *v, 
     wl_status st;
     for (int c = 0; c < 3; ++c)
         if ((st = check_theta(ths[c], names[c])) != WL_OK) return st;
+    if ((st = check_same_dtype(ths, 3, "qkv")) != WL_OK) return st;
     if (k->d_in != q->d_in || v->d_in != q->d_in)
         return fail(WL_ERR_INVALID_ARG, "q, k, v must share d_in (%d, %d, %d)", q->d_in, k->d_in, v->d_in);
     const int64_t width = (int64_t)q->d_out + k->d_out + v->d_out;
@@ -455,14 +567,19 @@ wl_status wl_qkv_fused(const wl_theta *q, const wl_theta *k, const wl_theta *v, 
     if (T == 0) return ok();
     const Layout L = layout(WL_OP_QKV, ths, T);
     if ((st = check_ws(L.total, ws, ws_bytes)) != WL_OK) return st;
+    const size_t es = elem_bytes(q);
     Range in[14];
     for (int c = 0; c < 3; ++c) theta_ranges(ths[c], in + 4 * c);
-    in[12] = {x, (size_t)T * q->d_in * 2};
+    in[12] = {x, (size_t)T * q->d_in * es};
     in[13] = {ws, ws_bytes};
-    if ((st = check_overlap({y_qkv, (size_t)T * width * 2}, in, 14)) != WL_OK) return st;
+    if ((st = check_overlap({y_qkv, (size_t)T * width * es}, in, 14)) != WL_OK) return st;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     char *w = static_cast<char *>(ws);
+    if (q->dtype == WL_DTYPE_F32) {
+        if ((st = run_proj_f32(ths, 3, false, q->d_in, T, x, y_qkv, (int)width, w, L, stream)) != WL_OK) return st;
+        return ok();
+    }
     wl::Child ch[3];
     int col0 = 0;
     for (int c = 0; c < 3; ++c) {
@@ -480,6 +597,7 @@ wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta 
     wl_status st;
     for (int c = 0; c < 3; ++c)
         if ((st = check_theta(ths[c], names[c])) != WL_OK) return st;
+    if ((st = check_same_dtype(ths, 3, "mlp")) != WL_OK) return st;
     if (up->d_in != gate->d_in || up->d_out != gate->d_out || down->d_in != gate->d_out)
         return fail(WL_ERR_INVALID_ARG,
                     "MLP shapes disagree: gate %dx%d, up %dx%d, down %dx%d (need gate == up, down.d_in == d_ff)",
@@ -489,16 +607,23 @@ wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta 
     if (T == 0) return ok();
     const Layout L = layout(WL_OP_MLP, ths, T);
     if ((st = check_ws(L.total, ws, ws_bytes)) != WL_OK) return st;
+    const size_t es = elem_bytes(gate);
     Range in[14];
     for (int c = 0; c < 3; ++c) theta_ranges(ths[c], in + 4 * c);
-    in[12] = {x, (size_t)T * gate->d_in * 2};
+    in[12] = {x, (size_t)T * gate->d_in * es};
     in[13] = {ws, ws_bytes};
-    if ((st = check_overlap({y, (size_t)T * down->d_out * 2}, in, 14)) != WL_OK) return st;
+    if ((st = check_overlap({y, (size_t)T * down->d_out * es}, in, 14)) != WL_OK) return st;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     char *w = static_cast<char *>(ws);
     void *h = w + L.h;
     const int d_ff = gate->d_out;
+    if (gate->dtype == WL_DTYPE_F32) {
+        // gate/up -> h = gelu_tanh(g) * u (fp32), then down over h
+        if ((st = run_proj_f32(ths, 2, true, gate->d_in, T, x, h, d_ff, w, L, stream)) != WL_OK) return st;
+        if ((st = run_proj_f32(ths + 2, 1, false, d_ff, T, h, y, down->d_out, w, L, stream)) != WL_OK) return st;
+        return ok();
+    }
     // gate/up -> h = bf16(gelu_tanh(g) * u), then down over h
     const wl::Child gu[2] = {make_child(gate, 0), make_child(up, 0)};
     if ((st = run_proj(gu, 2, true, gate->d_in, T, x, h, d_ff, w, L, stream)) != WL_OK) return st;
@@ -514,7 +639,21 @@ wl_status wl_materialize_weff(const wl_theta *th, void *W_eff, void *hip_stream)
     if (!aligned(W_eff, 16)) return fail(WL_ERR_INVALID_ARG, "W_eff is not 16-byte aligned");
     Range in[4];
     theta_ranges(th, in);
-    if ((st = check_overlap({W_eff, (size_t)th->d_out * th->d_in * 2}, in, 4)) != WL_OK) return st;
+    if ((st = check_overlap({W_eff, (size_t)th->d_out * th->d_in * elem_bytes(th)}, in, 4)) != WL_OK) return st;
+    if (th->dtype == WL_DTYPE_F32) {
+        wl::WeffF32 w{};
+        w.W0 = static_cast<const float *>(th->W0);
+        w.s = th->s;
+        w.U = static_cast<const float *>(th->U);
+        w.V = static_cast<const float *>(th->V);
+        w.W_eff = static_cast<float *>(W_eff);
+        w.d_in = th->d_in;
+        w.d_out = th->d_out;
+        w.r = th->r;
+        const hipError_t e = wl::launch_weff_f32(w, static_cast<hipStream_t>(hip_stream));
+        if (e != hipSuccess) return fail(WL_ERR_HIP, "materialize launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
     wl::Weff w{};
     w.W0 = static_cast<const uint16_t *>(th->W0);
     w.s = th->s;
@@ -542,14 +681,15 @@ wl_status wl_bundle_size(const wl_theta *const *th, int32_t n_th, size_t *bundle
         bool seen = false;
         for (int32_t i = 0; i < j; ++i)
             if (th[i]->W0 == t->W0) {
-                if (th[i]->d_in != t->d_in || th[i]->d_out != t->d_out)
-                    return fail(WL_ERR_INVALID_ARG, "thetas %d and %d share W0 but not its shape", i, j);
+                if (th[i]->d_in != t->d_in || th[i]->d_out != t->d_out || th[i]->dtype != t->dtype)
+                    return fail(WL_ERR_INVALID_ARG, "thetas %d and %d share W0 but not its shape or dtype", i, j);
                 seen = true;
                 break;
             }
-        const size_t w0 = (size_t)2 * t->d_out * t->d_in;
+        const size_t es = elem_bytes(t);
+        const size_t w0 = es * t->d_out * t->d_in;
         if (!seen) bundle += w0;
-        bundle += (t->s ? (size_t)4 * t->d_out : 0) + (size_t)2 * t->r * ((size_t)t->d_out + t->d_in);
+        bundle += (t->s ? (size_t)4 * t->d_out : 0) + es * t->r * ((size_t)t->d_out + t->d_in);
         dense += w0;
     }
     *bundle_bytes = bundle;

@@ -171,6 +171,46 @@ GemmSplit gemm_split_plan(int T, int d_in, int rows, int n_ch, int pair);
 hipError_t launch_gemm(const Gemm &g, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
+// The fp32 variant (W0, U, V, x, y in binary32; s fp32).
+struct F32Child {
+    const float *W0;      // [d_out][d_in]
+    const float *s;       // [d_out], or null: every s[o] is 1
+    const float *U;       // [d_out][r]  (r > 0)
+    const float *vtx;     // [T][r]: V^T x, complete (r > 0)
+    int r, d_out, col0;
+};
+// One projection over shared x: children side by side in y (ldy = total width),
+// or the gate/up pair (pair = 1, y = h = gelu_tanh(gate) * up).
+struct F32Proj {
+    F32Child ch[kMaxChildren];
+    int n_ch, pair, d_in, T, ldy;
+    const float *x;       // [T][d_in]
+    float *y;             // [T][ldy]
+};
+constexpr int kF32GemvMaxTok = 8;   // T above this runs on the matrix cores
+hipError_t launch_f32_gemv(const F32Proj &g, hipStream_t stream);
+hipError_t launch_f32_gemm(const F32Proj &g, hipStream_t stream);
+// V^T x of up to three children: slice partials part[c] ([n_slices][T][r_c])
+// then vtx[c] ([T][r_c]) with the slices added in order (two launches).
+constexpr int kF32VtxSlice = 256;   // inputs per slice
+struct F32Vtx {
+    const float *x;                 // [T][d_in]
+    const float *V[kMaxChildren];   // [d_in][r_c]
+    float *part[kMaxChildren];
+    float *vtx[kMaxChildren];
+    int r[kMaxChildren];            // 1 <= r_c <= kMaxRank
+    int n_ch, d_in, T, n_slices, slice_len;
+};
+int f32_vtx_slices(int d_in);
+hipError_t launch_f32_vtx(const F32Vtx &job, hipStream_t stream);
+struct WeffF32 {
+    const float *W0, *s, *U, *V;
+    float *W_eff;
+    int d_in, d_out, r;
+};
+hipError_t launch_weff_f32(const WeffF32 &w, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
 // Effective weight: W_eff[o][i] = bf16( s[o] * W0[o][i] + sum_k U[o][k] V[i][k] ).
 struct Weff {
     const uint16_t *W0;

@@ -103,7 +103,7 @@ def layer_inputs(gen: torch.Generator, dims: dict, T: int, dtype: torch.dtype = 
 
 
 def layers(gen: torch.Generator, dims: dict, r: int, n_layers: int, G: int, *,
-           w0_std: float = 0.02) -> list:
+           w0_std: float = 0.02, dtype: torch.dtype = torch.bfloat16) -> list:
     """``n_layers`` layers with ``G`` distinct W0 blocks per family: layer l uses
     block l // ceil(n_layers / G) (bands of consecutive layers). G == n_layers is
     the passthrough point (own W0 per layer); G == 1 shares one W0 everywhere."""
@@ -112,7 +112,7 @@ def layers(gen: torch.Generator, dims: dict, r: int, n_layers: int, G: int, *,
     out, bands = [], {}
     for l in range(n_layers):
         b = l // band
-        lay = layer(gen, dims, r, w0_std=w0_std, shared_W0=bands.get(b))
+        lay = layer(gen, dims, r, w0_std=w0_std, shared_W0=bands.get(b), dtype=dtype)
         bands.setdefault(b, {f: lay[f]["W0"] for f in FAMILIES})
         out.append(lay)
     return out

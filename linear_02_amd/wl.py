@@ -6,10 +6,11 @@ library, and returns the output tensor. All arithmetic runs in the library's
 HIP kernels; there is no fallback of any kind. If libwl.so is missing the
 import fails loudly (build it with ``python -m linear_02_amd.build``).
 
-A theta is a dict with device tensors ``W0`` (bf16 [d_out][d_in]), ``s`` (fp32
-[d_out] or None), ``U`` (bf16 [d_out][r]), ``V`` (bf16 [d_in][r]) and the ints
-``d_in``, ``d_out``, ``r``, as drawn by ``linear_02_amd.inputs.theta`` and
-moved with :func:`theta_to`.
+A theta is a dict with device tensors ``W0`` ([d_out][d_in]), ``s`` (fp32
+[d_out] or None), ``U`` ([d_out][r]), ``V`` ([d_in][r]) and the ints ``d_in``,
+``d_out``, ``r``, as drawn by ``linear_02_amd.inputs.theta`` and moved with
+:func:`theta_to`. W0, U, V, x and the outputs are all bf16 or all fp32 (the
+dtype of W0 picks the variant).
 """
 from __future__ import annotations
 
@@ -30,10 +31,14 @@ class WlError(RuntimeError):
         self.status = status
 
 
+DTYPE_BF16, DTYPE_F32 = 0, 1
+_CODES = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}
+
+
 class Theta(ctypes.Structure):
     _fields_ = [("W0", ctypes.c_void_p), ("s", ctypes.c_void_p), ("U", ctypes.c_void_p),
                 ("V", ctypes.c_void_p), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
-                ("r", ctypes.c_int32)]
+                ("r", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 def _load(path: str = LIBRARY) -> ctypes.CDLL:
@@ -96,15 +101,16 @@ def make_theta(th: dict) -> Theta:
     """The C struct of a theta dict (device tensors). The dict keeps them alive."""
     W0, s, U, V = th["W0"], th.get("s"), th.get("U"), th.get("V")
     d_in, d_out, r = int(th["d_in"]), int(th["d_out"]), int(th["r"])
-    if W0.dtype != torch.bfloat16 or not W0.is_contiguous() or tuple(W0.shape) != (d_out, d_in):
-        raise ValueError("W0 must be a contiguous bf16 [d_out][d_in] tensor")
+    if W0.dtype not in _CODES or not W0.is_contiguous() or tuple(W0.shape) != (d_out, d_in):
+        raise ValueError("W0 must be a contiguous bf16 or fp32 [d_out][d_in] tensor")
     if s is not None and (s.dtype != torch.float32 or not s.is_contiguous() or s.numel() != d_out):
         raise ValueError("s must be a contiguous fp32 [d_out] tensor or None")
     if r > 0:
         for name, t, rows in (("U", U, d_out), ("V", V, d_in)):
-            if t is None or t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != (rows, r):
-                raise ValueError(f"{name} must be a contiguous bf16 [{rows}][{r}] tensor")
-    return Theta(_ptr(W0), _ptr(s), _ptr(U) if r > 0 else None, _ptr(V) if r > 0 else None, d_in, d_out, r)
+            if t is None or t.dtype != W0.dtype or not t.is_contiguous() or tuple(t.shape) != (rows, r):
+                raise ValueError(f"{name} must be a contiguous [{rows}][{r}] tensor of W0's dtype")
+    return Theta(_ptr(W0), _ptr(s), _ptr(U) if r > 0 else None, _ptr(V) if r > 0 else None, d_in, d_out, r,
+                 _CODES[W0.dtype])
 
 
 def workspace_bytes(op: int, thetas: list, T: int) -> int:
@@ -135,20 +141,20 @@ class Workspace:
 WORKSPACE = Workspace()
 
 
-def _io(x: torch.Tensor, d_in: int) -> int:
-    if x.dtype != torch.bfloat16 or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != d_in:
-        raise ValueError(f"x must be a contiguous bf16 [T][{d_in}] tensor")
+def _io(x: torch.Tensor, d_in: int, dtype: torch.dtype) -> int:
+    if x.dtype != dtype or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != d_in:
+        raise ValueError(f"x must be a contiguous {dtype} [T][{d_in}] tensor")
     if not x.is_cuda:
         raise ValueError("x must be a device tensor")
     return x.shape[0]
 
 
 def wl_linear(th: dict, x: torch.Tensor, y: torch.Tensor | None = None, ws: torch.Tensor | None = None):
-    """y = s (.) (W0 x) + U (V^T x), bf16 [T][d_out]."""
-    T = _io(x, int(th["d_in"]))
+    """y = s (.) (W0 x) + U (V^T x), [T][d_out] of W0's dtype."""
+    T = _io(x, int(th["d_in"]), th["W0"].dtype)
     st = make_theta(th)
     if y is None:
-        y = torch.empty(T, int(th["d_out"]), dtype=torch.bfloat16, device=x.device)
+        y = torch.empty(T, int(th["d_out"]), dtype=th["W0"].dtype, device=x.device)
     need = workspace_bytes(OP_LINEAR, [th], T)
     ws = ws if ws is not None else WORKSPACE.get(x.device, need)
     _check(lib.wl_linear(ctypes.byref(st), _ptr(x), _ptr(y), T, _ptr(ws),
@@ -158,12 +164,12 @@ def wl_linear(th: dict, x: torch.Tensor, y: torch.Tensor | None = None, ws: torc
 
 def wl_qkv_fused(q: dict, k: dict, v: dict, x: torch.Tensor, y: torch.Tensor | None = None,
                  ws: torch.Tensor | None = None):
-    """Q | K | V side by side, bf16 [T][dq + dk + dv]."""
-    T = _io(x, int(q["d_in"]))
+    """Q | K | V side by side, [T][dq + dk + dv] of the thetas' dtype."""
+    T = _io(x, int(q["d_in"]), q["W0"].dtype)
     sq, sk, sv = make_theta(q), make_theta(k), make_theta(v)
     width = int(q["d_out"]) + int(k["d_out"]) + int(v["d_out"])
     if y is None:
-        y = torch.empty(T, width, dtype=torch.bfloat16, device=x.device)
+        y = torch.empty(T, width, dtype=q["W0"].dtype, device=x.device)
     need = workspace_bytes(OP_QKV, [q, k, v], T)
     ws = ws if ws is not None else WORKSPACE.get(x.device, need)
     _check(lib.wl_qkv_fused(ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(sv), _ptr(x), _ptr(y), T,
@@ -173,11 +179,11 @@ def wl_qkv_fused(q: dict, k: dict, v: dict, x: torch.Tensor, y: torch.Tensor | N
 
 def wl_mlp_fused(gate: dict, up: dict, down: dict, x: torch.Tensor, y: torch.Tensor | None = None,
                  ws: torch.Tensor | None = None):
-    """down(bf16(gelu_tanh(gate x) * up x)), bf16 [T][down.d_out]."""
-    T = _io(x, int(gate["d_in"]))
+    """down(round(gelu_tanh(gate x) * up x)), [T][down.d_out] of the thetas' dtype."""
+    T = _io(x, int(gate["d_in"]), gate["W0"].dtype)
     sg, su, sd = make_theta(gate), make_theta(up), make_theta(down)
     if y is None:
-        y = torch.empty(T, int(down["d_out"]), dtype=torch.bfloat16, device=x.device)
+        y = torch.empty(T, int(down["d_out"]), dtype=gate["W0"].dtype, device=x.device)
     need = workspace_bytes(OP_MLP, [gate, up, down], T)
     ws = ws if ws is not None else WORKSPACE.get(x.device, need)
     _check(lib.wl_mlp_fused(ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), _ptr(x), _ptr(y), T,
@@ -186,18 +192,18 @@ def wl_mlp_fused(gate: dict, up: dict, down: dict, x: torch.Tensor, y: torch.Ten
 
 
 def wl_materialize_weff(th: dict, W_eff: torch.Tensor | None = None):
-    """W_eff = bf16(s (.) W0 + U V^T), bf16 [d_out][d_in]."""
+    """W_eff = round(s (.) W0 + U V^T), [d_out][d_in] of W0's dtype."""
     st = make_theta(th)
     dev = th["W0"].device
     if W_eff is None:
-        W_eff = torch.empty(int(th["d_out"]), int(th["d_in"]), dtype=torch.bfloat16, device=dev)
+        W_eff = torch.empty(int(th["d_out"]), int(th["d_in"]), dtype=th["W0"].dtype, device=dev)
     _check(lib.wl_materialize_weff(ctypes.byref(st), _ptr(W_eff), _stream(dev)))
     return W_eff
 
 
 def bundle_size(thetas: list) -> tuple:
     """(bundle bytes, dense bytes) of a set of thetas: each distinct W0 counted once,
-    s, U and V per theta, against the bf16 dense weights they stand for."""
+    s, U and V per theta, against the dense weights (of the thetas' dtype) they stand for."""
     structs = [make_theta(t) for t in thetas]
     arr = (ctypes.POINTER(Theta) * len(structs))(*[ctypes.pointer(st) for st in structs])
     b, d = ctypes.c_size_t(0), ctypes.c_size_t(0)

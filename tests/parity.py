@@ -45,6 +45,34 @@ def check(y_gpu: torch.Tensor, y_ref: np.ndarray, bound: np.ndarray, what: str =
     return dict(rel_l2=rel, max_err_over_bound=worst)
 
 
+# fp32 variant. Sums of n products accumulated in fp32 (fused multiply-adds, any
+# order) err by at most about n * 2^-24 of the sum of the magnitudes (Higham's
+# gamma_n), so the per-element bar is (n + 4) * 2^-24 * bound, with n the longest
+# accumulation of the call (d_in + r; the MLP adds the gate/up path, whose h
+# errors feed the down projection). Rounding errors of random sign grow like
+# sqrt(n) * 2^-24 of the output norm; relL2 <= 4 * sqrt(n) * 2^-24.
+EPS32 = 2.0 ** -24
+
+
+def check_f32(y_gpu: torch.Tensor, y_ref: np.ndarray, bound: np.ndarray, n_acc: int, what: str = "") -> dict:
+    assert y_gpu.dtype == torch.float32, f"{what}: output is {y_gpu.dtype}"
+    yg = y_gpu.detach().cpu().double().numpy().reshape(y_ref.shape)
+    assert np.all(np.isfinite(yg)), f"{what}: non-finite output"
+    diff = yg - y_ref
+    nref = float(np.linalg.norm(y_ref))
+    ndiff = float(np.linalg.norm(diff))
+    rel = ndiff / nref if nref > 0 else (0.0 if ndiff == 0 else float("inf"))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, np.abs(diff) / bound, np.where(diff == 0, 0.0, np.inf))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    rel_bar, elem_bar = 4.0 * np.sqrt(n_acc) * EPS32, (n_acc + 4) * EPS32
+    if y_ref.size >= MIN_REL_L2_ELEMS:
+        assert rel <= rel_bar, f"{what}: relL2 {rel:.3e} > {rel_bar:.3e}"
+    assert worst <= elem_bar, (f"{what}: max |err|/bound {worst:.3e} > {elem_bar:.3e} at "
+                               f"{np.unravel_index(ratio.argmax(), ratio.shape)}")
+    return dict(rel_l2=rel, max_err_over_bound=worst)
+
+
 def check_exact(y_gpu: torch.Tensor, y_ref: np.ndarray, what: str = "") -> None:
     yg = to_f64(y_gpu).reshape(y_ref.shape)
     bad = np.argwhere(yg != y_ref)

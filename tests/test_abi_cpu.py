@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol(wl):
 
 
 def test_abi_version_and_status_strings(wl):
-    assert wl.abi_version() == 2
+    assert wl.abi_version() == 3
     assert wl.lib.wl_status_str(0) == b"ok"
     assert wl.lib.wl_status_str(4) == b"workspace too small"
     assert wl.lib.wl_status_str(99) == b"unknown status"
@@ -241,6 +241,55 @@ def test_bundle_checks(wl):
     assert bundle(wl, [wl.Theta(A, None, B, C, 60, 32, 4)])[0] == 1
     st, b, d = bundle(wl, [wl.Theta(A, None, B, C, 64, 32, 0)])
     assert (st, b, d) == (0, 2 * 64 * 32, 2 * 64 * 32)   # r = 0, no s: the bundle is W0 itself
+
+
+# -- the fp32 variant: host checks ------------------------------------------------------------
+
+F32 = 1
+
+
+def test_dtype_is_checked(wl):
+    bad = theta()
+    bad.dtype = 2
+    assert call_linear(wl, bad) == 2 and b"dtype" in wl.lib.wl_last_error()
+    arr = (ctypes.POINTER(wl.Theta) * 1)(ctypes.pointer(bad))
+    assert wl.lib.wl_workspace_bytes(0, arr, 1, 1) == 0
+
+
+def test_fused_calls_need_one_dtype(wl):
+    q, k = theta(d_in=64), theta(W0=A + 0x100000, d_in=64)
+    v = theta(W0=A + 0x200000, d_in=64)
+    k.dtype = F32
+    rc = wl.lib.wl_qkv_fused(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), D, D + 0x1000000, 1,
+                             D + 0x2000000, 1 << 30, None)
+    assert rc == 1 and b"dtype" in wl.lib.wl_last_error()
+    gate, up = theta(W0=A, d_in=64, d_out=128), theta(W0=A + 0x100000, d_in=64, d_out=128)
+    down = theta(W0=A + 0x200000, d_in=128, d_out=64)
+    down.dtype = F32
+    rc = wl.lib.wl_mlp_fused(ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down), D, D + 0x1000000,
+                             1, D + 0x2000000, 1 << 30, None)
+    assert rc == 1 and b"dtype" in wl.lib.wl_last_error()
+
+
+def test_f32_sizes(wl):
+    # Overlap checks count 4-byte elements: W0 of 32 x 64 fp32 spans 8192 bytes from A.
+    th = theta()
+    th.dtype = F32
+    assert call_linear(wl, th, y=A + 5120) == 1 and b"overlap" in wl.lib.wl_last_error()
+    # The fp32 MLP keeps h = [T][d_ff] fp32 in the workspace.
+    g, u = theta(d_in=1152, d_out=6912, r=32), theta(W0=A + 0x100000, d_in=1152, d_out=6912, r=32)
+    d = theta(W0=A + 0x200000, d_in=6912, d_out=1152, r=32)
+    for t_ in (g, u, d):
+        t_.dtype = F32
+    mlp_arr = (ctypes.POINTER(wl.Theta) * 3)(ctypes.pointer(g), ctypes.pointer(u), ctypes.pointer(d))
+    sizes = [wl.lib.wl_workspace_bytes(2, mlp_arr, 3, T) for T in (1, 8, 2048)]
+    assert sizes == sorted(sizes) and sizes[-1] >= 2048 * 6912 * 4 and all(s % 256 == 0 for s in sizes)
+    # Bundle sizes count 4 bytes per fp32 element; a W0 shared across dtypes is an error.
+    st, b, dn = bundle(wl, [wl.Theta(A, None, B, C, 64, 32, 0, F32)])
+    assert (st, b, dn) == (0, 4 * 64 * 32, 4 * 64 * 32)
+    st, b, dn = bundle(wl, [wl.Theta(A, D, B, C, 64, 32, 2, F32)])
+    assert (st, b, dn) == (0, 4 * 64 * 32 + 4 * 32 + 4 * 2 * (32 + 64), 4 * 64 * 32)
+    assert bundle(wl, [wl.Theta(A, None, B, C, 64, 32, 0, F32), wl.Theta(A, None, B, C, 64, 32, 0, 0)])[0] == 1
 
 
 def test_rel_frob_checks(wl):
