@@ -415,7 +415,6 @@ wl_status run_proj_f32(const wl_theta *const *ths, int n_ch, bool pair, int d_in
     vj.x = static_cast<const float *>(x);
     vj.d_in = d_in;
     vj.T = T;
-    vj.slice_len = wl::kF32VtxSlice;
     vj.n_slices = wl::f32_vtx_slices(d_in);
     size_t poff = L.f32_part, voff = L.f32_vtx;
     int col0 = 0;

@@ -199,7 +199,7 @@ struct F32Vtx {
     float *part[kMaxChildren];
     float *vtx[kMaxChildren];
     int r[kMaxChildren];            // 1 <= r_c <= kMaxRank
-    int n_ch, d_in, T, n_slices, slice_len;
+    int n_ch, d_in, T, n_slices;    // n_slices = f32_vtx_slices(d_in)
 };
 int f32_vtx_slices(int d_in);
 hipError_t launch_f32_vtx(const F32Vtx &job, hipStream_t stream);

@@ -89,6 +89,14 @@ def test_linear_rejects_bad_theta(wl, case, status):
     assert wl.lib.wl_last_error() != b""
 
 
+def test_tensor_size_limit(wl):
+    # W0 of exactly 2^31 elements is one too many; 2^31 - 32768 is accepted (the
+    # call then fails only on the fake workspace size).
+    assert call_linear(wl, theta(d_in=32768, d_out=65536)) == 1
+    assert b"2^31" in wl.lib.wl_last_error()
+    assert call_linear(wl, theta(d_in=32768, d_out=65535), ws_bytes=0) == 4
+
+
 def test_linear_rejects_null_theta_and_io(wl):
     assert call_linear(wl, None) == 1
     assert call_linear(wl, theta(), x=None) == 1
