@@ -539,7 +539,8 @@ def write_traffic(args) -> int:
     path = os.path.join(REPO, "profiles", f"traffic_{traffic_key(args, args.workload)}_r{r}_T{T}.txt")
     def rel(pth):
         return os.path.relpath(os.path.dirname(os.path.abspath(pth)), REPO)
-    run = f"python3 bench.py --workload {args.workload} --rank {r}" + (" --shared-w0" if args.shared_w0 else "")
+    run = (f"python3 bench.py --workload {args.workload} --rank {r}" + (" --shared-w0" if args.shared_w0 else "")
+           + (" --dtype f32" if args.dtype == "f32" else ""))
     with open(path, "w") as f:
         f.write(f"# HBM traffic of the dominant call of bench.py --workload {args.workload} (r={r}, T={T}),\n"
                 f"# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE passes over a --dominant-only run,\n"
