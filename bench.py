@@ -134,7 +134,7 @@ def _regime_sources(tokens: int, dtype: str = "bf16") -> tuple:
     if dtype == "f32":
         return ("k_f32.hip",)
     if tokens <= 8:
-        return ("k_gemv.hip", "k_vtx.hip")
+        return ("k_gemv.hip", "k_vtx.hip", "wl_vtx_slice.h")
     if tokens <= 64:
         return ("k_skinny.hip",)
     return ("k_gemm.hip", "k_vtxmm.hip")

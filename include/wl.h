@@ -49,9 +49,19 @@
  *            NULL = the default stream) and returns; errors that happen on the
  *            device surface at the caller's next synchronization.
  * Workspace. Operations that take `ws` need at least wl_workspace_bytes(...)
- *            bytes of scratch device memory; its contents on entry do not
- *            matter. Calls that can run at the same time (different streams)
- *            must not share a workspace.
+ *            bytes of device memory. For wl_linear, wl_qkv_fused and
+ *            wl_mlp_fused its first WL_SYNC_BYTES bytes are a sync area
+ *            (counters and generation-tagged words by which the decode
+ *            kernel's workgroups hand V^T x to each other within one launch,
+ *            "In-kernel reconstruction"): the caller zeroes them
+ *            once, before the workspace's first use, and does not write them
+ *            afterwards; the calls keep them consistent from then on. A sync
+ *            area holding anything else can make results wrong. Bytes 4088
+ *            to 4095 of the area count (int64) the decode workgroups that
+ *            stopped waiting and computed V^T x themselves (a diagnostic; the
+ *            result is the same). The rest of the workspace is scratch whose
+ *            contents on entry do not matter. Calls that can run at the same
+ *            time (different streams) must not share a workspace.
  * Errors.    Every argument is checked on the host before anything is
  *            enqueued; a fused operation checks all of its thetas first, so an
  *            invalid argument never leaves a partial launch.
@@ -78,7 +88,10 @@
 extern "C" {
 #endif
 
-#define WL_ABI_VERSION 3
+#define WL_ABI_VERSION 4
+
+/* Bytes at the start of a projection workspace that hold the sync area. */
+#define WL_SYNC_BYTES 203776
 
 typedef enum {
     WL_OK = 0,
@@ -194,13 +207,21 @@ wl_status wl_relative_frobenius_error(const void *W, const void *R, int64_t n, d
  * default), 1 forces the decode GEMV wherever it applies (V^T x computed by
  * every workgroup when V is small, else by a separate launch before it), 2
  * forces the matrix-core GEMM, 3 forces the decode GEMV with V^T x always
- * computed by a separate launch, 4 forces the few-token path (split matrix-core
+ * computed by a separate launch (never by workgroups of the same launch), 4 forces the few-token path (split matrix-core
  * products and an epilogue launch) wherever it applies (T <= 64, d_in <= 8192).
  * Where a forced regime does not apply the matrix-core GEMM runs. Results agree
  * within rounding in every regime; the switch exists for tests and
  * measurements. Process-wide; returns the previous value, or -1 (and changes
  * nothing) for any other argument. */
 int32_t wl_set_regime(int32_t regime);
+
+/* Bound on the wait of a decode workgroup for the V^T x slices that other
+ * workgroups of its launch compute (one to two tokens per pass): the number of
+ * times it reads a group of slice words again, default 4096. A workgroup whose wait runs out
+ * computes every slice itself, in the same order, so the result does not
+ * change; 0 makes every workgroup do so (for tests). Process-wide; returns the
+ * previous value, or -1 (and changes nothing) for a negative argument. */
+int32_t wl_set_spin_limit(int32_t polls);
 
 /* Static description of a status code. */
 const char *wl_status_str(wl_status status);

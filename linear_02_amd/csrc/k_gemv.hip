@@ -13,10 +13,26 @@
 //     unit (a 16-byte column of V, or a part of one), its lanes walk the rows,
 //     and a wave sum per rank entry finishes the unit; units of one column are
 //     added in part order. No workgroup depends on another.
-//   * Slice partials (otherwise): a V^T x launch just before this one wrote
-//     per-slice partial sums; they are loaded before the W0 stream and added in
-//     fixed groups of 16 slices, group sums in order, the same association in
-//     every workgroup and for a child computed alone or with Q/K/V siblings.
+//   * Slice partials (otherwise): per-slice partial sums are added in fixed
+//     groups of 16 slices, group sums in order, the same association in every
+//     workgroup and for a child computed alone or with Q/K/V siblings. The
+//     partials come from one of two places:
+//     - In-launch (at most 2 tokens per pass): the first workgroups of this
+//       launch are producers, one per (child, slice), each computing its slice
+//       as the V^T x launch would. Each partial is stored as one 64-bit word,
+//       the launch's tag (generation + 1, from a ticket counter) beside the
+//       fp32 value, by a single device-scope atomic store. The other
+//       workgroups take the same tag at their start, stream W0, then read the
+//       words with device-scope atomic loads and read again any word still
+//       without their tag. A word with the right tag holds the right value,
+//       so no fence or flag is needed (a release fence writes back the whole
+//       L2 on this chip and cost more than the separate launch it replaces).
+//       Producers come first in the grid, so they are dispatched before any
+//       workgroup waits for them, and each wait is bounded: a workgroup whose
+//       wait runs out computes every slice itself in the same order, and gets
+//       the same bits.
+//     - A V^T x launch just before this one; the partials are then loaded
+//       before the W0 stream.
 // W0 x. A workgroup owns a few consecutive output rows; each of its four waves
 //   streams R rows (or one segment of a long row) with its 64 lanes side by
 //   side, 16 bytes per lane per load and up to 8 loads per row in flight. Each
@@ -37,6 +53,7 @@
 //   bf16(gelu_tanh(g) * u).
 #include "wl_device.h"
 #include "wl_kernels.h"
+#include "wl_vtx_slice.h"
 
 namespace wl {
 
@@ -47,6 +64,10 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxRowsG = 8;                 // rows per workgroup: (4 / nseg) * R <= 8
 constexpr int kUPerThread = kMaxRowsG * 2 * kMaxRank / kThreads;
 constexpr int kGroup = 16;                   // slices per group in the partial sums
+#ifndef WL_ONE_LEVEL_MAX_KB
+#define WL_ONE_LEVEL_MAX_KB 3072
+#endif
+constexpr long long kOneLevelMaxBytes = (long long)WL_ONE_LEVEL_MAX_KB << 10;   // in-launch hand-off, see gemv_plan
 
 __device__ __forceinline__ int child_index(const GemvF &g, int row) {
     if (g.n_ch > 2 && row >= g.ch[2].col0) return 2;
@@ -103,7 +124,7 @@ __device__ __forceinline__ void vtx_item(const GemvF &g, int tt, int item, int &
 __device__ __forceinline__ float group_sum(const float *base, int stride, int s0, int s1) {
     float v[kGroup];
 #pragma unroll
-    for (int u = 0; u < kGroup; ++u) v[u] = base[(size_t)min(s0 + u, s1 - 1) * stride];
+    for (int u = 0; u < kGroup; ++u) v[u] = ldg(base + (size_t)min(s0 + u, s1 - 1) * stride);
     float sum = 0.f;
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) sum += s0 + u < s1 ? v[u] : 0.f;
@@ -146,6 +167,262 @@ __device__ void gather_full(const GemvF &g, int n_items, float (*vs)[TT][kMaxRan
         float sum = 0.f;
         for (int s0 = 0; s0 < g.S; s0 += kGroup) sum += group_sum(base, TT * r, s0, min(g.S, s0 + kGroup));
         vs[c][t][k] = sum;
+    }
+}
+
+// ---- in-launch hand-off ----
+
+// This workgroup's ticket (thread 0 only): one fetch-add on counter copy
+// blockIdx % kSyncCopies. Every copy gains exactly kSyncStride per launch: the
+// copy's last workgroup adds what its others leave, and workgroup 0 also
+// advances the copies no workgroup maps to. So every ticket of one launch lies
+// in [gen * kSyncStride, (gen + 1) * kSyncStride), whatever the order of the adds.
+__device__ __forceinline__ unsigned long long take_ticket(const GemvF &g) {
+    const int grid = gridDim.x, b = blockIdx.x, c = b % kSyncCopies;
+    const int n_c = (grid - c + kSyncCopies - 1) / kSyncCopies;
+    const unsigned long long add = b + kSyncCopies >= grid ? kSyncStride - (unsigned long long)(n_c - 1) : 1ull;
+    // The address is uniform; hiding that keeps the compiler from rewriting the
+    // add as a wave-combined one whose result it would wait for right here,
+    // before the loads that follow are issued.
+    auto *ctr = (__attribute__((address_space(1))) unsigned long long *)(g.sync + c);
+    asm volatile("" : "+v"(ctr));
+    return __hip_atomic_fetch_add(ctr, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void advance_empty_copies(const GemvF &g) {
+    const int e = threadIdx.x;
+    if (blockIdx.x == 0 && e >= (int)gridDim.x && e < kSyncCopies)
+        __hip_atomic_fetch_add(g.sync + e, kSyncStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The launch's tag from thread 0's ticket: the generation mapped into
+// [1, 2^32 - 1] (never 0, the tag of a word no launch has written).
+__device__ __forceinline__ uint32_t ticket_tag(unsigned long long ticket) {
+    // Opaque to the compiler, so the division is not moved up to the atomic
+    // (where its wait would hold back the loads issued after it).
+    asm volatile("" : "+v"(ticket));
+    return (uint32_t)((ticket / kSyncStride) % 0xFFFFFFFFull) + 1u;
+}
+
+// Child index of the j-th child with r > 0 (j < number of such children).
+__device__ __forceinline__ int vtx_child(const GemvF &g, int j) {
+    const int a0 = g.ch[0].r > 0, a1 = g.n_ch > 1 && g.ch[1].r > 0;
+    if (j == 0) return a0 ? 0 : a1 ? 1 : 2;
+    if (j == 1) return a0 && a1 ? 1 : 2;
+    return 2;
+}
+
+// Tagged slice partials: word [c][slice][t][k] of the partial area, 64 bits,
+// the launch's tag in the high half and the fp32 partial in the low half,
+// written and read with single device-scope atomic accesses. A reader that
+// sees the tag of its own launch therefore sees that launch's value: nothing
+// depends on the order in which different words become visible.
+__device__ __forceinline__ unsigned long long *tagged_base(const GemvF &g, int c) {
+    return g.tagged + (size_t)c * kGemvTaggedPerChild;
+}
+__device__ __forceinline__ unsigned long long ld_word(const unsigned long long *p) {
+    return __hip_atomic_load(const_cast<unsigned long long *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float word_value(unsigned long long w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ bool word_is(unsigned long long w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+
+// Tagged gathers of a projection workgroup, in the association of the plain
+// ones. Only words of tokens present in the pass (t < tn) are waited for; a
+// word still without this launch's tag is read again, at most spin_limit more
+// times per group. False when some wait ran out (spin_limit 0: at once).
+
+// Split mapping: thread (item, group) reads its group's words.
+template <int TT>
+__device__ __forceinline__ bool gather_tagged_split(const GemvF &g, int n_items, int n_groups, uint32_t tag,
+                                                    float (&v)[kGroup], int &n) {
+    int item = threadIdx.x / n_groups;
+    const int grp = threadIdx.x - item * n_groups;
+    const bool in = item < n_items;
+    item = in ? item : 0;
+    int c, t, k;
+    vtx_item(g, TT, item, c, t, k);
+    const int r = ch_r(g, c);
+    const unsigned long long *base = tagged_base(g, c) + t * r + k;
+    const int s0 = grp * kGroup, s1 = min(g.S, s0 + kGroup);
+    const bool need = in && g.t0 + t < g.T;
+    unsigned long long w[kGroup];
+    bool ok = g.spin_limit > 0;
+    for (int spin = 0; ok; ++spin) {
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) w[u] = ld_word(base + (size_t)min(s0 + u, s1 - 1) * (TT * r));
+        bool ready = true;
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) ready = ready && (!need || word_is(w[u], tag));
+        if (ready) break;
+        ok = spin < g.spin_limit;
+    }
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) v[u] = word_value(w[u]);
+    n = in ? s1 - s0 : 0;
+    return ok;
+}
+
+// Full mapping: thread per item, groups in order, into vs.
+template <int TT>
+__device__ bool gather_tagged_full(const GemvF &g, int n_items, uint32_t tag, float (*vs)[TT][kMaxRank]) {
+    bool ok = g.spin_limit > 0;
+    for (int item = threadIdx.x; item < n_items && ok; item += kThreads) {
+        int c, t, k;
+        vtx_item(g, TT, item, c, t, k);
+        const int r = ch_r(g, c);
+        const unsigned long long *base = tagged_base(g, c) + t * r + k;
+        const bool need = g.t0 + t < g.T;
+        float sum = 0.f;
+        for (int s0 = 0; s0 < g.S && ok; s0 += kGroup) {
+            const int s1 = min(g.S, s0 + kGroup);
+            unsigned long long w[kGroup];
+            for (int spin = 0;; ++spin) {
+#pragma unroll
+                for (int u = 0; u < kGroup; ++u) w[u] = ld_word(base + (size_t)min(s0 + u, s1 - 1) * (TT * r));
+                bool ready = true;
+#pragma unroll
+                for (int u = 0; u < kGroup; ++u) ready = ready && (!need || word_is(w[u], tag));
+                if (ready) break;
+                if (spin >= g.spin_limit) {
+                    ok = false;
+                    break;
+                }
+            }
+            float gs = 0.f;
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) gs += s0 + u < s1 ? word_value(w[u]) : 0.f;
+            sum += gs;
+        }
+        vs[c][t][k] = sum;
+    }
+    return ok;
+}
+
+__device__ __forceinline__ unsigned long long *final_words(const GemvF &g) {
+    return g.sync + kSyncFinalOffset / 8;
+}
+
+// Producer workgroup p: slice p % S of child vtx_child(p / S), for the pass's
+// tokens, as the V^T x launch computes it, stored as tagged words. With
+// two_level, producer 0 then gathers every slice as a projection workgroup
+// would (same association, same bits) and stores the complete V^T x as one
+// tagged word per item.
+template <int TT>
+__device__ void vtx_produce(const GemvF &g, float (*red)[TT + 1], uint32_t *tag_lds, float *gsum,
+                            float (*vs)[TT][kMaxRank]) {
+    const int tid = threadIdx.x, p = blockIdx.x;
+    unsigned long long ticket;
+    if (tid == 0) ticket = take_ticket(g);
+    advance_empty_copies(g);
+    const int slice = p % g.S, c = vtx_child(g, p / g.S);
+    const int r = ch_r(g, c);
+    const uint16_t *V = reinterpret_cast<const uint16_t *>(
+        blend3(c, (uint64_t)g.ch[0].V, (uint64_t)g.ch[1].V, (uint64_t)g.ch[2].V));
+    const int i0 = slice * g.slice_len, len = max(0, min(g.d_in - i0, g.slice_len));
+    const int tn = min(TT, g.T - g.t0);
+    const VtxXGlobal<TT> xg{g.x + (size_t)g.t0 * g.d_in, g.d_in, i0, tn};
+    if (tid == 0) *tag_lds = ticket_tag(ticket);
+    vtx_slice_sums<TT>(V, r, i0, len, xg, red);   // its barriers publish tag_lds
+    const uint32_t tag32 = *tag_lds;
+    const unsigned long long tag = (unsigned long long)tag32 << 32;
+    unsigned long long *part = tagged_base(g, c) + (size_t)slice * TT * r;
+    for (int idx = tid; idx < r * tn; idx += kThreads) {
+        const int t = idx / r, kk = idx - t * r;
+        const unsigned long long w = tag | __float_as_uint(vtx_slice_total<TT>(red, r, t, kk));
+        __hip_atomic_store(part + t * r + kk, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!g.two_level || p != 0) return;
+
+    const int n_items = vtx_items(g, TT);
+    const int n_groups = (g.S + kGroup - 1) / kGroup;
+    const bool split = n_items * n_groups <= kThreads;
+    float gv[kGroup];
+    int gn = 0;
+    const bool got = split ? gather_tagged_split<TT>(g, n_items, n_groups, tag32, gv, gn)
+                           : gather_tagged_full<TT>(g, n_items, tag32, vs);
+    if (__syncthreads_or(!got)) return;   // the projection workgroups will compute V^T x themselves
+    if (split) {
+        gsum[tid] = gather_finish(gv, gn);
+        __syncthreads();
+    }
+    unsigned long long *fin = final_words(g);
+    for (int item = tid; item < n_items; item += kThreads) {
+        int cc, t, k;
+        vtx_item(g, TT, item, cc, t, k);
+        float v;
+        if (split) {
+            v = 0.f;
+            for (int j = 0; j < n_groups; ++j) v += gsum[item * n_groups + j];
+        } else {
+            v = vs[cc][t][k];
+        }
+        __hip_atomic_store(fin + item, tag | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Two-level: thread per item reads the complete word (again while it lacks the
+// tag, at most spin_limit more times) into vs.
+template <int TT>
+__device__ bool gather_final(const GemvF &g, int n_items, uint32_t tag, float (*vs)[TT][kMaxRank]) {
+    bool ok = g.spin_limit > 0;
+    const unsigned long long *fin = final_words(g);
+    for (int item = threadIdx.x; item < n_items && ok; item += kThreads) {
+        int c, t, k;
+        vtx_item(g, TT, item, c, t, k);
+        const bool need = g.t0 + t < g.T;
+        unsigned long long w;
+        for (int spin = 0;; ++spin) {
+            w = ld_word(fin + item);
+            if (!need || word_is(w, tag)) break;
+            if (spin >= g.spin_limit) {
+                ok = false;
+                break;
+            }
+        }
+        vs[c][t][k] = word_value(w);
+    }
+    return ok;
+}
+
+// Fallback of a workgroup whose wait ran out: every slice of every child with
+// r > 0, computed as the producers do, added in the gathers' association
+// (groups of kGroup slices, each group's sum from 0 and padded with +0 as the
+// gathers pad a short group, group sums in order from 0). gs: LDS, n_items floats.
+template <int TT>
+__device__ void vtx_fallback(const GemvF &g, int n_items, float (*vs)[TT][kMaxRank], float (*red)[TT + 1],
+                             float *gs) {
+    const int tid = threadIdx.x;
+    for (int item = tid; item < n_items; item += kThreads) {
+        int c, t, k;
+        vtx_item(g, TT, item, c, t, k);
+        vs[c][t][k] = 0.f;
+        gs[item] = 0.f;
+    }
+    const int n_v = g.n_prod / g.S;
+    const int tn = min(TT, g.T - g.t0);
+    for (int s = 0; s < g.S; ++s) {
+        const int i0 = s * g.slice_len, len = max(0, min(g.d_in - i0, g.slice_len));
+        const VtxXGlobal<TT> xg{g.x + (size_t)g.t0 * g.d_in, g.d_in, i0, tn};
+        for (int j = 0; j < n_v; ++j) {
+            const int c = vtx_child(g, j);
+            const int r = ch_r(g, c);
+            const uint16_t *V = reinterpret_cast<const uint16_t *>(
+                blend3(c, (uint64_t)g.ch[0].V, (uint64_t)g.ch[1].V, (uint64_t)g.ch[2].V));
+            vtx_slice_sums<TT>(V, r, i0, len, xg, red);   // begins and ends with a barrier
+            for (int item = tid; item < n_items; item += kThreads) {
+                int cc, t, k;
+                vtx_item(g, TT, item, cc, t, k);
+                if (cc == c) gs[item] += vtx_slice_total<TT>(red, r, t, k);
+            }
+        }
+        const bool group_end = (s % kGroup) == kGroup - 1 || s == g.S - 1;
+        if (group_end)
+            for (int item = tid; item < n_items; item += kThreads) {
+                int c, t, k;
+                vtx_item(g, TT, item, c, t, k);
+                float v = gs[item];
+                if ((s % kGroup) != kGroup - 1) v += 0.f;   // a short last group
+                vs[c][t][k] += v;
+                gs[item] = 0.f;
+            }
     }
 }
 
@@ -223,7 +500,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     constexpr int NB0 = (TT <= 2 ? 8 : TT == 4 ? 4 : 2) / (R * P);
     constexpr int NB = NB0 > 0 ? NB0 : 1;       // 16-byte loads per row per lane per batch
     constexpr bool RED_OK = RED && TT <= kRedMaxTok;
+    constexpr bool INL = TT <= 2 && !RED;        // in-launch hand-off (RED instances serve the redundant mode only)
     __shared__ float mbuf[kWaves][R][P][TT];
+    __shared__ float vred[INL ? kThreads : 1][TT + 1];             // producer / fallback slice sums
+    __shared__ float fgs[INL ? kMaxChildren * TT * kMaxRank : 1];  // fallback group sums
+    __shared__ uint32_t tag_lds;
     __shared__ float vs[kMaxChildren][TT][kMaxRank];
     __shared__ float ulds[kMaxRowsG][P][kMaxRank];
     __shared__ float slds[kMaxRowsG][P];
@@ -236,9 +517,20 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     const int nch = g.d_in >> 3;
     const int nseg = g.nseg;
     const int rows_g = (kWaves / nseg) * R;
-    const int rowbase = blockIdx.x * rows_g;
     const bool red = RED_OK && g.vmode == kVtxRedundant;
     const bool parts = g.vmode == kVtxPartials;
+    const bool inl = INL && g.vmode == kVtxInLaunch;
+    unsigned long long ticket;   // thread 0 of an in-launch projection workgroup only
+    if constexpr (INL) {
+        if (inl) {
+            if ((int)blockIdx.x < g.n_prod) {
+                vtx_produce<TT>(g, vred, &tag_lds, gsum, vs);
+                return;
+            }
+            if (tid == 0) ticket = take_ticket(g);   // used after the stream
+        }
+    }
+    const int rowbase = ((int)blockIdx.x - g.n_prod) * rows_g;
 
     // ---- everything the epilogue needs, issued before the stream ----
     const ChFields cf(g);
@@ -334,6 +626,22 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
                 }
     }
 
+    // ---- V^T x from this launch's producers ----
+    bool have = false, fallback = false;
+    if constexpr (INL) {
+        if (inl) {
+            if (tid == 0) tag_lds = ticket_tag(ticket);
+            __syncthreads();
+            const bool got = g.two_level ? gather_final<TT>(g, n_items, tag_lds, vs)
+                             : split       ? gather_tagged_split<TT>(g, n_items, n_groups, tag_lds, gv, gn)
+                                           : gather_tagged_full<TT>(g, n_items, tag_lds, vs);
+            fallback = __syncthreads_or(!got);
+            have = !fallback;
+            if (fallback && tid == 0)
+                __hip_atomic_fetch_add(g.sync + kSyncFallbackWord, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
     // ---- epilogue ----
 #pragma unroll
     for (int u = 0; u < kUPerThread; ++u) {
@@ -343,14 +651,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     if (tid < rows_g * P) (&slds[0][0])[tid] = spre;
     if constexpr (RED_OK)
         if (red) red_reduce<TT>(g, rl, wave, lane, upart);
-    if (parts) {
+    if (parts || (have && !g.two_level)) {
         if (split)
             gsum[tid] = gather_finish(gv, gn);
-        else
-            gather_full<TT>(g, n_items, vs);
+        else if (parts)
+            gather_full(g, n_items, vs);
     }
+    if constexpr (INL)
+        if (fallback) vtx_fallback<TT>(g, n_items, vs, vred, fgs);
     __syncthreads();
-    if (parts && split)
+    if ((parts || (have && !g.two_level)) && split)
         for (int item = tid; item < n_items; item += kThreads) {
             float sum = 0.f;
             for (int j = 0; j < n_groups; ++j) sum += gsum[item * n_groups + j];
@@ -444,7 +754,9 @@ int gemv_tokens_per_pass(int d_in, int T) {
     return tt;
 }
 
-GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_redundant) {
+namespace {
+
+GemvPlan plan_vtx(const GemvF &g, int tt, bool allow_redundant) {
     GemvPlan p;
     const int nch = g.d_in / 8;
     p.nseg = nch <= 640 ? 1 : nch <= 1280 ? 2 : 4;
@@ -494,24 +806,50 @@ GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_redundant) {
     return p;
 }
 
+}  // namespace
+
+GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_redundant, bool allow_inlaunch) {
+    GemvPlan p = plan_vtx(g, tt, allow_redundant);
+    if (p.vmode != kVtxPartials || !allow_inlaunch || tt > 2) return p;
+    int n_v = 0;
+    for (int c = 0; c < g.n_ch; ++c) n_v += g.ch[c].r > 0;
+    const int n_prod = p.S * n_v;
+    p.vmode = kVtxInLaunch;
+    p.n_prod = n_prod;
+    // One level: every projection workgroup reads every slice word, device-scope
+    // reads that miss L2 and all fall on the same few lines. Measured on the
+    // Gemma-3-1B-shaped layer: up to 2.7 MB of such reads per launch (Q/K/V at
+    // 2 tokens) one level is faster; from 4 MB (gate/up at 1 token) the extra
+    // step of two levels costs less than the reads it saves.
+    int sum_r = 0;
+    for (int c = 0; c < g.n_ch; ++c) sum_r += g.ch[c].r;
+    const long long one_level_bytes = (long long)p.n_wg * tt * sum_r * p.S * 8;
+    p.two_level = one_level_bytes > kOneLevelMaxBytes;
+    return p;
+}
+
 hipError_t launch_gemv(const GemvF &g, const GemvPlan &plan, int tt, hipStream_t stream) {
     GemvF a = g;
     a.nseg = plan.nseg;
     a.S = plan.S;
     a.vmode = plan.vmode;
     a.red_units = plan.red_units;
+    a.n_prod = plan.vmode == kVtxInLaunch ? plan.n_prod : 0;
+    a.two_level = plan.two_level;
+    a.slice_len = plan.slice_len;
     for (int u = 0; u < kWaves; ++u) {
         a.red_c[u] = plan.red_c[u];
         a.red_kc[u] = plan.red_kc[u];
         a.red_lo[u] = plan.red_lo[u];
         a.red_hi[u] = plan.red_hi[u];
     }
+    const int n_wg = plan.n_wg + a.n_prod;   // producers first
     if (g.pair) {
-        if (plan.R == 2) return launch_r<2, 2>(a, tt, plan.n_wg, stream);
-        return launch_r<1, 2>(a, tt, plan.n_wg, stream);
+        if (plan.R == 2) return launch_r<2, 2>(a, tt, n_wg, stream);
+        return launch_r<1, 2>(a, tt, n_wg, stream);
     }
-    if (plan.R == 2) return launch_r<2, 1>(a, tt, plan.n_wg, stream);
-    return launch_r<1, 1>(a, tt, plan.n_wg, stream);
+    if (plan.R == 2) return launch_r<2, 1>(a, tt, n_wg, stream);
+    return launch_r<1, 1>(a, tt, n_wg, stream);
 }
 
 }  // namespace wl

@@ -10,12 +10,13 @@
 // on scheduling. There is no cross-workgroup communication inside the kernel.
 #include "wl_device.h"
 #include "wl_kernels.h"
+#include "wl_vtx_slice.h"
 
 namespace wl {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kVtxSliceThreads;
 
 template <int TB>
 __global__ __launch_bounds__(kThreads) void vtx_kernel(VtxJob job) {
@@ -48,56 +49,19 @@ __global__ __launch_bounds__(kThreads) void vtx_kernel(VtxJob job) {
     const uint16_t *xs = reinterpret_cast<const uint16_t *>(xs_raw);
 
     const int r = job.r[c];
-    int rp = 1;
-    while (rp < r) rp <<= 1;
-    const int k = tid & (rp - 1), g = tid / rp, G = kThreads / rp;
-    const uint16_t *__restrict__ V = job.V[c];
-
-    // Thread (g, k) sums rows g, g+G, ...; the loads of 16 rows are issued
-    // before any of them is used.
-    float acc[TB];
-#pragma unroll
-    for (int t = 0; t < TB; ++t) acc[t] = 0.f;
-    if (k < r) {
-        for (int ib = g; ib < len; ib += 16 * G) {
-            float v[16], xv[16][TB];
-            // Every address is valid (rows clamped into the slice, tokens into
-            // the block) and the values are masked afterwards, so the 16 rows'
-            // loads are all in flight at once.
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int i = ib + u * G;
-                const bool in = i < len;
-                const int ic = min(i, len - 1);
-                const float vv = bf16_f(V[(size_t)(i0 + ic) * r + k]);
-                v[u] = in ? vv : 0.f;
-#pragma unroll
-                for (int t = 0; t < TB; ++t) {
-                    if constexpr (kStage) {
-                        xv[u][t] = bf16_f(xs[t * kVtxMaxSlice + ic]);
-                    } else {
-                        const float xx = bf16_f(job.x[(size_t)(t0 + min(t, tn - 1)) * job.d_in + i0 + ic]);
-                        xv[u][t] = t < tn ? xx : 0.f;
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-#pragma unroll
-                for (int t = 0; t < TB; ++t) acc[t] += v[u] * xv[u][t];
-        }
+    if constexpr (kStage) {
+        vtx_slice_sums<TB>(job.V[c], r, i0, len, [&](int ic, int t) { return bf16_f(xs[t * kVtxMaxSlice + ic]); },
+                           red);
+    } else {
+        const VtxXGlobal<TB> xg{job.x + (size_t)t0 * job.d_in, job.d_in, i0, tn};
+        vtx_slice_sums<TB>(job.V[c], r, i0, len, xg, red);
     }
-#pragma unroll
-    for (int t = 0; t < TB; ++t) red[tid][t] = acc[t];
-    __syncthreads();
 
     // partial[c][slice][t][k]
     float *part = job.partial[c] + (size_t)slice * job.ld_T * r;
     for (int idx = tid; idx < r * tn; idx += kThreads) {
         const int t = idx / r, kk = idx - t * r;
-        float sum = 0.f;
-        for (int gg = 0; gg < G; ++gg) sum += red[gg * rp + kk][t];
-        part[(size_t)(t0 + t) * r + kk] = sum;
+        part[(size_t)(t0 + t) * r + kk] = vtx_slice_total<TB>(red, r, t, kk);
     }
 }
 

@@ -18,6 +18,7 @@
 namespace {
 
 thread_local std::string g_error;
+std::atomic<int> g_spin_limit{wl::kSpinLimit};   // polls before a decode workgroup computes V^T x itself
 std::atomic<int> g_regime{0};   // 0 auto, 1 GEMV, 2 matrix-core GEMM, 3 GEMV always after a V^T x launch, 4 skinny
 
 constexpr size_t kAlign = 256;
@@ -127,9 +128,12 @@ Kind choose(int T, int d_in, int sum_r) {
 // calls, so the two always agree. Every region any regime could use at this T
 // is reserved, so the size does not depend on the regime switch.
 //
-//   [0, 256)          reserved
+//   [0, kSyncBytes)   sync area of the decode kernel's in-launch V^T x hand-off:
+//                     ticket counters, a fallback count and the tagged V^T x
+//                     words (64-bit); zero before the workspace's first use,
+//                     then kept consistent by the kernels
 //   gemv_partial      fp32 3 x [kGemvMaxSlices][kGemvMaxTok][kMaxRank] V^T x slices
-//                     (decode regime)
+//                     (decode regime, V^T x in a launch of its own)
 //   skinny part       fp32 [S][P][T][rows] split partials (T <= kSkMaxTok), the
 //                     largest of the call's projections
 //   skinny vpart      fp32 [n_vsl][n_ch][T][kMaxRank] V^T x slice partials
@@ -139,7 +143,8 @@ Kind choose(int T, int d_in, int sum_r) {
 //                     matrix-core regime (the largest of the call's projections)
 //   h                 bf16 [T][d_ff] (MLP only)
 
-constexpr size_t kReservedBytes = 256;
+constexpr size_t kReservedBytes = wl::kSyncBytes;
+static_assert(WL_SYNC_BYTES == wl::kSyncBytes, "sync area size");
 
 struct Layout {
     size_t gemv_partial = 0;
@@ -346,8 +351,11 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
         g.x = static_cast<const uint16_t *>(x);
         g.y = static_cast<uint16_t *>(y);
         g.partial = reinterpret_cast<float *>(ws + L.gemv_partial);
-        const bool allow_redundant = g_regime.load(std::memory_order_relaxed) != 3;
-        const wl::GemvPlan plan = wl::gemv_plan(g, tt, allow_redundant);
+        g.tagged = reinterpret_cast<unsigned long long *>(ws + wl::kSyncTaggedOffset);
+        g.sync = reinterpret_cast<unsigned long long *>(ws);   // the sync area at offset 0
+        g.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+        const bool separate = g_regime.load(std::memory_order_relaxed) == 3;
+        const wl::GemvPlan plan = wl::gemv_plan(g, tt, !separate, !separate);
         auto part = [&](int c) { return g.partial + (size_t)c * wl::kGemvPartialPerChild; };
         for (int t0 = 0; t0 < T && e == hipSuccess; t0 += tt) {
             g.t0 = t0;
@@ -507,6 +515,11 @@ const char *wl_last_error(void) { return g_error.c_str(); }
 int32_t wl_set_regime(int32_t regime) {
     if (regime < 0 || regime > 4) return -1;
     return g_regime.exchange(regime);
+}
+
+int32_t wl_set_spin_limit(int32_t polls) {
+    if (polls < 0) return -1;
+    return g_spin_limit.exchange(polls);
 }
 
 size_t wl_workspace_bytes(int32_t op, const wl_theta *const *th, int32_t n_th, int32_t T) {

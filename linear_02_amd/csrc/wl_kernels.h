@@ -67,11 +67,35 @@ hipError_t launch_vtx(const VtxJob &job, hipStream_t stream);
 //   y[t][o] = bf16( gelu_tanh(gate value) * up value ).
 // vtx comes either from every workgroup reading V itself (kVtxRedundant) or
 // from slice partials written by a V^T x launch just before (kVtxPartials).
-enum { kVtxNone = 0, kVtxRedundant = 1, kVtxPartials = 2 };
+// kVtxInLaunch: the slice partials are computed by the first n_prod workgroups of
+// the projection's own launch and stored as tagged 64-bit words (the launch's
+// tag beside the value); the other workgroups stream W0, then read the words
+// until each carries their launch's tag (bounded). The tag comes from ticket
+// counters in the workspace's sync area (see kSyncBytes), which also holds the
+// words, so no word is ever reset. A workgroup whose wait runs out computes V^T x itself.
+enum { kVtxNone = 0, kVtxRedundant = 1, kVtxPartials = 2, kVtxInLaunch = 3 };
+// The sync area, the first kSyncBytes of every workspace, 64-bit words:
+//   [0, kSyncCopies)          ticket counters, each advanced by exactly
+//                             kSyncStride per launch that hands V^T x over
+//                             in-launch, so that ticket / kSyncStride is the
+//                             launch's generation in every workgroup
+//   kSyncFallbackWord         count of workgroups that computed V^T x themselves
+//   from kSyncTaggedOffset    the tagged V^T x slice words (kGemvTaggedPerChild per child)
+//   from kSyncFinalOffset     the tagged complete V^T x words, one per (child, token, k)
+//                             item (two-level hand-off)
+// Zero before first use; never reset afterwards.
+constexpr int kSyncCopies = 64;
+constexpr unsigned long long kSyncStride = 1ull << 24;
+constexpr int kSyncFallbackWord = 511;
+constexpr size_t kSyncTaggedOffset = 4096;
+constexpr int kSpinLimit = 1 << 12;   // re-reads of a group of tagged words before a workgroup computes V^T x itself
 constexpr int kGemvMaxTok = 8;                // tokens per pass
 constexpr int kGemvMaxDin = 32768;            // widest input of the decode kernel
 constexpr int kGemvMaxSlices = 64;
 constexpr size_t kGemvPartialPerChild = (size_t)kGemvMaxSlices * kGemvMaxTok * kMaxRank;
+constexpr size_t kGemvTaggedPerChild = (size_t)kGemvMaxSlices * 2 * kMaxRank;   // in-launch: at most 2 tokens
+constexpr size_t kSyncFinalOffset = kSyncTaggedOffset + kMaxChildren * kGemvTaggedPerChild * 8;
+constexpr size_t kSyncBytes = kSyncFinalOffset + kMaxChildren * 2 * kMaxRank * 8;
 constexpr int kRedMaxTok = 2;                 // redundant V^T x: at most 2 tokens per pass
 constexpr int kRedMaxPieces = 20;             //   and 20 16-byte pieces of V per lane
 constexpr int kRedUnits = 4;                  //   one unit per wave
@@ -91,21 +115,33 @@ struct GemvF {
     const uint16_t *x;    // bf16 [T][d_in]
     uint16_t *y;          // bf16 [T][ldy]
     float *partial;       // slice partials, child c at c * kGemvPartialPerChild: fp32 [S][tt][r_c]
+    unsigned long long *tagged;   // in-launch tagged words, child c at c * kGemvTaggedPerChild: [S][tt][r_c]
     // set from the plan
     int nseg;             // segments per row (1, 2 or 4)
     int S;                // slices of the partials
-    int vmode;            // kVtxNone / kVtxRedundant / kVtxPartials
+    int vmode;            // kVtxNone / kVtxRedundant / kVtxPartials / kVtxInLaunch
     int red_units;        // redundant mode: unit u = rows [red_lo, red_hi) of 16-byte
     int red_c[kRedUnits], red_kc[kRedUnits], red_lo[kRedUnits], red_hi[kRedUnits];   // column red_kc of child red_c
+    // kVtxInLaunch: workgroup p < n_prod of the grid is a producer, slice p % S of
+    // the (p / S)-th child with r > 0 (slice_len inputs per slice, all tt tokens
+    // of the pass) into tagged; the other workgroups are the projection's. sync = the workspace's sync area; spin_limit bounds each
+    // workgroup's wait. n_prod = 0 in the other modes.
+    // two_level: producer 0 also adds the slices up (in the gathers' order) and
+    // publishes complete V^T x words, so that projection workgroups read one
+    // word per item instead of one per (item, slice).
+    int n_prod, slice_len, spin_limit, two_level;
+    unsigned long long *sync;
 };
 struct GemvPlan {
-    int nseg = 1, R = 1, n_wg = 1, S = 0, slice_len = 0, vmode = kVtxNone, red_units = 0;
+    int nseg = 1, R = 1, n_wg = 1, S = 0, slice_len = 0, vmode = kVtxNone, red_units = 0, n_prod = 0, two_level = 0;
     int red_c[kRedUnits] = {0, 0, 0, 0}, red_kc[kRedUnits] = {0, 0, 0, 0};
     int red_lo[kRedUnits] = {0, 0, 0, 0}, red_hi[kRedUnits] = {0, 0, 0, 0};
 };
 int gemv_tokens_per_pass(int d_in, int T);
 int gemv_slice_len(int d_in);
-GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_redundant);
+// allow_redundant: the redundant V^T x mode may be chosen; allow_inlaunch: the
+// in-launch hand-off may replace a separate V^T x launch (at most 2 tokens per pass).
+GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_redundant, bool allow_inlaunch);
 hipError_t launch_gemv(const GemvF &g, const GemvPlan &plan, int tt, hipStream_t stream);
 
 // ---------------------------------------------------------------------------

@@ -22,6 +22,11 @@ import torch
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwl.so")
 
 OP_LINEAR, OP_QKV, OP_MLP = 0, 1, 2
+# The first SYNC_BYTES of a projection workspace are the library's sync area:
+# zero them before the workspace's first use and never write them afterwards
+# (torch.zeros does the first).
+SYNC_BYTES = 203776
+_FALLBACK_WORD = 511   # int64 word of the sync area counting decode workgroups that stopped waiting
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error", 4: "workspace too small"}
 
 
@@ -57,6 +62,8 @@ def _load(path: str = LIBRARY) -> ctypes.CDLL:
         getattr(lib, name).restype = ctypes.c_int
     lib.wl_set_regime.argtypes = [i32]
     lib.wl_set_regime.restype = i32
+    lib.wl_set_spin_limit.argtypes = [i32]
+    lib.wl_set_spin_limit.restype = i32
     lib.wl_status_str.argtypes = [ctypes.c_int]
     lib.wl_status_str.restype = ctypes.c_char_p
     lib.wl_last_error.argtypes = []
@@ -120,7 +127,8 @@ def workspace_bytes(op: int, thetas: list, T: int) -> int:
 
 
 class Workspace:
-    """A device workspace per (device, stream) that grows on demand.
+    """A device workspace per (device, stream) that grows on demand, allocated
+    zeroed (the sync area must start at zero).
 
     Calls on one stream run in order, so they can share one workspace."""
 
@@ -237,6 +245,23 @@ def set_regime(regime: int) -> int:
     if prev < 0:
         raise ValueError(f"regime {regime} is not 0, 1, 2, 3 or 4")
     return prev
+
+
+def set_spin_limit(polls: int) -> int:
+    """Times a decode workgroup reads a group of in-launch V^T x words again
+    before it computes V^T x itself (0: at once); returns the previous setting."""
+    prev = int(lib.wl_set_spin_limit(polls))
+    if prev < 0:
+        raise ValueError(f"spin limit {polls} is negative")
+    return prev
+
+
+def fallback_count(ws: torch.Tensor) -> int:
+    """Decode workgroups, over all calls on workspace ``ws`` so far, whose wait
+    for the in-launch V^T x ran out (a counter in the sync area); waits for the
+    device."""
+    w = _FALLBACK_WORD * 8
+    return int(ws[w:w + 8].view(torch.int64).item())
 
 
 def abi_version() -> int:

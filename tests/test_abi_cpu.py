@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol(wl):
 
 
 def test_abi_version_and_status_strings(wl):
-    assert wl.abi_version() == 3
+    assert wl.abi_version() == 4
     assert wl.lib.wl_status_str(0) == b"ok"
     assert wl.lib.wl_status_str(4) == b"workspace too small"
     assert wl.lib.wl_status_str(99) == b"unknown status"
@@ -194,6 +194,27 @@ def test_regime_switch(wl):
             wl.set_regime(5)
     finally:
         wl.set_regime(prev)
+
+
+def test_spin_limit_switch(wl):
+    prev = wl.set_spin_limit(0)
+    try:
+        assert prev == 4096
+        assert wl.set_spin_limit(7) == 0
+        with pytest.raises(ValueError):
+            wl.set_spin_limit(-1)
+        assert wl.set_spin_limit(7) == 7
+    finally:
+        wl.set_spin_limit(prev)
+
+
+def test_workspace_starts_with_the_sync_area(wl):
+    # Every projection workspace holds the sync area before anything else.
+    for d_in, d_out, r in ((1152, 1152, 32), (64, 8, 0)):
+        th = theta(d_in=d_in, d_out=d_out, r=r)
+        arr = (ctypes.POINTER(wl.Theta) * 1)(ctypes.pointer(th))
+        assert wl.lib.wl_workspace_bytes(0, arr, 1, 1) >= wl.SYNC_BYTES + 256
+    assert wl.SYNC_BYTES == 203776
 
 
 def test_library_resolves_its_own_symbols(wl):
