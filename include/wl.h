@@ -217,7 +217,7 @@ int32_t wl_set_regime(int32_t regime);
 
 /* Bound on the wait of a decode workgroup for the V^T x slices that other
  * workgroups of its launch compute (one to two tokens per pass): the number of
- * times it reads a group of slice words again, default 4096. A workgroup whose wait runs out
+ * times it reads each group of tagged words, default 4096. A workgroup whose wait runs out
  * computes every slice itself, in the same order, so the result does not
  * change; 0 makes every workgroup do so (for tests). Process-wide; returns the
  * previous value, or -1 (and changes nothing) for a negative argument. */

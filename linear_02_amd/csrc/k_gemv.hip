@@ -224,15 +224,15 @@ __device__ __forceinline__ unsigned long long ld_word(const unsigned long long *
 __device__ __forceinline__ float word_value(unsigned long long w) { return __uint_as_float((uint32_t)w); }
 __device__ __forceinline__ bool word_is(unsigned long long w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
 
-// Tagged gathers of a projection workgroup, in the association of the plain
-// ones. Only words of tokens present in the pass (t < tn) are waited for; a
-// word still without this launch's tag is read again, at most spin_limit more
-// times per group. False when some wait ran out (spin_limit 0: at once).
+// Tagged gathers, in the association of the plain ones. Only words of tokens
+// present in the pass (t < tn) are waited for; a group of words with one still
+// lacking this launch's tag is read again, at most `retries` more times. False
+// when some wait ran out.
 
 // Split mapping: thread (item, group) reads its group's words.
 template <int TT>
 __device__ __forceinline__ bool gather_tagged_split(const GemvF &g, int n_items, int n_groups, uint32_t tag,
-                                                    float (&v)[kGroup], int &n) {
+                                                    int retries, float (&v)[kGroup], int &n) {
     int item = threadIdx.x / n_groups;
     const int grp = threadIdx.x - item * n_groups;
     const bool in = item < n_items;
@@ -244,15 +244,18 @@ __device__ __forceinline__ bool gather_tagged_split(const GemvF &g, int n_items,
     const int s0 = grp * kGroup, s1 = min(g.S, s0 + kGroup);
     const bool need = in && g.t0 + t < g.T;
     unsigned long long w[kGroup];
-    bool ok = g.spin_limit > 0;
-    for (int spin = 0; ok; ++spin) {
+    bool ok = false;
+    for (int spin = 0;; ++spin) {
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) w[u] = ld_word(base + (size_t)min(s0 + u, s1 - 1) * (TT * r));
         bool ready = true;
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) ready = ready && (!need || word_is(w[u], tag));
-        if (ready) break;
-        ok = spin < g.spin_limit;
+        if (ready) {
+            ok = true;
+            break;
+        }
+        if (spin >= retries) break;
     }
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) v[u] = word_value(w[u]);
@@ -262,8 +265,9 @@ __device__ __forceinline__ bool gather_tagged_split(const GemvF &g, int n_items,
 
 // Full mapping: thread per item, groups in order, into vs.
 template <int TT>
-__device__ bool gather_tagged_full(const GemvF &g, int n_items, uint32_t tag, float (*vs)[TT][kMaxRank]) {
-    bool ok = g.spin_limit > 0;
+__device__ bool gather_tagged_full(const GemvF &g, int n_items, uint32_t tag, int retries,
+                                   float (*vs)[TT][kMaxRank]) {
+    bool ok = true;
     for (int item = threadIdx.x; item < n_items && ok; item += kThreads) {
         int c, t, k;
         vtx_item(g, TT, item, c, t, k);
@@ -281,7 +285,7 @@ __device__ bool gather_tagged_full(const GemvF &g, int n_items, uint32_t tag, fl
 #pragma unroll
                 for (int u = 0; u < kGroup; ++u) ready = ready && (!need || word_is(w[u], tag));
                 if (ready) break;
-                if (spin >= g.spin_limit) {
+                if (spin >= retries) {
                     ok = false;
                     break;
                 }
@@ -329,15 +333,16 @@ __device__ void vtx_produce(const GemvF &g, float (*red)[TT + 1], uint32_t *tag_
         const unsigned long long w = tag | __float_as_uint(vtx_slice_total<TT>(red, r, t, kk));
         __hip_atomic_store(part + t * r + kk, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (!g.two_level || p != 0) return;
+    if (!g.two_level || p != 0 || g.spin_limit == 0) return;
+    const int retries = g.spin_limit - 1;
 
     const int n_items = vtx_items(g, TT);
     const int n_groups = (g.S + kGroup - 1) / kGroup;
     const bool split = n_items * n_groups <= kThreads;
     float gv[kGroup];
     int gn = 0;
-    const bool got = split ? gather_tagged_split<TT>(g, n_items, n_groups, tag32, gv, gn)
-                           : gather_tagged_full<TT>(g, n_items, tag32, vs);
+    const bool got = split ? gather_tagged_split<TT>(g, n_items, n_groups, tag32, retries, gv, gn)
+                           : gather_tagged_full<TT>(g, n_items, tag32, retries, vs);
     if (__syncthreads_or(!got)) return;   // the projection workgroups will compute V^T x themselves
     if (split) {
         gsum[tid] = gather_finish(gv, gn);
@@ -359,10 +364,10 @@ __device__ void vtx_produce(const GemvF &g, float (*red)[TT + 1], uint32_t *tag_
 }
 
 // Two-level: thread per item reads the complete word (again while it lacks the
-// tag, at most spin_limit more times) into vs.
+// tag, at most `retries` more times) into vs.
 template <int TT>
-__device__ bool gather_final(const GemvF &g, int n_items, uint32_t tag, float (*vs)[TT][kMaxRank]) {
-    bool ok = g.spin_limit > 0;
+__device__ bool gather_final(const GemvF &g, int n_items, uint32_t tag, int retries, float (*vs)[TT][kMaxRank]) {
+    bool ok = true;
     const unsigned long long *fin = final_words(g);
     for (int item = threadIdx.x; item < n_items && ok; item += kThreads) {
         int c, t, k;
@@ -372,7 +377,7 @@ __device__ bool gather_final(const GemvF &g, int n_items, uint32_t tag, float (*
         for (int spin = 0;; ++spin) {
             w = ld_word(fin + item);
             if (!need || word_is(w, tag)) break;
-            if (spin >= g.spin_limit) {
+            if (spin >= retries) {
                 ok = false;
                 break;
             }
@@ -632,9 +637,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
         if (inl) {
             if (tid == 0) tag_lds = ticket_tag(ticket);
             __syncthreads();
-            const bool got = g.two_level ? gather_final<TT>(g, n_items, tag_lds, vs)
-                             : split       ? gather_tagged_split<TT>(g, n_items, n_groups, tag_lds, gv, gn)
-                                           : gather_tagged_full<TT>(g, n_items, tag_lds, vs);
+            const int retries = g.spin_limit - 1;   // spin_limit reads in all; 0: none
+            const bool got = g.spin_limit > 0 &&
+                             (g.two_level ? gather_final<TT>(g, n_items, tag_lds, retries, vs)
+                              : split     ? gather_tagged_split<TT>(g, n_items, n_groups, tag_lds, retries, gv, gn)
+                                          : gather_tagged_full<TT>(g, n_items, tag_lds, retries, vs));
             fallback = __syncthreads_or(!got);
             have = !fallback;
             if (fallback && tid == 0)

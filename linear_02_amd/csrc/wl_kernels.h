@@ -88,7 +88,7 @@ constexpr int kSyncCopies = 64;
 constexpr unsigned long long kSyncStride = 1ull << 24;
 constexpr int kSyncFallbackWord = 511;
 constexpr size_t kSyncTaggedOffset = 4096;
-constexpr int kSpinLimit = 1 << 12;   // re-reads of a group of tagged words before a workgroup computes V^T x itself
+constexpr int kSpinLimit = 1 << 12;   // reads of a group of tagged words before a workgroup computes V^T x itself
 constexpr int kGemvMaxTok = 8;                // tokens per pass
 constexpr int kGemvMaxDin = 32768;            // widest input of the decode kernel
 constexpr int kGemvMaxSlices = 64;

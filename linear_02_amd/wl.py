@@ -248,8 +248,8 @@ def set_regime(regime: int) -> int:
 
 
 def set_spin_limit(polls: int) -> int:
-    """Times a decode workgroup reads a group of in-launch V^T x words again
-    before it computes V^T x itself (0: at once); returns the previous setting."""
+    """Times a decode workgroup reads each group of in-launch V^T x words before
+    it computes V^T x itself (0: at once); returns the previous setting."""
     prev = int(lib.wl_set_spin_limit(polls))
     if prev < 0:
         raise ValueError(f"spin limit {polls} is negative")
