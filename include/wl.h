@@ -205,9 +205,10 @@ wl_status wl_relative_frobenius_error(const void *W, const void *R, int64_t n, d
 
 /* Kernel regime for the projection calls: 0 chooses by token count (the
  * default), 1 forces the decode GEMV wherever it applies (V^T x computed by
- * every workgroup when V is small, else by a separate launch before it), 2
- * forces the matrix-core GEMM, 3 forces the decode GEMV with V^T x always
- * computed by a separate launch (never by workgroups of the same launch), 4 forces the few-token path (split matrix-core
+ * the first workgroups of the same launch at 1 or 2 tokens per pass, else by a
+ * separate launch before it), 2 forces the matrix-core GEMM, 3 forces the
+ * decode GEMV with V^T x always computed by a separate launch, 4 forces the
+ * few-token path (split matrix-core
  * products and an epilogue launch) wherever it applies (T <= 64, d_in <= 8192).
  * Where a forced regime does not apply the matrix-core GEMM runs. Results agree
  * within rounding in every regime; the switch exists for tests and

@@ -6,17 +6,10 @@
 // computes:
 //
 // V^T x ("In-kernel reconstruction", introduction: the inner sum over i of
-//   V[i,k] x[t,i]) reaches the epilogue in one of two ways.
-//   * Redundant (small V, at most 2 tokens): every workgroup reads all of V
-//     (from L2 after the first workgroup) with 16-byte loads issued before the
-//     W0 stream, and reduces it itself after the stream. Each wave owns one
-//     unit (a 16-byte column of V, or a part of one), its lanes walk the rows,
-//     and a wave sum per rank entry finishes the unit; units of one column are
-//     added in part order. No workgroup depends on another.
-//   * Slice partials (otherwise): per-slice partial sums are added in fixed
-//     groups of 16 slices, group sums in order, the same association in every
-//     workgroup and for a child computed alone or with Q/K/V siblings. The
-//     partials come from one of two places:
+//   V[i,k] x[t,i]) reaches the epilogue as per-slice partial sums, added in
+//   fixed groups of 16 slices, group sums in order: the same association in
+//   every workgroup and for a child computed alone or with Q/K/V siblings. The
+//   partials come from one of two places:
 //     - In-launch (at most 2 tokens per pass): the first workgroups of this
 //       launch are producers, one per (child, slice), each computing its slice
 //       as the V^T x launch would. Each partial is stored as one 64-bit word,
@@ -64,10 +57,10 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxRowsG = 8;                 // rows per workgroup: (4 / nseg) * R <= 8
 constexpr int kUPerThread = kMaxRowsG * 2 * kMaxRank / kThreads;
 constexpr int kGroup = 16;                   // slices per group in the partial sums
-#ifndef WL_ONE_LEVEL_MAX_KB
-#define WL_ONE_LEVEL_MAX_KB 3072
+#ifndef WL_ONE_LEVEL_MAX_READS
+#define WL_ONE_LEVEL_MAX_READS 4096
 #endif
-constexpr long long kOneLevelMaxBytes = (long long)WL_ONE_LEVEL_MAX_KB << 10;   // in-launch hand-off, see gemv_plan
+constexpr long long kOneLevelMaxReads = WL_ONE_LEVEL_MAX_READS;   // in-launch hand-off, see gemv_plan
 
 __device__ __forceinline__ int child_index(const GemvF &g, int row) {
     if (g.n_ch > 2 && row >= g.ch[2].col0) return 2;
@@ -306,16 +299,15 @@ __device__ __forceinline__ unsigned long long *final_words(const GemvF &g) {
 
 // Producer workgroup p: slice p % S of child vtx_child(p / S), for the pass's
 // tokens, as the V^T x launch computes it, stored as tagged words. With
-// two_level, producer 0 then gathers every slice as a projection workgroup
-// would (same association, same bits) and stores the complete V^T x as one
-// tagged word per item.
+// two_level, the last producer (dispatched last, so usually the last to finish
+// and the one whose first read finds every word) then gathers every slice as a
+// projection workgroup would (same association, same bits) and stores the
+// complete V^T x as one tagged word per item.
 template <int TT>
 __device__ void vtx_produce(const GemvF &g, float (*red)[TT + 1], uint32_t *tag_lds, float *gsum,
                             float (*vs)[TT][kMaxRank]) {
     const int tid = threadIdx.x, p = blockIdx.x;
     unsigned long long ticket;
-    if (tid == 0) ticket = take_ticket(g);
-    advance_empty_copies(g);
     const int slice = p % g.S, c = vtx_child(g, p / g.S);
     const int r = ch_r(g, c);
     const uint16_t *V = reinterpret_cast<const uint16_t *>(
@@ -323,8 +315,14 @@ __device__ void vtx_produce(const GemvF &g, float (*red)[TT + 1], uint32_t *tag_
     const int i0 = slice * g.slice_len, len = max(0, min(g.d_in - i0, g.slice_len));
     const int tn = min(TT, g.T - g.t0);
     const VtxXGlobal<TT> xg{g.x + (size_t)g.t0 * g.d_in, g.d_in, i0, tn};
+    // The ticket is taken once the V and x loads are issued, so its round trip
+    // overlaps theirs.
+    vtx_slice_sums<TT>(V, r, i0, len, xg, red, [&]() {
+        if (tid == 0) ticket = take_ticket(g);
+    });
+    advance_empty_copies(g);
     if (tid == 0) *tag_lds = ticket_tag(ticket);
-    vtx_slice_sums<TT>(V, r, i0, len, xg, red);   // its barriers publish tag_lds
+    __syncthreads();
     const uint32_t tag32 = *tag_lds;
     const unsigned long long tag = (unsigned long long)tag32 << 32;
     unsigned long long *part = tagged_base(g, c) + (size_t)slice * TT * r;
@@ -333,7 +331,7 @@ __device__ void vtx_produce(const GemvF &g, float (*red)[TT + 1], uint32_t *tag_
         const unsigned long long w = tag | __float_as_uint(vtx_slice_total<TT>(red, r, t, kk));
         __hip_atomic_store(part + t * r + kk, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (!g.two_level || p != 0 || g.spin_limit == 0) return;
+    if (!g.two_level || p != g.n_prod - 1 || g.spin_limit == 0) return;
     const int retries = g.spin_limit - 1;
 
     const int n_items = vtx_items(g, TT);
@@ -431,81 +429,11 @@ __device__ void vtx_fallback(const GemvF &g, int n_items, float (*vs)[TT][kMaxRa
     }
 }
 
-// Redundant V^T x: this lane's 16-byte pieces of its wave's unit, and the
-// matching tokens, loaded before the W0 stream.
-//   r >= 8: piece j is V[j][kc*8 .. kc*8+8), token value x[t][j]
-//   r == 4: piece j is rows 2j and 2j+1 of V (4 entries each), x[t][2j .. 2j+1]
-template <int TT>
-struct RedLoads {
-    u32x4 v[kRedMaxPieces];
-    uint32_t x[kRedMaxPieces][TT];
-};
-
-template <int TT>
-__device__ __forceinline__ void red_issue(const GemvF &g, RedLoads<TT> &rl, int wave, int lane) {
-    if (wave >= g.red_units) return;
-    const Child &c = g.ch[g.red_c[wave]];
-    const int r = c.r, lo = g.red_lo[wave], hi = g.red_hi[wave], kc = g.red_kc[wave];
-#pragma unroll
-    for (int m = 0; m < kRedMaxPieces; ++m) {
-        const int j = lo + lane + kWave * m;
-        const bool in = j < hi;
-        const int jc = in ? j : lo;   // a valid piece; the value is dropped below
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(r >= 8 ? c.V + (size_t)jc * r + kc * 8 : c.V + (size_t)jc * 8);
-        rl.v[m] = in ? v : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            const bool tin = in && g.t0 + t < g.T;
-            const uint16_t *xt = g.x + (size_t)min(g.t0 + t, g.T - 1) * g.d_in;
-            const uint32_t xv = r >= 8 ? (uint32_t)xt[jc] : *reinterpret_cast<const uint32_t *>(xt + 2 * jc);
-            rl.x[m][t] = tin ? xv : 0u;
-        }
-    }
-}
-
-// Reduce the loaded pieces: lane 63 of the wave ends with the unit's sums for
-// its 8 rank slots, stored to upart[wave][slot][t].
-template <int TT>
-__device__ __forceinline__ void red_reduce(const GemvF &g, const RedLoads<TT> &rl, int wave, int lane,
-                                           float (*upart)[8][TT]) {
-    if (wave >= g.red_units) return;
-    const int r = g.ch[g.red_c[wave]].r;
-    float acc[8][TT];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int t = 0; t < TT; ++t) acc[e][t] = 0.f;
-#pragma unroll
-    for (int m = 0; m < kRedMaxPieces; ++m) {
-        const u32x4 v = rl.v[m];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            const uint32_t xv = rl.x[m][t];
-            const float x0 = bf16_f(xv & 0xFFFFu);
-            const float x1 = r >= 8 ? x0 : bf16_f(xv >> 16);   // r == 4: second row of the piece
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float ve = bf16_f(e & 1 ? w[e >> 1] >> 16 : w[e >> 1] & 0xFFFFu);
-                acc[e][t] += ve * (e < 4 ? x0 : x1);
-            }
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            const float s = wave_sum(acc[e][t]);
-            if (lane == kWave - 1) upart[wave][e][t] = s;
-        }
-}
-
-template <int TT, int R, int P, bool RED>
+template <int TT, int R, int P>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     constexpr int NB0 = (TT <= 2 ? 8 : TT == 4 ? 4 : 2) / (R * P);
     constexpr int NB = NB0 > 0 ? NB0 : 1;       // 16-byte loads per row per lane per batch
-    constexpr bool RED_OK = RED && TT <= kRedMaxTok;
-    constexpr bool INL = TT <= 2 && !RED;        // in-launch hand-off (RED instances serve the redundant mode only)
+    constexpr bool INL = TT <= 2;                // in-launch hand-off
     __shared__ float mbuf[kWaves][R][P][TT];
     __shared__ float vred[INL ? kThreads : 1][TT + 1];             // producer / fallback slice sums
     __shared__ float fgs[INL ? kMaxChildren * TT * kMaxRank : 1];  // fallback group sums
@@ -514,7 +442,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     __shared__ float ulds[kMaxRowsG][P][kMaxRank];
     __shared__ float slds[kMaxRowsG][P];
     __shared__ float gsum[kThreads];
-    __shared__ float upart[kWaves][8][TT];
     __shared__ float rterm[kMaxRowsG][P][TT];
 
     // The wave index is uniform: keep it (and what derives from it) in scalar registers.
@@ -522,7 +449,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     const int nch = g.d_in >> 3;
     const int nseg = g.nseg;
     const int rows_g = (kWaves / nseg) * R;
-    const bool red = RED_OK && g.vmode == kVtxRedundant;
     const bool parts = g.vmode == kVtxPartials;
     const bool inl = INL && g.vmode == kVtxInLaunch;
     unsigned long long ticket;   // thread 0 of an in-launch projection workgroup only
@@ -539,9 +465,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
 
     // ---- everything the epilogue needs, issued before the stream ----
     const ChFields cf(g);
-    RedLoads<RED_OK ? TT : 1> rl;
-    if constexpr (RED_OK)
-        if (red) red_issue<TT>(g, rl, wave, lane);
     float upre[kUPerThread];
 #pragma unroll
     for (int u = 0; u < kUPerThread; ++u) {
@@ -656,8 +579,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
         if (item < kMaxRowsG * P * kMaxRank) (&ulds[0][0][0])[item] = upre[u];
     }
     if (tid < rows_g * P) (&slds[0][0])[tid] = spre;
-    if constexpr (RED_OK)
-        if (red) red_reduce<TT>(g, rl, wave, lane, upart);
     if (parts || (have && !g.two_level)) {
         if (split)
             gsum[tid] = gather_finish(gv, gn);
@@ -673,19 +594,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
             for (int j = 0; j < n_groups; ++j) sum += gsum[item * n_groups + j];
             int c, t, k;
             vtx_item(g, TT, item, c, t, k);
-            vs[c][t][k] = sum;
-        }
-    if (red)
-        for (int item = tid; item < n_items; item += kThreads) {
-            // Units of the column holding (c, k), in part order.
-            int c, t, k;
-            vtx_item(g, TT, item, c, t, k);
-            const bool wide = ch_r(g, c) >= 8;
-            const int kc = wide ? k >> 3 : 0, e = wide ? (k & 7) : k;
-            float sum = 0.f;
-            for (int u = 0; u < g.red_units; ++u)
-                if (g.red_c[u] == c && g.red_kc[u] == kc)
-                    sum += wide ? upart[u][e][t] : upart[u][e][t] + upart[u][e + 4][t];
             vs[c][t][k] = sum;
         }
     __syncthreads();
@@ -724,20 +632,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     }
 }
 
-template <int TT, int R, int P, bool RED>
+template <int TT, int R, int P>
 hipError_t launch_tt(const GemvF &g, int n_wg, hipStream_t stream) {
-    hipLaunchKernelGGL((gemv_kernel<TT, R, P, RED>), dim3(n_wg), dim3(kThreads), 0, stream, g);
+    hipLaunchKernelGGL((gemv_kernel<TT, R, P>), dim3(n_wg), dim3(kThreads), 0, stream, g);
     return hipGetLastError();
 }
 
 template <int R, int P>
 hipError_t launch_r(const GemvF &g, int tt, int n_wg, hipStream_t stream) {
-    const bool red = g.vmode == kVtxRedundant;
     switch (tt) {
-        case 8: return launch_tt<8, R, P, false>(g, n_wg, stream);
-        case 4: return launch_tt<4, R, P, false>(g, n_wg, stream);
-        case 2: return red ? launch_tt<2, R, P, true>(g, n_wg, stream) : launch_tt<2, R, P, false>(g, n_wg, stream);
-        default: return red ? launch_tt<1, R, P, true>(g, n_wg, stream) : launch_tt<1, R, P, false>(g, n_wg, stream);
+        case 8: return launch_tt<8, R, P>(g, n_wg, stream);
+        case 4: return launch_tt<4, R, P>(g, n_wg, stream);
+        case 2: return launch_tt<2, R, P>(g, n_wg, stream);
+        default: return launch_tt<1, R, P>(g, n_wg, stream);
     }
 }
 
@@ -761,9 +668,11 @@ int gemv_tokens_per_pass(int d_in, int T) {
     return tt;
 }
 
-namespace {
-
-GemvPlan plan_vtx(const GemvF &g, int tt, bool allow_redundant) {
+// V^T x at 1 or 2 tokens per pass comes from producer workgroups of the same
+// launch (measured faster than every workgroup reading a small V itself, by
+// about 1 µs, and than a separate launch), unless allow_inlaunch is false; then,
+// and above 2 tokens, from a V^T x launch just before.
+GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_inlaunch) {
     GemvPlan p;
     const int nch = g.d_in / 8;
     p.nseg = nch <= 640 ? 1 : nch <= 1280 ? 2 : 4;
@@ -771,67 +680,23 @@ GemvPlan plan_vtx(const GemvF &g, int tt, bool allow_redundant) {
     const int rows_g = (kWaves / p.nseg) * p.R;
     p.n_wg = (g.rows + rows_g - 1) / rows_g;
     p.slice_len = gemv_slice_len(g.d_in);
-    int sum_r = 0;
-    for (int c = 0; c < g.n_ch; ++c) sum_r += g.ch[c].r;
+    int sum_r = 0, n_v = 0;
+    for (int c = 0; c < g.n_ch; ++c) {
+        sum_r += g.ch[c].r;
+        n_v += g.ch[c].r > 0;
+    }
     p.S = sum_r > 0 ? (g.d_in + p.slice_len - 1) / p.slice_len : 0;
     p.vmode = sum_r > 0 ? kVtxPartials : kVtxNone;
-    if (sum_r == 0 || !allow_redundant || tt > kRedMaxTok) return p;
-
-    // Redundant V^T x: every child's rank must be 4 or a multiple of 8, the
-    // columns (16-byte wide, or one for r == 4) at most one per wave, each
-    // lane's share of its unit within kRedMaxPieces pieces, and the re-reads of
-    // V by all workgroups within kRedMaxTraffic bytes (measured: beyond a few MB
-    // they cost more than a separate V^T x launch).
-    if ((long long)p.n_wg * g.d_in * sum_r * 2 > kRedMaxTraffic) return p;
-    int cols = 0;
-    for (int c = 0; c < g.n_ch; ++c) {
-        const int r = g.ch[c].r;
-        if (r == 0) continue;
-        if (r != 4 && r % 8) return p;
-        cols += r >= 8 ? r / 8 : 1;
-    }
-    if (cols > kWaves) return p;
-    const int parts = cols == 1 ? 4 : cols == 2 ? 2 : 1;
-    int u = 0;
-    for (int c = 0; c < g.n_ch; ++c) {
-        const int r = g.ch[c].r;
-        if (r == 0) continue;
-        const int pieces = r >= 8 ? g.d_in : g.d_in / 2;
-        const int per = (pieces + parts - 1) / parts;
-        if ((per + kWave - 1) / kWave > kRedMaxPieces) return p;
-        for (int kc = 0; kc < (r >= 8 ? r / 8 : 1); ++kc)
-            for (int q = 0; q < parts; ++q) {
-                p.red_c[u] = c;
-                p.red_kc[u] = kc;
-                p.red_lo[u] = q * per;
-                p.red_hi[u] = min(pieces, (q + 1) * per);
-                ++u;
-            }
-    }
-    p.red_units = u;
-    p.vmode = kVtxRedundant;
-    return p;
-}
-
-}  // namespace
-
-GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_redundant, bool allow_inlaunch) {
-    GemvPlan p = plan_vtx(g, tt, allow_redundant);
-    if (p.vmode != kVtxPartials || !allow_inlaunch || tt > 2) return p;
-    int n_v = 0;
-    for (int c = 0; c < g.n_ch; ++c) n_v += g.ch[c].r > 0;
-    const int n_prod = p.S * n_v;
+    if (sum_r == 0 || !allow_inlaunch || tt > 2) return p;
     p.vmode = kVtxInLaunch;
-    p.n_prod = n_prod;
-    // One level: every projection workgroup reads every slice word, device-scope
-    // reads that miss L2 and all fall on the same few lines. Measured on the
-    // Gemma-3-1B-shaped layer: up to 2.7 MB of such reads per launch (Q/K/V at
-    // 2 tokens) one level is faster; from 4 MB (gate/up at 1 token) the extra
-    // step of two levels costs less than the reads it saves.
-    int sum_r = 0;
-    for (int c = 0; c < g.n_ch; ++c) sum_r += g.ch[c].r;
-    const long long one_level_bytes = (long long)p.n_wg * tt * sum_r * p.S * 8;
-    p.two_level = one_level_bytes > kOneLevelMaxBytes;
+    p.n_prod = p.S * n_v;
+    // One level: every projection workgroup reads the words of every slice,
+    // device-scope reads that miss L2 and all fall on the same few lines.
+    // Measured on the Gemma-3-1B-shaped layer at ranks 4, 16 and 32, 1 and 2
+    // tokens: one level is faster for Q/K/V and O (1,152 to 1,728 workgroup x
+    // slice reads per launch), two levels for gate/up and down (7,776 and
+    // 31,104), whatever the bytes read.
+    p.two_level = (long long)p.n_wg * p.S > kOneLevelMaxReads;
     return p;
 }
 
@@ -840,16 +705,9 @@ hipError_t launch_gemv(const GemvF &g, const GemvPlan &plan, int tt, hipStream_t
     a.nseg = plan.nseg;
     a.S = plan.S;
     a.vmode = plan.vmode;
-    a.red_units = plan.red_units;
     a.n_prod = plan.vmode == kVtxInLaunch ? plan.n_prod : 0;
     a.two_level = plan.two_level;
     a.slice_len = plan.slice_len;
-    for (int u = 0; u < kWaves; ++u) {
-        a.red_c[u] = plan.red_c[u];
-        a.red_kc[u] = plan.red_kc[u];
-        a.red_lo[u] = plan.red_lo[u];
-        a.red_hi[u] = plan.red_hi[u];
-    }
     const int n_wg = plan.n_wg + a.n_prod;   // producers first
     if (g.pair) {
         if (plan.R == 2) return launch_r<2, 2>(a, tt, n_wg, stream);

@@ -355,7 +355,7 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
         g.sync = reinterpret_cast<unsigned long long *>(ws);   // the sync area at offset 0
         g.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
         const bool separate = g_regime.load(std::memory_order_relaxed) == 3;
-        const wl::GemvPlan plan = wl::gemv_plan(g, tt, !separate, !separate);
+        const wl::GemvPlan plan = wl::gemv_plan(g, tt, !separate);
         auto part = [&](int c) { return g.partial + (size_t)c * wl::kGemvPartialPerChild; };
         for (int t0 = 0; t0 < T && e == hipSuccess; t0 += tt) {
             g.t0 = t0;

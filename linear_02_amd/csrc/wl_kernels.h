@@ -65,15 +65,15 @@ hipError_t launch_vtx(const VtxJob &job, hipStream_t stream);
 // over the concatenated rows of up to three children. Pair mode (the MLP's
 // gate/up): ch[0] = gate, ch[1] = up with equal shapes, and
 //   y[t][o] = bf16( gelu_tanh(gate value) * up value ).
-// vtx comes either from every workgroup reading V itself (kVtxRedundant) or
-// from slice partials written by a V^T x launch just before (kVtxPartials).
+// vtx comes from slice partials written by a V^T x launch just before
+// (kVtxPartials) or by the first workgroups of the same launch (kVtxInLaunch).
 // kVtxInLaunch: the slice partials are computed by the first n_prod workgroups of
 // the projection's own launch and stored as tagged 64-bit words (the launch's
 // tag beside the value); the other workgroups stream W0, then read the words
 // until each carries their launch's tag (bounded). The tag comes from ticket
 // counters in the workspace's sync area (see kSyncBytes), which also holds the
 // words, so no word is ever reset. A workgroup whose wait runs out computes V^T x itself.
-enum { kVtxNone = 0, kVtxRedundant = 1, kVtxPartials = 2, kVtxInLaunch = 3 };
+enum { kVtxNone = 0, kVtxPartials = 2, kVtxInLaunch = 3 };
 // The sync area, the first kSyncBytes of every workspace, 64-bit words:
 //   [0, kSyncCopies)          ticket counters, each advanced by exactly
 //                             kSyncStride per launch that hands V^T x over
@@ -96,13 +96,6 @@ constexpr size_t kGemvPartialPerChild = (size_t)kGemvMaxSlices * kGemvMaxTok * k
 constexpr size_t kGemvTaggedPerChild = (size_t)kGemvMaxSlices * 2 * kMaxRank;   // in-launch: at most 2 tokens
 constexpr size_t kSyncFinalOffset = kSyncTaggedOffset + kMaxChildren * kGemvTaggedPerChild * 8;
 constexpr size_t kSyncBytes = kSyncFinalOffset + kMaxChildren * 2 * kMaxRank * 8;
-constexpr int kRedMaxTok = 2;                 // redundant V^T x: at most 2 tokens per pass
-constexpr int kRedMaxPieces = 20;             //   and 20 16-byte pieces of V per lane
-constexpr int kRedUnits = 4;                  //   one unit per wave
-#ifndef WL_RED_CAP_MB
-#define WL_RED_CAP_MB 4
-#endif
-constexpr long long kRedMaxTraffic = (long long)WL_RED_CAP_MB << 20;  //   V re-read by all workgroups
 
 struct GemvF {
     Child ch[kMaxChildren];
@@ -119,29 +112,25 @@ struct GemvF {
     // set from the plan
     int nseg;             // segments per row (1, 2 or 4)
     int S;                // slices of the partials
-    int vmode;            // kVtxNone / kVtxRedundant / kVtxPartials / kVtxInLaunch
-    int red_units;        // redundant mode: unit u = rows [red_lo, red_hi) of 16-byte
-    int red_c[kRedUnits], red_kc[kRedUnits], red_lo[kRedUnits], red_hi[kRedUnits];   // column red_kc of child red_c
+    int vmode;            // kVtxNone / kVtxPartials / kVtxInLaunch
     // kVtxInLaunch: workgroup p < n_prod of the grid is a producer, slice p % S of
     // the (p / S)-th child with r > 0 (slice_len inputs per slice, all tt tokens
     // of the pass) into tagged; the other workgroups are the projection's. sync = the workspace's sync area; spin_limit bounds each
     // workgroup's wait. n_prod = 0 in the other modes.
-    // two_level: producer 0 also adds the slices up (in the gathers' order) and
+    // two_level: the last producer also adds the slices up (in the gathers' order) and
     // publishes complete V^T x words, so that projection workgroups read one
     // word per item instead of one per (item, slice).
     int n_prod, slice_len, spin_limit, two_level;
     unsigned long long *sync;
 };
 struct GemvPlan {
-    int nseg = 1, R = 1, n_wg = 1, S = 0, slice_len = 0, vmode = kVtxNone, red_units = 0, n_prod = 0, two_level = 0;
-    int red_c[kRedUnits] = {0, 0, 0, 0}, red_kc[kRedUnits] = {0, 0, 0, 0};
-    int red_lo[kRedUnits] = {0, 0, 0, 0}, red_hi[kRedUnits] = {0, 0, 0, 0};
+    int nseg = 1, R = 1, n_wg = 1, S = 0, slice_len = 0, vmode = kVtxNone, n_prod = 0, two_level = 0;
 };
 int gemv_tokens_per_pass(int d_in, int T);
 int gemv_slice_len(int d_in);
-// allow_redundant: the redundant V^T x mode may be chosen; allow_inlaunch: the
-// in-launch hand-off may replace a separate V^T x launch (at most 2 tokens per pass).
-GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_redundant, bool allow_inlaunch);
+// allow_inlaunch: the in-launch hand-off may replace a separate V^T x launch
+// (at most 2 tokens per pass).
+GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_inlaunch);
 hipError_t launch_gemv(const GemvF &g, const GemvPlan &plan, int tt, hipStream_t stream);
 
 // ---------------------------------------------------------------------------

@@ -12,16 +12,24 @@ namespace wl {
 
 constexpr int kVtxSliceThreads = 256;
 
-// Per-thread sums, then stored to red[tid][t]. Thread (g, k), with rp the
-// smallest power of two >= r and G = 256 / rp, sums rows g, g + G, ... of the
-// slice for rank column k; the loads of 16 rows are issued before any of them
-// is used. Every address is valid (rows clamped into the slice) and the values
-// are masked afterwards, so the 16 rows' loads are all in flight at once.
+// Thread (g, k), with rp the smallest power of two >= r and G = 256 / rp, sums
+// rows g, g + G, ... of the slice for rank column k; the loads of 16 rows are
+// issued before any of them is used. Every address is valid (rows clamped into
+// the slice) and the values are masked afterwards, so the 16 rows' loads are
+// all in flight at once. The groups of one wave are then added by an xor
+// butterfly over the lanes of column k (a + b = b + a, so every lane ends with
+// the same bits), and the wave sums stored to red for vtx_slice_total, which
+// adds the four waves in order.
 // x_at(ic, t) returns x[t][i0 + ic] as fp32 (0 for absent tokens).
+// issued() runs once in every thread, right after the first 16 rows' loads are
+// issued (a caller's own memory operation issued there overlaps them).
 // Ends with a barrier; begins with one, so red may be reused right away.
-template <int TB, class XAt>
+struct NoHook {
+    __device__ __forceinline__ void operator()() const {}
+};
+template <int TB, class XAt, class Hook = NoHook>
 __device__ __forceinline__ void vtx_slice_sums(const uint16_t *__restrict__ V, int r, int i0, int len, XAt x_at,
-                                               float (*red)[TB + 1]) {
+                                               float (*red)[TB + 1], Hook issued = Hook()) {
     const int tid = threadIdx.x;
     int rp = 1;
     while (rp < r) rp <<= 1;
@@ -29,40 +37,54 @@ __device__ __forceinline__ void vtx_slice_sums(const uint16_t *__restrict__ V, i
     float acc[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t) acc[t] = 0.f;
-    if (k < r) {
-        for (int ib = g; ib < len; ib += 16 * G) {
-            float v[16], xv[16][TB];
+    auto rows16 = [&](int ib, bool first) {
+        float v[16], xv[16][TB];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int i = ib + u * G;
-                const bool in = i < len;
-                const int ic = min(i, len - 1);
-                const float vv = bf16_f(V[(size_t)(i0 + ic) * r + k]);
-                v[u] = in ? vv : 0.f;
+        for (int u = 0; u < 16; ++u) {
+            const int i = ib + u * G;
+            const bool in = i < len;
+            const int ic = min(i, len - 1);
+            const float vv = bf16_f(V[(size_t)(i0 + ic) * r + k]);
+            v[u] = in ? vv : 0.f;
 #pragma unroll
-                for (int t = 0; t < TB; ++t) xv[u][t] = x_at(ic, t);
-            }
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-#pragma unroll
-                for (int t = 0; t < TB; ++t) acc[t] += v[u] * xv[u][t];
+            for (int t = 0; t < TB; ++t) xv[u][t] = x_at(ic, t);
         }
-    }
-    __syncthreads();
+        if (first) issued();
 #pragma unroll
-    for (int t = 0; t < TB; ++t) red[tid][t] = acc[t];
+        for (int u = 0; u < 16; ++u)
+#pragma unroll
+            for (int t = 0; t < TB; ++t) acc[t] += v[u] * xv[u][t];
+    };
+    // The first 16 rows outside the loop: a loop header makes the compiler wait
+    // for every earlier memory operation (a caller's atomic, say) before these
+    // loads are issued.
+    if (k < r && g < len) {
+        rows16(g, true);
+        for (int ib = g + 16 * G; ib < len; ib += 16 * G) rows16(ib, false);
+    } else {
+        issued();
+    }
+    for (int off = rp; off < kWave; off <<= 1)
+#pragma unroll
+        for (int t = 0; t < TB; ++t) acc[t] += __shfl_xor(acc[t], off);
+    __syncthreads();
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    float *r1 = &red[0][0];   // [4 waves][64 columns][TB] within red
+    if (lane < rp)
+#pragma unroll
+        for (int t = 0; t < TB; ++t) r1[(wave * kWave + lane) * TB + t] = acc[t];
     __syncthreads();
 }
 
-// The slice's partial sum for (t, kk) after vtx_slice_sums: the G group sums
-// of column kk added in group order.
+// The slice's partial sum for (t, kk) after vtx_slice_sums: the four wave sums
+// of column kk added in wave order.
 template <int TB>
 __device__ __forceinline__ float vtx_slice_total(const float (*red)[TB + 1], int r, int t, int kk) {
-    int rp = 1;
-    while (rp < r) rp <<= 1;
-    const int G = kVtxSliceThreads / rp;
+    (void)r;
+    const float *r1 = &red[0][0];
     float sum = 0.f;
-    for (int gg = 0; gg < G; ++gg) sum += red[gg * rp + kk][t];
+#pragma unroll
+    for (int w = 0; w < kVtxSliceThreads / kWave; ++w) sum += r1[(w * kWave + kk) * TB + t];
     return sum;
 }
 

@@ -67,9 +67,8 @@ def slices(d_in: int) -> int:
 
 
 def two_level(d_in: int, rows: int, T: int, sum_r: int) -> bool:
-    """The plan's choice: two levels once one level would make every projection
-    workgroup read more than 3 MiB of slice words in all."""
-    return consumer_workgroups(d_in, rows) * T * sum_r * slices(d_in) * 8 > 3 << 20
+    """The plan's choice: two levels once projection workgroups x slices exceeds 4096."""
+    return consumer_workgroups(d_in, rows) * slices(d_in) > 4096
 
 
 # op, shapes, ranks. Every projection here takes the hand-off route (its V is
