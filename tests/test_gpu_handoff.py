@@ -71,8 +71,8 @@ def two_level(d_in: int, rows: int, T: int, sum_r: int) -> bool:
     return consumer_workgroups(d_in, rows) * slices(d_in) > 4096
 
 
-# op, shapes, ranks. Every projection here takes the hand-off route (its V is
-# too large, or its rank unsuited, for every workgroup to read V itself).
+# op, shapes, ranks: one and two levels, ragged and tiny grids, ranks 1 to 64,
+# children without the low-rank term, the most producers one launch takes.
 CASES = [
     ("linear", (1152, 1152), (32,)),
     ("linear", (6912, 1152), (32,)),          # 54 slices, rows in two segments
