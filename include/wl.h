@@ -91,7 +91,7 @@ extern "C" {
 #define WL_ABI_VERSION 4
 
 /* Bytes at the start of a projection workspace that hold the sync area. */
-#define WL_SYNC_BYTES 203776
+#define WL_SYNC_BYTES 403456
 
 typedef enum {
     WL_OK = 0,
@@ -205,7 +205,7 @@ wl_status wl_relative_frobenius_error(const void *W, const void *R, int64_t n, d
 
 /* Kernel regime for the projection calls: 0 chooses by token count (the
  * default), 1 forces the decode GEMV wherever it applies (V^T x computed by
- * the first workgroups of the same launch at 1 or 2 tokens per pass, else by a
+ * the first workgroups of the same launch at 1 to 4 tokens per pass, else by a
  * separate launch before it), 2 forces the matrix-core GEMM, 3 forces the
  * decode GEMV with V^T x always computed by a separate launch, 4 forces the
  * few-token path (split matrix-core
@@ -217,7 +217,7 @@ wl_status wl_relative_frobenius_error(const void *W, const void *R, int64_t n, d
 int32_t wl_set_regime(int32_t regime);
 
 /* Bound on the wait of a decode workgroup for the V^T x slices that other
- * workgroups of its launch compute (one to two tokens per pass): the number of
+ * workgroups of its launch compute (one to four tokens per pass): the number of
  * times it reads each group of tagged words, default 4096. A workgroup whose wait runs out
  * computes every slice itself, in the same order, so the result does not
  * change; 0 makes every workgroup do so (for tests). Process-wide; returns the

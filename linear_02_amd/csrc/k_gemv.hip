@@ -10,7 +10,7 @@
 //   fixed groups of 16 slices, group sums in order: the same association in
 //   every workgroup and for a child computed alone or with Q/K/V siblings. The
 //   partials come from one of two places:
-//     - In-launch (at most 2 tokens per pass): the first workgroups of this
+//     - In-launch (at most 4 tokens per pass): the first workgroups of this
 //       launch are producers, one per (child, slice), each computing its slice
 //       as the V^T x launch would. Each partial is stored as one 64-bit word,
 //       the launch's tag (generation + 1, from a ticket counter) beside the
@@ -297,6 +297,38 @@ __device__ __forceinline__ unsigned long long *final_words(const GemvF &g) {
     return g.sync + kSyncFinalOffset / 8;
 }
 
+// One slice's x for the producers and the fallback. Up to 2 tokens: read
+// straight from global memory with the V loads. More: staged in LDS first
+// (xs: TT x kXStageMax bf16, absent tokens zero), as the V^T x launch does, so
+// that the x values held in registers stay few. The values, and so the bits of
+// the sums, are the same either way.
+constexpr int kXStageMax = 512;   // >= every slice length of the decode kernel (d_in <= 32768, <= 64 slices)
+template <int TT>
+__device__ __forceinline__ void stage_x(const GemvF &g, int i0, int len, int tn, u32x4 *xs) {
+    if constexpr (TT > 2) {
+        const int nchunk = len >> 3, row_chunks = g.d_in >> 3;
+        const u32x4 *xg = reinterpret_cast<const u32x4 *>(g.x);
+        for (int idx = threadIdx.x; idx < TT * nchunk; idx += kThreads) {
+            const int t = idx / nchunk, j = idx - t * nchunk;
+            xs[t * (kXStageMax / 8) + j] =
+                t < tn ? xg[(size_t)(g.t0 + t) * row_chunks + (i0 >> 3) + j] : u32x4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+    }
+}
+template <int TT, class Hook = NoHook>
+__device__ __forceinline__ void slice_sums(const GemvF &g, const uint16_t *V, int r, int i0, int len, int tn,
+                                           const u32x4 *xs, float (*red)[TT + 1], Hook hook = Hook()) {
+    if constexpr (TT > 2) {
+        const uint16_t *x16 = reinterpret_cast<const uint16_t *>(xs);
+        vtx_slice_sums<TT>(V, r, i0, len, [&](int ic, int t) { return bf16_f(x16[t * kXStageMax + ic]); }, red,
+                           hook);
+    } else {
+        const VtxXGlobal<TT> xg{g.x + (size_t)g.t0 * g.d_in, g.d_in, i0, tn};
+        vtx_slice_sums<TT>(V, r, i0, len, xg, red, hook);
+    }
+}
+
 // Producer workgroup p: slice p % S of child vtx_child(p / S), for the pass's
 // tokens, as the V^T x launch computes it, stored as tagged words. With
 // two_level, the last producer (dispatched last, so usually the last to finish
@@ -304,7 +336,7 @@ __device__ __forceinline__ unsigned long long *final_words(const GemvF &g) {
 // projection workgroup would (same association, same bits) and stores the
 // complete V^T x as one tagged word per item.
 template <int TT>
-__device__ void vtx_produce(const GemvF &g, float (*red)[TT + 1], uint32_t *tag_lds, float *gsum,
+__device__ void vtx_produce(const GemvF &g, float (*red)[TT + 1], u32x4 *xs, uint32_t *tag_lds, float *gsum,
                             float (*vs)[TT][kMaxRank]) {
     const int tid = threadIdx.x, p = blockIdx.x;
     unsigned long long ticket;
@@ -314,10 +346,10 @@ __device__ void vtx_produce(const GemvF &g, float (*red)[TT + 1], uint32_t *tag_
         blend3(c, (uint64_t)g.ch[0].V, (uint64_t)g.ch[1].V, (uint64_t)g.ch[2].V));
     const int i0 = slice * g.slice_len, len = max(0, min(g.d_in - i0, g.slice_len));
     const int tn = min(TT, g.T - g.t0);
-    const VtxXGlobal<TT> xg{g.x + (size_t)g.t0 * g.d_in, g.d_in, i0, tn};
-    // The ticket is taken once the V and x loads are issued, so its round trip
+    stage_x<TT>(g, i0, len, tn, xs);
+    // The ticket is taken once the V (and x) loads are issued, so its round trip
     // overlaps theirs.
-    vtx_slice_sums<TT>(V, r, i0, len, xg, red, [&]() {
+    slice_sums<TT>(g, V, r, i0, len, tn, xs, red, [&]() {
         if (tid == 0) ticket = take_ticket(g);
     });
     advance_empty_copies(g);
@@ -391,7 +423,7 @@ __device__ bool gather_final(const GemvF &g, int n_items, uint32_t tag, int retr
 // gathers pad a short group, group sums in order from 0). gs: LDS, n_items floats.
 template <int TT>
 __device__ void vtx_fallback(const GemvF &g, int n_items, float (*vs)[TT][kMaxRank], float (*red)[TT + 1],
-                             float *gs) {
+                             u32x4 *xs, float *gs) {
     const int tid = threadIdx.x;
     for (int item = tid; item < n_items; item += kThreads) {
         int c, t, k;
@@ -403,13 +435,13 @@ __device__ void vtx_fallback(const GemvF &g, int n_items, float (*vs)[TT][kMaxRa
     const int tn = min(TT, g.T - g.t0);
     for (int s = 0; s < g.S; ++s) {
         const int i0 = s * g.slice_len, len = max(0, min(g.d_in - i0, g.slice_len));
-        const VtxXGlobal<TT> xg{g.x + (size_t)g.t0 * g.d_in, g.d_in, i0, tn};
+        stage_x<TT>(g, i0, len, tn, xs);   // the previous slice's reads ended before its sums' barriers
         for (int j = 0; j < n_v; ++j) {
             const int c = vtx_child(g, j);
             const int r = ch_r(g, c);
             const uint16_t *V = reinterpret_cast<const uint16_t *>(
                 blend3(c, (uint64_t)g.ch[0].V, (uint64_t)g.ch[1].V, (uint64_t)g.ch[2].V));
-            vtx_slice_sums<TT>(V, r, i0, len, xg, red);   // begins and ends with a barrier
+            slice_sums<TT>(g, V, r, i0, len, tn, xs, red);   // begins and ends with a barrier
             for (int item = tid; item < n_items; item += kThreads) {
                 int cc, t, k;
                 vtx_item(g, TT, item, cc, t, k);
@@ -433,11 +465,12 @@ template <int TT, int R, int P>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     constexpr int NB0 = (TT <= 2 ? 8 : TT == 4 ? 4 : 2) / (R * P);
     constexpr int NB = NB0 > 0 ? NB0 : 1;       // 16-byte loads per row per lane per batch
-    constexpr bool INL = TT <= 2;                // in-launch hand-off
+    constexpr bool INL = TT <= kInLaunchMaxTok;  // in-launch hand-off
     __shared__ float mbuf[kWaves][R][P][TT];
     __shared__ float vred[INL ? kThreads : 1][TT + 1];             // producer / fallback slice sums
     __shared__ float fgs[INL ? kMaxChildren * TT * kMaxRank : 1];  // fallback group sums
     __shared__ uint32_t tag_lds;
+    __shared__ u32x4 xstage[INL && TT > 2 ? TT * kXStageMax / 8 : 1];   // producer / fallback x slice
     __shared__ float vs[kMaxChildren][TT][kMaxRank];
     __shared__ float ulds[kMaxRowsG][P][kMaxRank];
     __shared__ float slds[kMaxRowsG][P];
@@ -455,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     if constexpr (INL) {
         if (inl) {
             if ((int)blockIdx.x < g.n_prod) {
-                vtx_produce<TT>(g, vred, &tag_lds, gsum, vs);
+                vtx_produce<TT>(g, vred, xstage, &tag_lds, gsum, vs);
                 return;
             }
             if (tid == 0) ticket = take_ticket(g);   // used after the stream
@@ -586,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
             gather_full(g, n_items, vs);
     }
     if constexpr (INL)
-        if (fallback) vtx_fallback<TT>(g, n_items, vs, vred, fgs);
+        if (fallback) vtx_fallback<TT>(g, n_items, vs, vred, xstage, fgs);
     __syncthreads();
     if ((parts || (have && !g.two_level)) && split)
         for (int item = tid; item < n_items; item += kThreads) {
@@ -668,7 +701,7 @@ int gemv_tokens_per_pass(int d_in, int T) {
     return tt;
 }
 
-// V^T x at 1 or 2 tokens per pass comes from producer workgroups of the same
+// V^T x at 1 to 4 tokens per pass comes from producer workgroups of the same
 // launch (measured faster than every workgroup reading a small V itself, by
 // about 1 µs, and than a separate launch), unless allow_inlaunch is false; then,
 // and above 2 tokens, from a V^T x launch just before.
@@ -687,7 +720,7 @@ GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_inlaunch) {
     }
     p.S = sum_r > 0 ? (g.d_in + p.slice_len - 1) / p.slice_len : 0;
     p.vmode = sum_r > 0 ? kVtxPartials : kVtxNone;
-    if (sum_r == 0 || !allow_inlaunch || tt > 2) return p;
+    if (sum_r == 0 || !allow_inlaunch || tt > kInLaunchMaxTok) return p;
     p.vmode = kVtxInLaunch;
     p.n_prod = p.S * n_v;
     // One level: every projection workgroup reads the words of every slice,

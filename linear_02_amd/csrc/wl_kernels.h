@@ -93,9 +93,13 @@ constexpr int kGemvMaxTok = 8;                // tokens per pass
 constexpr int kGemvMaxDin = 32768;            // widest input of the decode kernel
 constexpr int kGemvMaxSlices = 64;
 constexpr size_t kGemvPartialPerChild = (size_t)kGemvMaxSlices * kGemvMaxTok * kMaxRank;
-constexpr size_t kGemvTaggedPerChild = (size_t)kGemvMaxSlices * 2 * kMaxRank;   // in-launch: at most 2 tokens
+// The in-launch hand-off serves passes of up to kInLaunchMaxTok tokens (measured:
+// at 8 tokens the producer code's registers cost the MLP kernels more than the
+// separate V^T x launch it saves).
+constexpr int kInLaunchMaxTok = 4;
+constexpr size_t kGemvTaggedPerChild = (size_t)kGemvMaxSlices * kInLaunchMaxTok * kMaxRank;
 constexpr size_t kSyncFinalOffset = kSyncTaggedOffset + kMaxChildren * kGemvTaggedPerChild * 8;
-constexpr size_t kSyncBytes = kSyncFinalOffset + kMaxChildren * 2 * kMaxRank * 8;
+constexpr size_t kSyncBytes = kSyncFinalOffset + kMaxChildren * kInLaunchMaxTok * kMaxRank * 8;
 
 struct GemvF {
     Child ch[kMaxChildren];
@@ -129,7 +133,7 @@ struct GemvPlan {
 int gemv_tokens_per_pass(int d_in, int T);
 int gemv_slice_len(int d_in);
 // allow_inlaunch: the in-launch hand-off may replace a separate V^T x launch
-// (at most 2 tokens per pass).
+// (at most kInLaunchMaxTok tokens per pass).
 GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_inlaunch);
 hipError_t launch_gemv(const GemvF &g, const GemvPlan &plan, int tt, hipStream_t stream);
 

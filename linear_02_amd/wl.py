@@ -25,7 +25,7 @@ OP_LINEAR, OP_QKV, OP_MLP = 0, 1, 2
 # The first SYNC_BYTES of a projection workspace are the library's sync area:
 # zero them before the workspace's first use and never write them afterwards
 # (torch.zeros does the first).
-SYNC_BYTES = 203776
+SYNC_BYTES = 403456
 _FALLBACK_WORD = 511   # int64 word of the sync area counting decode workgroups that stopped waiting
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error", 4: "workspace too small"}
 

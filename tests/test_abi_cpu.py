@@ -214,7 +214,7 @@ def test_workspace_starts_with_the_sync_area(wl):
         th = theta(d_in=d_in, d_out=d_out, r=r)
         arr = (ctypes.POINTER(wl.Theta) * 1)(ctypes.pointer(th))
         assert wl.lib.wl_workspace_bytes(0, arr, 1, 1) >= wl.SYNC_BYTES + 256
-    assert wl.SYNC_BYTES == 203776
+    assert wl.SYNC_BYTES == 403456
 
 
 def test_library_resolves_its_own_symbols(wl):

@@ -1,4 +1,4 @@
-"""The decode kernel's in-launch V^T x hand-off (one or two tokens per pass).
+"""The decode kernel's in-launch V^T x hand-off (one to four tokens per pass).
 
 Producer workgroups of the projection's own launch compute the V^T x slices
 and publish them through the workspace's sync area; the other workgroups wait
@@ -51,7 +51,7 @@ def sync_words(ws: torch.Tensor) -> np.ndarray:
     return ws[:4096].view(torch.int64).cpu().numpy()
 
 
-FINAL_OFFSET = 4096 + 3 * 64 * 2 * 64 * 8    # complete V^T x words of the two-level hand-off
+FINAL_OFFSET = 4096 + 3 * 64 * 4 * 64 * 8    # complete V^T x words of the two-level hand-off
 
 
 def final_tags(ws: torch.Tensor, n_items: int) -> np.ndarray:
@@ -125,7 +125,7 @@ def oracle(op, ths, x):
     return y, b
 
 
-@pytest.mark.parametrize("T", [1, 2])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_handoff_fallback_and_separate_launch_agree(wl, case, T):
     op, shape, ranks = CASES[case]
