@@ -13,9 +13,10 @@
  * ---------------------------------------
  * Memory.    Every tensor pointer is a DEVICE pointer on the current HIP device.
  *            The caller allocates and owns every buffer, including the
- *            workspace; the library never allocates or frees memory and keeps
- *            no per-call state (its only global state is the regime switch
- *            below).
+ *            workspace; the library never allocates or frees memory. What
+ *            carries from call to call lives in the caller's workspace (its
+ *            sync area, below); the library's own global state is two
+ *            process-wide switches for tests and measurements (wl_testing.h).
  * Layout.    All tensors are row-major and contiguous:
  *              W0 [d_out][d_in]   s fp32 [d_out]
  *              U  [d_out][r]      V [d_in][r]
@@ -50,18 +51,20 @@
  *            device surface at the caller's next synchronization.
  * Workspace. Operations that take `ws` need at least wl_workspace_bytes(...)
  *            bytes of device memory. For wl_linear, wl_qkv_fused and
- *            wl_mlp_fused its first WL_SYNC_BYTES bytes are a sync area
- *            (counters and generation-tagged words by which the decode
- *            kernel's workgroups hand V^T x to each other within one launch,
- *            "In-kernel reconstruction"): the caller zeroes them
- *            once, before the workspace's first use, and does not write them
- *            afterwards; the calls keep them consistent from then on. A sync
- *            area holding anything else can make results wrong. Bytes 4088
- *            to 4095 of the area count (int64) the decode workgroups that
- *            stopped waiting and computed V^T x themselves (a diagnostic; the
- *            result is the same). The rest of the workspace is scratch whose
- *            contents on entry do not matter. Calls that can run at the same
- *            time (different streams) must not share a workspace.
+ *            wl_mlp_fused its first WL_SYNC_BYTES bytes are a sync area:
+ *            ticket counters and generation-tagged 64-bit words by which the
+ *            workgroups of one decode launch hand each other V^T x and partial
+ *            outputs ("In-kernel reconstruction", the custom-op path: V^T x
+ *            formed once and shared). Before a workspace's first use, and after
+ *            anything other than these calls has written its first
+ *            WL_SYNC_BYTES, the caller runs wl_workspace_init on it (a kernel,
+ *            so it may be captured in a graph); the calls keep the area
+ *            consistent from then on. Bytes 4088 to 4095 of the area count
+ *            (int64) the decode workgroups that stopped waiting and computed
+ *            V^T x themselves (a diagnostic; the result is the same). The rest
+ *            of the workspace is scratch whose contents on entry do not matter.
+ *            Calls that can run at the same time (different streams) must not
+ *            share a workspace.
  * Errors.    Every argument is checked on the host before anything is
  *            enqueued; a fused operation checks all of its thetas first, so an
  *            invalid argument never leaves a partial launch.
@@ -88,10 +91,10 @@
 extern "C" {
 #endif
 
-#define WL_ABI_VERSION 4
+#define WL_ABI_VERSION 5
 
 /* Bytes at the start of a projection workspace that hold the sync area. */
-#define WL_SYNC_BYTES 403456
+#define WL_SYNC_BYTES 9502720
 
 typedef enum {
     WL_OK = 0,
@@ -203,26 +206,17 @@ size_t wl_rel_frob_workspace_bytes(int64_t n);
 wl_status wl_relative_frobenius_error(const void *W, const void *R, int64_t n, double *result,
                                       void *ws, size_t ws_bytes, void *hip_stream);
 
-/* Kernel regime for the projection calls: 0 chooses by token count (the
- * default), 1 forces the decode GEMV wherever it applies (V^T x computed by
- * the first workgroups of the same launch at 1 to 4 tokens per pass, else by a
- * separate launch before it), 2 forces the matrix-core GEMM, 3 forces the
- * decode GEMV with V^T x always computed by a separate launch, 4 forces the
- * few-token path (split matrix-core
- * products and an epilogue launch) wherever it applies (T <= 64, d_in <= 8192).
- * Where a forced regime does not apply the matrix-core GEMM runs. Results agree
- * within rounding in every regime; the switch exists for tests and
- * measurements. Process-wide; returns the previous value, or -1 (and changes
- * nothing) for any other argument. */
-int32_t wl_set_regime(int32_t regime);
+/* Prepares a projection workspace: clears its sync area (the first
+ * WL_SYNC_BYTES) with a kernel enqueued on hip_stream. Needed once before the
+ * workspace's first use by wl_linear, wl_qkv_fused or wl_mlp_fused, and again
+ * after anything else has written that area (the calls write it with
+ * generation-tagged words that are never reset; a tag left by foreign data
+ * could make a later call take a stale value). ws must be 256-byte aligned and
+ * ws_bytes >= WL_SYNC_BYTES (else WL_ERR_INVALID_ARG / WL_ERR_WORKSPACE). */
+wl_status wl_workspace_init(void *ws, size_t ws_bytes, void *hip_stream);
 
-/* Bound on the wait of a decode workgroup for the V^T x slices that other
- * workgroups of its launch compute (one to four tokens per pass): the number of
- * times it reads each group of tagged words, default 4096. A workgroup whose wait runs out
- * computes every slice itself, in the same order, so the result does not
- * change; 0 makes every workgroup do so (for tests). Process-wide; returns the
- * previous value, or -1 (and changes nothing) for a negative argument. */
-int32_t wl_set_spin_limit(int32_t polls);
+/* WL_SYNC_BYTES of the built library. */
+size_t wl_sync_bytes(void);
 
 /* Static description of a status code. */
 const char *wl_status_str(wl_status status);

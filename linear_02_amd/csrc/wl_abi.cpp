@@ -3,6 +3,7 @@
 // above that) and kernel launches. Nothing here computes any part of the
 // projection; every arithmetic step runs in the HIP kernels.
 #include "wl.h"
+#include "wl_testing.h"
 
 #include <hip/hip_runtime.h>
 
@@ -19,7 +20,15 @@ namespace {
 
 thread_local std::string g_error;
 std::atomic<int> g_spin_limit{wl::kSpinLimit};   // polls before a decode workgroup computes V^T x itself
-std::atomic<int> g_regime{0};   // 0 auto, 1 GEMV, 2 matrix-core GEMM, 3 GEMV always after a V^T x launch, 4 skinny
+// 0 auto, 1 GEMV, 2 matrix-core GEMM, 3 GEMV always after a V^T x launch, 4 skinny,
+// 5 GEMV with the MLP as two launches (gate/up, then down)
+std::atomic<int> g_regime{0};
+
+// WL_LOG is read once per process.
+bool log_on() {
+    static const bool on = getenv("WL_LOG") != nullptr;
+    return on;
+}
 
 constexpr size_t kAlign = 256;
 
@@ -30,7 +39,7 @@ wl_status fail(wl_status st, const char *fmt, ...) {
     vsnprintf(buf, sizeof buf, fmt, ap);
     va_end(ap);
     g_error = buf;
-    if (getenv("WL_LOG")) fprintf(stderr, "wl: %s\n", buf);
+    if (log_on()) fprintf(stderr, "wl: %s\n", buf);
     return st;
 }
 
@@ -115,7 +124,8 @@ Kind choose(int T, int d_in, int sum_r) {
     const bool sk = skinny_ok(T, d_in, sum_r);
     switch (regime) {
         case 1:
-        case 3: return tt ? kKindGemv : kKindGemm;
+        case 3:
+        case 5: return tt ? kKindGemv : kKindGemm;
         case 2: return kKindGemm;
         case 4: return sk ? kKindSkinny : kKindGemm;
         default: break;
@@ -312,7 +322,7 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
     if (pair) rows = ch[0].d_out;
     const Kind kind = choose(T, d_in, sum_r);
     const int tt = kind == kKindGemv ? wl::gemv_tokens_per_pass(d_in, T) : 0;
-    if (getenv("WL_LOG"))
+    if (log_on())
         fprintf(stderr, "wl: proj n_ch=%d pair=%d d_in=%d T=%d -> %s (tt=%d)\n", n_ch, (int)pair, d_in, T,
                 kind == kKindGemv ? "gemv" : kind == kKindSkinny ? "skinny" : "mfma", tt);
     if (kind == kKindSkinny) {
@@ -353,6 +363,7 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
         g.partial = reinterpret_cast<float *>(ws + L.gemv_partial);
         g.tagged = reinterpret_cast<unsigned long long *>(ws + wl::kSyncTaggedOffset);
         g.sync = reinterpret_cast<unsigned long long *>(ws);   // the sync area at offset 0
+        g.fin = reinterpret_cast<unsigned long long *>(ws + wl::kSyncFinalOffset);
         g.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
         const bool separate = g_regime.load(std::memory_order_relaxed) == 3;
         const wl::GemvPlan plan = wl::gemv_plan(g, tt, !separate);
@@ -460,7 +471,7 @@ wl_status run_proj_f32(const wl_theta *const *ths, int n_ch, bool pair, int d_in
     g.y = static_cast<float *>(y);
     const int regime = g_regime.load(std::memory_order_relaxed);
     const bool gemv = T <= wl::kF32GemvMaxTok && regime != 2 && regime != 4;
-    if (getenv("WL_LOG"))
+    if (log_on())
         fprintf(stderr, "wl: fp32 proj n_ch=%d pair=%d d_in=%d T=%d -> %s\n", n_ch, (int)pair, d_in, T,
                 gemv ? "gemv" : "mfma");
     e = gemv ? wl::launch_f32_gemv(g, stream) : wl::launch_f32_gemm(g, stream);
@@ -499,6 +510,20 @@ extern "C" {
 
 int32_t wl_abi_version(void) { return WL_ABI_VERSION; }
 
+size_t wl_sync_bytes(void) { return wl::kSyncBytes; }
+
+wl_status wl_workspace_init(void *ws, size_t ws_bytes, void *hip_stream) {
+    if (!ws) return fail(WL_ERR_INVALID_ARG, "workspace is NULL");
+    if (!aligned(ws, kAlign)) return fail(WL_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (ws_bytes < wl::kSyncBytes)
+        return fail(WL_ERR_WORKSPACE, "workspace of %zu bytes is below the sync area's %zu", ws_bytes,
+                    (size_t)wl::kSyncBytes);
+    const hipError_t e = wl::launch_sync_clear(static_cast<unsigned long long *>(ws), wl::kSyncBytes / 8,
+                                               static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(WL_ERR_HIP, "workspace init launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 const char *wl_status_str(wl_status st) {
     switch (st) {
         case WL_OK: return "ok";
@@ -513,7 +538,7 @@ const char *wl_status_str(wl_status st) {
 const char *wl_last_error(void) { return g_error.c_str(); }
 
 int32_t wl_set_regime(int32_t regime) {
-    if (regime < 0 || regime > 4) return -1;
+    if (regime < 0 || regime > 5) return -1;
     return g_regime.exchange(regime);
 }
 
@@ -636,8 +661,49 @@ wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta 
         if ((st = run_proj_f32(ths + 2, 1, false, d_ff, T, h, y, down->d_out, w, L, stream)) != WL_OK) return st;
         return ok();
     }
-    // gate/up -> h = bf16(gelu_tanh(g) * u), then down over h
     const wl::Child gu[2] = {make_child(gate, 0), make_child(up, 0)};
+    const int regime = g_regime.load(std::memory_order_relaxed);
+    if (regime == 0 || regime == 1) {
+        const wl::MlpPlan plan =
+            wl::mlp_dec_plan(gate->d_in, d_ff, down->d_out, gate->r, up->r, down->r, T);
+        if (plan.tt > 0) {
+            // One launch per pass: gate/up, GELU-tanh and down together.
+            if (log_on())
+                fprintf(stderr, "wl: mlp d_model=%d d_ff=%d d_out=%d T=%d -> one launch (tt=%d, W=%d, slices=%d)\n",
+                        gate->d_in, d_ff, down->d_out, T, plan.tt, plan.W, plan.NS);
+            wl::MlpDec a{};
+            wl::GemvF &g = a.gu;
+            g.ch[0] = gu[0];
+            g.ch[1] = gu[1];
+            g.n_ch = 2;
+            g.pair = 1;
+            g.d_in = gate->d_in;
+            g.rows = d_ff;
+            g.ldy = d_ff;
+            g.T = T;
+            g.x = static_cast<const uint16_t *>(x);
+            g.tagged = reinterpret_cast<unsigned long long *>(w + wl::kSyncTaggedOffset);
+            g.sync = reinterpret_cast<unsigned long long *>(w);
+            g.fin = reinterpret_cast<unsigned long long *>(w + wl::kSyncFinalOffset);
+            g.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+            a.W0d = static_cast<const uint16_t *>(down->W0);
+            a.Ud = static_cast<const uint16_t *>(down->U);
+            a.Vd = static_cast<const uint16_t *>(down->V);
+            a.sd = down->s;
+            a.rd = down->r;
+            a.D = down->d_out;
+            a.F = d_ff;
+            a.y = static_cast<uint16_t *>(y);
+            a.part = reinterpret_cast<unsigned long long *>(w + wl::kSyncPartOffset);
+            for (int t0 = 0; t0 < T; t0 += plan.tt) {
+                g.t0 = t0;
+                const hipError_t e = wl::launch_mlp_dec(a, plan, stream);
+                if (e != hipSuccess) return fail(WL_ERR_HIP, "MLP launch failed: %s", hipGetErrorString(e));
+            }
+            return ok();
+        }
+    }
+    // gate/up -> h = bf16(gelu_tanh(g) * u), then down over h
     if ((st = run_proj(gu, 2, true, gate->d_in, T, x, h, d_ff, w, L, stream)) != WL_OK) return st;
     const wl::Child dc = make_child(down, 0);
     if ((st = run_proj(&dc, 1, false, d_ff, T, h, y, down->d_out, w, L, stream)) != WL_OK) return st;

@@ -76,14 +76,21 @@ hipError_t launch_vtx(const VtxJob &job, hipStream_t stream);
 enum { kVtxNone = 0, kVtxPartials = 2, kVtxInLaunch = 3 };
 // The sync area, the first kSyncBytes of every workspace, 64-bit words:
 //   [0, kSyncCopies)          ticket counters, each advanced by exactly
-//                             kSyncStride per launch that hands V^T x over
+//                             kSyncStride per launch that hands words over
 //                             in-launch, so that ticket / kSyncStride is the
 //                             launch's generation in every workgroup
 //   kSyncFallbackWord         count of workgroups that computed V^T x themselves
-//   from kSyncTaggedOffset    the tagged V^T x slice words (kGemvTaggedPerChild per child)
-//   from kSyncFinalOffset     the tagged complete V^T x words, one per (child, token, k)
-//                             item (two-level hand-off)
-// Zero before first use; never reset afterwards.
+//   from kSyncTaggedOffset    the tagged V^T x slice words, kGemvTaggedPerChild
+//                             per child slot (kSyncTaggedChildren slots)
+//   from kSyncFinalOffset     the tagged complete V^T x words, one per (child,
+//                             token, k) item (two-level hand-off),
+//                             kSyncFinalPerChild per child slot
+//   from kSyncPartOffset      the tagged partial outputs of the one-dispatch MLP
+//                             (kSyncPartWords)
+// Zero before first use (wl_workspace_init); never reset afterwards. Each
+// launch clears one word of the tagged areas that is not its own (walking
+// through the kSweepWords words in turn), so that no word keeps a tag for the
+// 2^32 - 1 generations after which tags repeat.
 constexpr int kSyncCopies = 64;
 constexpr unsigned long long kSyncStride = 1ull << 24;
 constexpr int kSyncFallbackWord = 511;
@@ -98,8 +105,17 @@ constexpr size_t kGemvPartialPerChild = (size_t)kGemvMaxSlices * kGemvMaxTok * k
 // separate V^T x launch it saves).
 constexpr int kInLaunchMaxTok = 4;
 constexpr size_t kGemvTaggedPerChild = (size_t)kGemvMaxSlices * kInLaunchMaxTok * kMaxRank;
-constexpr size_t kSyncFinalOffset = kSyncTaggedOffset + kMaxChildren * kGemvTaggedPerChild * 8;
-constexpr size_t kSyncBytes = kSyncFinalOffset + kMaxChildren * kInLaunchMaxTok * kMaxRank * 8;
+constexpr int kSyncTaggedChildren = 8;
+constexpr size_t kSyncFinalOffset = kSyncTaggedOffset + kSyncTaggedChildren * kGemvTaggedPerChild * 8;
+constexpr size_t kSyncFinalPerChild = (size_t)kInLaunchMaxTok * kMaxRank;
+constexpr size_t kSyncPartOffset =
+    (kSyncFinalOffset + kSyncTaggedChildren * kSyncFinalPerChild * 8 + 65535) / 65536 * 65536;
+constexpr size_t kSyncPartWords = (size_t)1 << 20;
+constexpr size_t kSyncBytes = kSyncPartOffset + kSyncPartWords * 8;
+constexpr size_t kSweepWords = (kSyncBytes - kSyncTaggedOffset) / 8;
+
+// Clears the sync area (n_words 64-bit words at sync) with a fill kernel.
+hipError_t launch_sync_clear(unsigned long long *sync, size_t n_words, hipStream_t stream);
 
 struct GemvF {
     Child ch[kMaxChildren];
@@ -125,7 +141,8 @@ struct GemvF {
     // publishes complete V^T x words, so that projection workgroups read one
     // word per item instead of one per (item, slice).
     int n_prod, slice_len, spin_limit, two_level;
-    unsigned long long *sync;
+    unsigned long long *sync;   // the workspace's sync area (ticket counters)
+    unsigned long long *fin;    // two-level: this launch's complete V^T x words (kSyncFinalPerChild per child)
 };
 struct GemvPlan {
     int nseg = 1, R = 1, n_wg = 1, S = 0, slice_len = 0, vmode = kVtxNone, n_prod = 0, two_level = 0;
@@ -136,6 +153,38 @@ int gemv_slice_len(int d_in);
 // (at most kInLaunchMaxTok tokens per pass).
 GemvPlan gemv_plan(const GemvF &g, int tt, bool allow_inlaunch);
 hipError_t launch_gemv(const GemvF &g, const GemvPlan &plan, int tt, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// The MLP at decode sizes (1 to kInLaunchMaxTok tokens per pass) in one launch.
+// The first n_prod workgroups produce the gate/up pair's V^T x slices (the
+// in-launch hand-off of GemvF). Then one workgroup per slice j of W
+// consecutive intermediate rows forms, for the pass's tokens,
+//   h[t][i]   = bf16( gelu_tanh(gate[t][i]) * up[t][i] )          i in slice j
+//   p_j[t][o] = s_d[o] * sum_{i in j} W0_d[o][i] h[t][i]
+//               + sum_k U_d[o][k] * sum_{i in j} V_d[i][k] h[t][i]   every output o
+// (the down projection split along its input axis, so no workgroup needs
+// another's h), and stores p_j as tagged words. Each slice workgroup then adds,
+// for groups of kMlpGroup outputs, the words of every slice in slice order and
+// rounds once: y[t][o] = bf16( sum_j p_j[t][o] ). A wait that runs out
+// computes the missing slices itself, with the same arithmetic.
+constexpr int kMlpGroup = 8;         // outputs per reduction group
+constexpr int kMlpMaxSlices = 256;   // slices (workgroups besides the producers)
+constexpr int kMlpDownBytes = 73728;   // a slice's down columns (d_out x W bf16), held in registers
+struct MlpDec {
+    GemvF gu;                        // gate (ch[0]) / up (ch[1]) pair: x, tokens, producers, hand-off
+    const uint16_t *W0d, *Ud, *Vd;   // down: bf16 [D][F], [D][rd], [F][rd]
+    const float *sd;                 // fp32 [D], or null: every s is 1
+    int rd, D, F;
+    int NS, NG;                      // slices, output groups
+    uint16_t *y;                     // bf16 [T][D]
+    unsigned long long *part;        // tagged words [NG][NS][tt][kMlpGroup]
+};
+struct MlpPlan {
+    int tt = 0, W = 0, NS = 0, NG = 0, S = 0, slice_len = 0, n_prod = 0;
+};
+// tt = 0 when the one-launch MLP does not serve this shape.
+MlpPlan mlp_dec_plan(int d_model, int F, int d_out, int r_gate, int r_up, int r_down, int T);
+hipError_t launch_mlp_dec(const MlpDec &a, const MlpPlan &p, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // A few tens of tokens (8 < T <= kSkMaxTok), same result as Gemv (including pair

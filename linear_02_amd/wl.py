@@ -22,10 +22,11 @@ import torch
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwl.so")
 
 OP_LINEAR, OP_QKV, OP_MLP = 0, 1, 2
+ABI_VERSION = 5
 # The first SYNC_BYTES of a projection workspace are the library's sync area:
-# zero them before the workspace's first use and never write them afterwards
-# (torch.zeros does the first).
-SYNC_BYTES = 403456
+# cleared by wl_workspace_init (new_workspace does it) before first use, then
+# written only by the library's calls.
+SYNC_BYTES = 9502720
 _FALLBACK_WORD = 511   # int64 word of the sync area counting decode workgroups that stopped waiting
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error", 4: "workspace too small"}
 
@@ -76,6 +77,13 @@ def _load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.wl_rel_frob_workspace_bytes.restype = sz
     lib.wl_relative_frobenius_error.argtypes = [vp, vp, ctypes.c_int64, vp, vp, sz, vp]
     lib.wl_relative_frobenius_error.restype = ctypes.c_int
+    lib.wl_workspace_init.argtypes = [vp, sz, vp]
+    lib.wl_workspace_init.restype = ctypes.c_int
+    lib.wl_sync_bytes.argtypes = []
+    lib.wl_sync_bytes.restype = sz
+    if lib.wl_abi_version() != ABI_VERSION or lib.wl_sync_bytes() != SYNC_BYTES:
+        raise ImportError(f"{path}: ABI version {lib.wl_abi_version()} / sync area {lib.wl_sync_bytes()} bytes, "
+                          f"this binding expects {ABI_VERSION} / {SYNC_BYTES}; rebuild the library")
     return lib
 
 
@@ -126,9 +134,24 @@ def workspace_bytes(op: int, thetas: list, T: int) -> int:
     return int(lib.wl_workspace_bytes(op, arr, len(structs), T))
 
 
+def workspace_init(ws: torch.Tensor) -> None:
+    """Clear the sync area of a projection workspace (wl_workspace_init, on the
+    current stream)."""
+    _check(lib.wl_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(ws.device)))
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A projection workspace of at least nbytes (and at least the sync area),
+    prepared by wl_workspace_init."""
+    device = torch.device(device)
+    ws = torch.empty(max(int(nbytes), SYNC_BYTES), dtype=torch.uint8, device=device)
+    workspace_init(ws)
+    return ws
+
+
 class Workspace:
-    """A device workspace per (device, stream) that grows on demand, allocated
-    zeroed (the sync area must start at zero).
+    """A device workspace per (device, stream) that grows on demand, prepared by
+    wl_workspace_init when allocated.
 
     Calls on one stream run in order, so they can share one workspace."""
 
@@ -141,7 +164,7 @@ class Workspace:
         key = (device.index, torch.cuda.current_stream(device).cuda_stream)
         buf = self._bufs.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            buf = new_workspace(max(nbytes, 1 << 20), device)
             self._bufs[key] = buf
         return buf
 
@@ -235,15 +258,17 @@ def relative_frobenius_error(W: torch.Tensor, R: torch.Tensor) -> float:
     return float(out.item())
 
 
-REGIME_AUTO, REGIME_GEMV, REGIME_MFMA, REGIME_GEMV_TWO_LAUNCH, REGIME_SKINNY = 0, 1, 2, 3, 4
+REGIME_AUTO, REGIME_GEMV, REGIME_MFMA, REGIME_GEMV_TWO_LAUNCH, REGIME_SKINNY, REGIME_GEMV_MLP_SPLIT = 0, 1, 2, 3, 4, 5
 
 
 def set_regime(regime: int) -> int:
-    """0 auto, 1 decode GEMV, 2 matrix-core GEMM, 3 decode GEMV always after a
-    separate V^T x launch, 4 few-token split path; returns the previous setting."""
+    """0 auto, 1 decode kernels (the MLP in one launch where it applies), 2
+    matrix-core GEMM, 3 decode GEMV always after a separate V^T x launch, 4
+    few-token split path, 5 as 1 with the MLP as two launches; returns the
+    previous setting (wl_testing.h)."""
     prev = int(lib.wl_set_regime(regime))
     if prev < 0:
-        raise ValueError(f"regime {regime} is not 0, 1, 2, 3 or 4")
+        raise ValueError(f"regime {regime} is not one of 0 to 5")
     return prev
 
 

@@ -15,6 +15,7 @@ import pytest
 
 REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(REPO, "include", "wl.h")
+TEST_HEADER = os.path.join(REPO, "include", "wl_testing.h")
 
 
 @pytest.fixture(scope="module")
@@ -26,16 +27,19 @@ def wl():
     return mod
 
 
-def declared_functions() -> list[str]:
-    text = open(HEADER).read()
+def declared_functions(header: str = HEADER) -> list[str]:
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(wl_[a-z_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(wl):
-    names = declared_functions()
+    names = declared_functions() + declared_functions(TEST_HEADER)
     assert {"wl_linear", "wl_qkv_fused", "wl_mlp_fused", "wl_materialize_weff",
-            "wl_workspace_bytes"} <= set(names)
+            "wl_workspace_bytes", "wl_workspace_init", "wl_sync_bytes"} <= set(names)
+    # the switches for tests live in the test header only
+    assert not {"wl_set_regime", "wl_set_spin_limit"} & set(declared_functions())
+    assert {"wl_set_regime", "wl_set_spin_limit"} <= set(declared_functions(TEST_HEADER))
     out = subprocess.run(["nm", "-D", "--defined-only", wl.LIBRARY], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (wl_\w+)", out))
@@ -46,7 +50,7 @@ def test_exports_every_declared_symbol(wl):
 
 
 def test_abi_version_and_status_strings(wl):
-    assert wl.abi_version() == 4
+    assert wl.abi_version() == 5
     assert wl.lib.wl_status_str(0) == b"ok"
     assert wl.lib.wl_status_str(4) == b"workspace too small"
     assert wl.lib.wl_status_str(99) == b"unknown status"
@@ -189,9 +193,10 @@ def test_weff_checks(wl):
 def test_regime_switch(wl):
     prev = wl.set_regime(2)
     try:
-        assert wl.set_regime(1) == 2
+        assert wl.set_regime(5) == 2
+        assert wl.set_regime(1) == 5
         with pytest.raises(ValueError):
-            wl.set_regime(5)
+            wl.set_regime(6)
     finally:
         wl.set_regime(prev)
 
@@ -214,7 +219,19 @@ def test_workspace_starts_with_the_sync_area(wl):
         th = theta(d_in=d_in, d_out=d_out, r=r)
         arr = (ctypes.POINTER(wl.Theta) * 1)(ctypes.pointer(th))
         assert wl.lib.wl_workspace_bytes(0, arr, 1, 1) >= wl.SYNC_BYTES + 256
-    assert wl.SYNC_BYTES == 403456
+    assert wl.SYNC_BYTES == wl.lib.wl_sync_bytes() == 9502720
+    text = open(HEADER).read()
+    assert re.search(r"#define WL_SYNC_BYTES 9502720\b", text)
+    assert re.search(r"#define WL_ABI_VERSION 5\b", text)
+
+
+def test_workspace_init_checks(wl):
+    # validation only: every call below fails before anything is enqueued
+    need = wl.SYNC_BYTES
+    assert wl.lib.wl_workspace_init(None, need, None) == 1
+    assert wl.lib.wl_workspace_init(A + 0x10, need, None) == 1          # misaligned
+    assert wl.lib.wl_workspace_init(A, need - 1, None) == 4              # below the sync area
+    assert b"sync area" in wl.lib.wl_last_error()
 
 
 def test_library_resolves_its_own_symbols(wl):

@@ -5,7 +5,9 @@ and publish them through the workspace's sync area; the other workgroups wait
 for them (bounded) or, when the wait runs out, compute every slice themselves.
 All three routes must give the same bits: the hand-off, the forced fallback
 (spin limit 0) and the separate V^T x launch (regime 3), and the hand-off must
-also meet the oracle bar. The sync area is checked after the calls: every
+also meet the oracle bar. The MLP cases here run as two launches (regime 5, and
+regime 3 for the separate V^T x launches); the one-launch MLP has tests of its
+own (test_gpu_mlp.py). The sync area is checked after the calls: every
 ticket counter advanced by exactly 2^24 per in-launch launch, no fallback on a
 quiet device, and one per projection workgroup when forced.
 """
@@ -51,7 +53,7 @@ def sync_words(ws: torch.Tensor) -> np.ndarray:
     return ws[:4096].view(torch.int64).cpu().numpy()
 
 
-FINAL_OFFSET = 4096 + 3 * 64 * 4 * 64 * 8    # complete V^T x words of the two-level hand-off
+FINAL_OFFSET = 4096 + 8 * 64 * 4 * 64 * 8    # complete V^T x words of the two-level hand-off
 
 
 def final_tags(ws: torch.Tensor, n_items: int) -> np.ndarray:
@@ -133,15 +135,16 @@ def test_handoff_fallback_and_separate_launch_agree(wl, case, T):
     dths = [wl.theta_to(th, DEV) for th in ths]
     xd = x.to(DEV)
     wop = {"linear": wl.OP_LINEAR, "qkv": wl.OP_QKV, "mlp": wl.OP_MLP}[op]
-    ws = torch.zeros(wl.workspace_bytes(wop, dths, T), dtype=torch.uint8, device=DEV)
+    ws = wl.new_workspace(wl.workspace_bytes(wop, dths, T), DEV)
     print(f"hand-off case {op} {shape} r={ranks} T={T}", flush=True)
+    in_launch = 5 if op == "mlp" else 1    # the MLP as two launches
 
     prev = wl.set_regime(3)
     try:
         y_sep = run(wl, op, dths, xd, ws).clone()
         torch.cuda.synchronize()
         assert not sync_words(ws).any(), "the separate V^T x launch touched the sync area"
-        wl.set_regime(1)
+        wl.set_regime(in_launch)
         reps = 3
         for _ in range(reps):
             y_inl = run(wl, op, dths, xd, ws).clone()
@@ -187,7 +190,7 @@ def test_sync_area_survives_workspace_sharing(wl):
     th = wl.theta_to(inputs.theta(g, 1152, 1152, 32), DEV)
     xs = [inputs.activations(g, T, 1152).to(DEV) for T in (1, 2, 40, 300, 1)]
     need = max(wl.workspace_bytes(wl.OP_LINEAR, [th], x.shape[0]) for x in xs)
-    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    ws = wl.new_workspace(need, DEV)
     prev = wl.set_regime(0)
     try:
         outs = [wl.wl_linear(th, x, ws=ws).clone() for x in xs]

@@ -4,9 +4,10 @@ Every call goes through the C ABI (linear_02_amd.wl -> libwl.so). Floating-point
 cases must meet relL2 <= 2e-3 and |err| <= 8e-3 * bound per element; cases with
 small-integer inputs, whose every partial sum is exact in fp32 and whose outputs
 are exact in bf16, must match bit for bit. All kernel regimes (wave-per-row GEMV
-with V^T x in the same launch or in a launch of its own, matrix-core GEMM, and
-the few-token split path) are run on the same cases (a forced regime that
-does not apply to a case runs the matrix-core GEMM).
+with V^T x in the same launch or in a launch of its own, matrix-core GEMM, the
+few-token split path, and the decode MLP in one launch or as two) are run on
+the same cases (a forced regime that does not apply to a case runs the
+matrix-core GEMM).
 """
 from __future__ import annotations
 
@@ -34,9 +35,9 @@ def wl():
     return mod
 
 
-@pytest.fixture(params=["gemv", "mfma", "gemv2", "skinny"])
+@pytest.fixture(params=["gemv", "mfma", "gemv2", "skinny", "mlp2"])
 def regime(request, wl):
-    prev = wl.set_regime({"gemv": 1, "mfma": 2, "gemv2": 3, "skinny": 4}[request.param])
+    prev = wl.set_regime({"gemv": 1, "mfma": 2, "gemv2": 3, "skinny": 4, "mlp2": 5}[request.param])
     yield request.param
     wl.set_regime(prev)
 
