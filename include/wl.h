@@ -94,7 +94,7 @@ extern "C" {
 #define WL_ABI_VERSION 5
 
 /* Bytes at the start of a projection workspace that hold the sync area. */
-#define WL_SYNC_BYTES 9502720
+#define WL_SYNC_BYTES 9764864
 
 typedef enum {
     WL_OK = 0,

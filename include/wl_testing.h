@@ -14,7 +14,8 @@ extern "C" {
 #endif
 
 /* Kernel regime for the projection calls:
- *   0  chooses by token count (the default);
+ *   0  chooses by token count (the default; the MLP in one launch at one or
+ *      two tokens per pass where its shape allows);
  *   1  forces the decode kernels wherever they apply (V^T x computed by the
  *      first workgroups of the same launch at 1 to 4 tokens per pass, else by
  *      a separate launch before it; the MLP in one launch where its shape

@@ -4,33 +4,34 @@
 //
 // The down projection's input h is the whole gate/up result, so a launch that
 // splits down by output rows needs every workgroup to wait for every other's
-// h. This kernel splits down along its input axis instead: the intermediate
-// axis is cut into slices of W rows, and the workgroup of slice j
-//   1. streams the W gate rows and W up rows of its slice (all d_model inputs)
-//      and forms h[t][i] = bf16(gelu_tanh(gate) * up) for i in the slice, with
-//      the gate/up rank terms from V^T x slices that producer workgroups of the
-//      same launch hand over (wl_handoff.h);
-//   2. forms the slice's share of down for every output o,
+// h. This kernel splits down along its input axis instead. The intermediate
+// axis is cut into slices of 64 rows; the P workgroups of slice j each
+//   1. stream their 64 / P gate rows and up rows (all d_model inputs) and form
+//      h[t][i] = bf16(gelu_tanh(gate) * up) for those rows, the gate/up rank
+//      terms from V^T x slices that producer workgroups of the same launch hand
+//      over (wl_handoff.h); the slice's workgroups then exchange their h rows
+//      as tagged words, so each holds the slice's whole h;
+//   2. form the slice's share of down for their d_out / P output rows o,
 //        p_j[t][o] = s[o] * sum_{i in j} W0[o][i] h[t][i]
 //                    + sum_k U[o][k] * sum_{i in j} V[i][k] h[t][i],
-//      which is the per-element expansion of the reconstruction formula
-//      ("In-kernel reconstruction", introduction) restricted to the slice's
-//      inputs: the formula is linear in h, so the slices' shares add up to it;
-//   3. stores p_j as 64-bit words tagged with the launch's generation, then, for
-//      its groups of 8 outputs, reads every slice's words, adds them in slice
-//      order and rounds once to bf16.
-// Only the partial outputs cross workgroups (and V^T x of gate/up); h never
-// leaves the workgroup that made it. Every wait is bounded: a workgroup whose
-// wait runs out computes what it waited for with the same arithmetic, so the
-// result does not depend on timing.
+//      the per-element expansion of the reconstruction formula ("In-kernel
+//      reconstruction", introduction) restricted to the slice's inputs: the
+//      formula is linear in h, so the slices' shares add up to it;
+//   3. store p_j as 64-bit words tagged with the launch's generation, then, for
+//      their groups of 8 outputs, read every slice's words, add them in slice
+//      order and round once to bf16.
+// Every wait is bounded: a workgroup whose wait runs out computes what it
+// waited for with the same arithmetic, so the result does not depend on
+// timing.
 //
-// Memory: the gate/up rows (2 W d_model bf16) are read by 16-lane row groups,
-// 16 bytes per lane, every load of a batch issued before any is used; the
-// slice's down columns (d_out rows x W inputs) follow into registers and stream
-// while V^T x is gathered and h formed. The down U rows and s, the same for
-// every slice, come from L2. Direct-to-LDS loads (the slice's small operands)
-// only target the first 64 KiB of LDS: their LDS address is taken from a
-// 16-bit field.
+// Memory (measured: reading 64-byte pieces of each down row streams at less
+// than half the rate of whole 128-byte lines, hence slices of 64 inputs shared
+// by P workgroups): the gate/up rows are read by 16-lane row groups, 16 bytes
+// per lane, in batches of two row steps whose loads are all issued before any
+// is used; the workgroup's down rows (128-byte pieces, 8 lanes per row) go into
+// registers right behind the first batch, so the whole workgroup's bytes are
+// in flight together. The down U rows and s, the same for every slice, come
+// from L2. Direct-to-LDS loads are kept to the slice's small operands.
 #include "wl_device.h"
 #include "wl_kernels.h"
 #include "wl_vtx_slice.h"
@@ -42,8 +43,13 @@ namespace {
 
 constexpr int kThreads = kHThreads;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kUB = 9;      // 16-byte loads per lane per gate/up row in one batch
-constexpr int kPB = kMlpDownBytes / 16 / kThreads;   // down passes (kThreads pieces each) at most
+constexpr int kW = kMlpSlice;             // slice rows = down inputs per slice
+constexpr int kL = kW / 8;                // lanes per down row (one 16-byte piece each)
+constexpr int kRW = kWave / kL;           // down rows per wave per pass
+constexpr int kPB = kMlpDownPasses;       // down passes per workgroup (kWaves x kRW rows each)
+constexpr int kUB = 9;                    // 16-byte pieces per lane per gate/up row in one batch
+constexpr int kSB = 2;                    // gate/up row steps (4 rows each) per batch
+constexpr int kEarlyWords = 16;           // tagged V^T x words per thread read ahead
 
 // 16-byte load through the global address space, not kept in the caches
 // (each W0 element is used once per launch).
@@ -51,7 +57,18 @@ __device__ __forceinline__ u32x4 ld_stream(const uint16_t *p) {
     return __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)p);
 }
 
-// Sum over the aligned groups of L lanes (L = 2, 4, 8 or 16, within a DPP row);
+// A read of LDS through an explicit LDS pointer: a pointer into the LDS struct
+// that passes through a select or a cast is otherwise read with flat
+// instructions, which also wait on the global-memory counter.
+template <class T>
+__device__ __forceinline__ T lds_ld(const T *p) {
+    return *(const __attribute__((address_space(3))) T *)p;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return bf16_f(w & 0xFFFFu); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return bf16_f(w >> 16); }
+
+// Sum over aligned groups of L lanes (L = 2, 4, 8 or 16, within a DPP row);
 // every lane of a group ends with the group's sum, in the same bits.
 template <int L>
 __device__ __forceinline__ float group_sum_lanes(float v) {
@@ -62,400 +79,572 @@ __device__ __forceinline__ float group_sum_lanes(float v) {
     return v;
 }
 
-// One 16-byte piece per lane of a contiguous region of n16 pieces copied into
-// LDS, the wave's 64 lanes side by side (the destination is padded to whole
+// A contiguous region of n16 16-byte pieces copied into LDS by direct-to-LDS
+// loads, the wave's 64 lanes side by side (the destination is padded to whole
 // waves' worth of pieces; lanes past the end reload the last piece).
 __device__ __forceinline__ void copy_to_lds(const uint16_t *src, int n16, u32x4 *dst) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const u32x4 *s = reinterpret_cast<const u32x4 *>(src);
-    for (int m = wave * kWave; m < n16; m += kThreads)
-        lds_dma16(s + min(m + lane, n16 - 1), dst + m);
+    for (int m = wave * kWave; m < n16; m += kThreads) lds_dma16(s + min(m + lane, n16 - 1), dst + m);
 }
 
-// Slice j's workgroup index mapping: slice workgroups on one XCD (workgroup b
-// runs on XCD b % 8) take consecutive slices, so that slices sharing a
-// 128-byte line of a down row are read through the same L2.
-__device__ __forceinline__ int slice_of_block(int b, int n_prod, int NS) {
-    const int x = b % 8;
-    int base = 0, first = 0;
-    for (int xx = 0; xx <= x; ++xx) {
-        first = n_prod + ((xx - n_prod % 8) % 8 + 8) % 8;
-        const int cnt = first < n_prod + NS ? (n_prod + NS - first + 7) / 8 : 0;
-        if (xx < x) base += cnt;
-    }
-    return base + (b - first) / 8;
-}
-
-template <int TT, int W>
+template <int TT>
 struct Lds {
-    // direct-to-LDS targets first (within the first 64 KiB)
-    u32x4 ug[W * kMaxRank / 8];                         // gate U rows of the slice, bf16 [W][r]
-    u32x4 uu[W * kMaxRank / 8];                         // up U rows
-    u32x4 vd[W * kMaxRank / 8];                         // down V rows of the slice, bf16 [W][rd]
+    // direct-to-LDS targets, each padded by one wave's worth of pieces (a copy
+    // writes whole waves' worth)
+    u32x4 ug[kW * kMaxRank / 8 + kWave];                // gate U rows of the slice, bf16 [64][r] (slice-local rows)
+    u32x4 uu[kW * kMaxRank / 8 + kWave];                // up U rows
+    u32x4 vd[kW * kMaxRank / 8 + kWave];                // down V rows of the slice, bf16 [64][rd]
     float vred[kThreads][TT + 1];                       // producer / fallback slice sums
     u32x4 xstage[TT > 2 ? TT * kXStageMax / 8 : 1];     // producer / fallback x slice
     float gsum[kThreads];
-    float vs[kMaxChildren][TT][kMaxRank];               // gate / up V^T x
+    alignas(16) float vs[kMaxChildren][TT][kMaxRank];   // gate / up V^T x
     float fgs[kMaxChildren * TT * kMaxRank];            // fallback group sums
-    float ml[2][W][TT];                                 // gate / up W0 x
-    float val[2][W][TT];                                // gate / up values
-    float sl[2][W];                                     // gate / up s
-    alignas(16) uint16_t h[TT][W];                      // bf16 h of the slice
+    float ml[2][kW][TT];                                // gate / up W0 x (slice-local rows)
+    float val[2][kW][TT];                               // gate / up values
+    float sl[2][kW];                                    // gate / up s
+    alignas(16) uint16_t h[TT][kW];                     // bf16 h of the slice
     float vj[TT][kMaxRank];                             // sum over the slice of V_d[i][k] h[t][i]
+    float vjp[kThreads];                                // its row-group sums
     float red[32][kMlpGroup];                           // reduction of the partial outputs
     uint32_t tag;
     int miss, need;
 };
 
-// ---- step 1: gate/up of slice j into h ----
+// A part of slice j: slice-local rows [r0, r0 + n) of the intermediate axis
+// (rows i0 + r0 ..); n is the part's rows that exist (the last slice may be
+// short, and a part of it empty).
+struct Part {
+    int j, p, i0, wj, r0, n;   // slice, part, first row of the slice, rows of the slice, part's first row, its rows
+};
+__device__ __forceinline__ Part make_part(const MlpDec &a, int j, int p) {
+    Part q;
+    q.j = j;
+    q.p = p;
+    q.i0 = j * kW;
+    q.wj = min(kW, a.F - q.i0);
+    q.r0 = p * a.WR;
+    q.n = max(0, min(a.WR, q.wj - q.r0));
+    return q;
+}
 
-// W0 x of the slice's 2 W gate/up rows into ml. Wave q takes slice rows
-// [q W/4, (q+1) W/4); a step covers 2 slice rows x {gate, up}, one per 16-lane
-// row group; each lane takes the row's 16-byte pieces l16, l16 + 16, ... and
-// the matching pieces of x (from L2). The loads of UB pieces x SB steps are
-// issued before any is used. issued() runs once in every thread, right after
-// the first batch's loads are issued (the first batch is peeled out of the
-// loops, so that what issued() does stays straight-line code). The caller
-// ends it with a barrier.
-template <int TT, int W>
+// ---- step 1: gate/up rows of a part ----
+
+// Wave q takes slice-local rows r0 + q WR/4 .. + WR/4 of gate and of up; a
+// step covers 2 rows x {gate, up}, one per 16-lane row group; each lane takes
+// the row's 16-byte pieces l16, l16 + 16, ... and the matching pieces of x
+// (from L2).
+template <int TT>
 struct GateUp {
-    static constexpr int STEPS = W / 8;
-    static constexpr int SB = STEPS < 4 ? STEPS : 4;
-    // A batch (SB x UB pieces of W0, UB x TT of x) keeps about 45 loads in
-    // flight per lane.
-    static constexpr int UB = 45 / (SB + TT) < kUB ? 45 / (SB + TT) : kUB;
-    u32x4 wv[SB][UB], xv[UB][TT];
-    float acc[SB][TT];
+    u32x4 wv[kSB][kUB], xv[kUB][TT];
+    float acc[kSB][TT];
 };
 
-template <int TT, int W>
-__device__ __forceinline__ void gu_issue(const MlpDec &a, int i0, int wj, int sb, int ub, GateUp<TT, W> &b) {
-    using B = GateUp<TT, W>;
+template <int TT>
+__device__ __forceinline__ void gu_issue(const MlpDec &a, const Part &pt, int sb, int ub, GateUp<TT> &b) {
     const int lane = threadIdx.x & (kWave - 1), q = threadIdx.x / kWave;
     const int rho = lane >> 4, l16 = lane & 15;
     const int D = a.gu.d_in, nch = D >> 3;
     const int tn = min(TT, a.gu.T - a.gu.t0);
     const uint16_t *Wrow = (rho & 1) ? a.gu.ch[1].W0 : a.gu.ch[0].W0;
     const u32x4 *xg = reinterpret_cast<const u32x4 *>(a.gu.x + (size_t)a.gu.t0 * D);
+    const int nr = max(pt.n, 1);
 #pragma unroll
-    for (int st = 0; st < B::SB; ++st) {
-        const int i = q * (W / 4) + 2 * (sb + st) + (rho >> 1);
-        const uint16_t *base = Wrow + (size_t)(i0 + min(i, wj - 1)) * D;
+    for (int st = 0; st < kSB; ++st) {
+        const int i = q * (a.WR / 4) + 2 * (sb + st) + (rho >> 1);
+        const uint16_t *base = Wrow + (size_t)(pt.i0 + pt.r0 + min(i, nr - 1)) * D;
 #pragma unroll
-        for (int u = 0; u < B::UB; ++u) b.wv[st][u] = ld_stream(base + 8 * min(l16 + 16 * (ub + u), nch - 1));
+        for (int u = 0; u < kUB; ++u) b.wv[st][u] = ld_stream(base + 8 * min(l16 + 16 * (ub + u), nch - 1));
     }
 #pragma unroll
-    for (int u = 0; u < B::UB; ++u) {
+    for (int u = 0; u < kUB; ++u) {
         const int ch = min(l16 + 16 * (ub + u), nch - 1);
 #pragma unroll
         for (int t = 0; t < TT; ++t) b.xv[u][t] = ldg(xg + (size_t)min(t, tn - 1) * nch + ch);
     }
 }
 
-template <int TT, int W>
-__device__ __forceinline__ void gu_compute(const MlpDec &a, int ub, GateUp<TT, W> &b) {
-    using B = GateUp<TT, W>;
+template <int TT>
+__device__ __forceinline__ void gu_compute(const MlpDec &a, int ub, GateUp<TT> &b) {
     const int l16 = threadIdx.x & 15, nch = a.gu.d_in >> 3;
     // Pieces past the row's end were loaded from its last piece; their x is
     // zeroed (a select, not a branch), so they add nothing.
 #pragma unroll
-    for (int u = 0; u < B::UB; ++u) {
+    for (int u = 0; u < kUB; ++u) {
         const bool in = l16 + 16 * (ub + u) < nch;
 #pragma unroll
         for (int t = 0; t < TT; ++t) b.xv[u][t] = in ? b.xv[u][t] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < B::UB; ++u)
+    for (int u = 0; u < kUB; ++u)
 #pragma unroll
-        for (int st = 0; st < B::SB; ++st)
+        for (int st = 0; st < kSB; ++st)
 #pragma unroll
             for (int t = 0; t < TT; ++t) b.acc[st][t] = dot8(b.wv[st][u], b.xv[u][t], b.acc[st][t]);
 }
 
-template <int TT, int W>
-__device__ __forceinline__ void gu_finish(int sb, GateUp<TT, W> &b, Lds<TT, W> &s) {
-    using B = GateUp<TT, W>;
+template <int TT>
+__device__ __forceinline__ void gu_finish(const MlpDec &a, const Part &pt, int sb, GateUp<TT> &b, Lds<TT> &s) {
     const int lane = threadIdx.x & (kWave - 1), q = threadIdx.x / kWave;
     const int rho = lane >> 4, l16 = lane & 15;
 #pragma unroll
-    for (int st = 0; st < B::SB; ++st) {
-        const int i = q * (W / 4) + 2 * (sb + st) + (rho >> 1);
+    for (int st = 0; st < kSB; ++st) {
+        const int i = q * (a.WR / 4) + 2 * (sb + st) + (rho >> 1);
+        const bool real = sb + st < a.WR / 8 && i < pt.n;
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
             const float v = group_sum_lanes<16>(b.acc[st][t]);
-            if (l16 == 0) s.ml[rho & 1][i][t] = v;
+            if (l16 == 0 && real) s.ml[rho & 1][pt.r0 + i][t] = v;
         }
     }
 }
 
-template <int TT, int W, class Hook>
-__device__ __forceinline__ void gateup_stream(const MlpDec &a, int i0, int wj, Lds<TT, W> &s, Hook issued) {
-    using B = GateUp<TT, W>;
+template <int TT>
+__device__ __forceinline__ void gu_zero(GateUp<TT> &b) {
+#pragma unroll
+    for (int st = 0; st < kSB; ++st)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) b.acc[st][t] = 0.f;
+}
+
+// W0 x of a part's gate/up rows into ml. first_issued() runs once in every
+// thread right after the first batch's loads are issued, later_issued() after
+// each later batch's (the first batch is peeled out of the loops, so what they
+// do stays straight-line code). The caller ends it with a barrier.
+template <int TT, class Hook1, class Hook2>
+__device__ __forceinline__ void gateup_rows(const MlpDec &a, const Part &pt, Lds<TT> &s, Hook1 first_issued,
+                                            Hook2 later_issued) {
     const int nu = ((a.gu.d_in >> 3) + 15) >> 4;
+    const int steps = a.WR / 8;
     {
-        B b;
-        gu_issue<TT, W>(a, i0, wj, 0, 0, b);
+        GateUp<TT> b;
+        gu_issue<TT>(a, pt, 0, 0, b);
         __builtin_amdgcn_sched_barrier(0);
-        issued();
+        first_issued();
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int st = 0; st < B::SB; ++st)
-#pragma unroll
-            for (int t = 0; t < TT; ++t) b.acc[st][t] = 0.f;
-        gu_compute<TT, W>(a, 0, b);
-        for (int ub = B::UB; ub < nu; ub += B::UB) {
-            gu_issue<TT, W>(a, i0, wj, 0, ub, b);
-            gu_compute<TT, W>(a, ub, b);
+        gu_zero<TT>(b);
+        gu_compute<TT>(a, 0, b);
+        for (int ub = kUB; ub < nu; ub += kUB) {
+            gu_issue<TT>(a, pt, 0, ub, b);
+            gu_compute<TT>(a, ub, b);
         }
-        gu_finish<TT, W>(0, b, s);
+        gu_finish<TT>(a, pt, 0, b, s);
     }
-    for (int sb = B::SB; sb < B::STEPS; sb += B::SB) {
-        B b;
-#pragma unroll
-        for (int st = 0; st < B::SB; ++st)
-#pragma unroll
-            for (int t = 0; t < TT; ++t) b.acc[st][t] = 0.f;
-        for (int ub = 0; ub < nu; ub += B::UB) {
-            gu_issue<TT, W>(a, i0, wj, sb, ub, b);
-            gu_compute<TT, W>(a, ub, b);
+    for (int sb = kSB; sb < steps; sb += kSB) {
+        GateUp<TT> b;
+        gu_zero<TT>(b);
+        gu_issue<TT>(a, pt, sb, 0, b);
+        __builtin_amdgcn_sched_barrier(0);
+        later_issued();
+        __builtin_amdgcn_sched_barrier(0);
+        gu_compute<TT>(a, 0, b);
+        for (int ub = kUB; ub < nu; ub += kUB) {
+            gu_issue<TT>(a, pt, sb, ub, b);
+            gu_compute<TT>(a, ub, b);
         }
-        gu_finish<TT, W>(sb, b, s);
+        gu_finish<TT>(a, pt, sb, b, s);
     }
 }
 
-// h of the slice from ml, the gate/up scales, U rows (LDS) and V^T x (vs):
-// thread (p, i) forms gate or up of slice row i for every token, rank term
-// summed over k in order; then thread (i, t) rounds h. Ends with a barrier.
-template <int TT, int W>
-__device__ __forceinline__ void form_h(const MlpDec &a, int wj, Lds<TT, W> &s) {
+// The part's gate/up U rows into LDS (direct-to-LDS), and the thread's gate/up
+// s value (threads below 2 x 64: gate or up of slice-local row tid % 64),
+// returned to be written with put_scale once it has arrived. The caller waits
+// (wait_vm<0>, barrier) before using the U rows.
+template <int TT>
+__device__ __forceinline__ float stage_part(const MlpDec &a, const Part &pt, Lds<TT> &s) {
+    const int rg = a.gu.ch[0].r, ru = a.gu.ch[1].r;
+    if (pt.n > 0) {
+        if (rg > 0) copy_to_lds(a.gu.ch[0].U + (size_t)(pt.i0 + pt.r0) * rg, pt.n * rg / 8, s.ug + pt.r0 * rg / 8);
+        if (ru > 0) copy_to_lds(a.gu.ch[1].U + (size_t)(pt.i0 + pt.r0) * ru, pt.n * ru / 8, s.uu + pt.r0 * ru / 8);
+    }
+    const int tid = threadIdx.x, p = (tid / kW) & 1, i = tid % kW;
+    const float *sp = p ? a.gu.ch[1].s : a.gu.ch[0].s;
+    const float *sg = sp ? sp + pt.i0 + min(i, pt.wj - 1) : reinterpret_cast<const float *>(a.gu.x);
+    const float v = ldg(sg);
+    return sp ? v : 1.f;
+}
+template <int TT>
+__device__ __forceinline__ void put_scale(float v, Lds<TT> &s) {
     const int tid = threadIdx.x;
-    if (tid < 2 * W) {
-        const int p = tid / W, i = tid % W;
-        const int r = p ? a.gu.ch[1].r : a.gu.ch[0].r;
-        const uint16_t *U = reinterpret_cast<const uint16_t *>(p ? s.uu : s.ug);
-        float rt[TT];
+    if (tid < 2 * kW) s.sl[tid / kW][tid % kW] = v;
+}
+// The slice's down V rows into LDS (direct-to-LDS).
+template <int TT>
+__device__ __forceinline__ void stage_vd(const MlpDec &a, const Part &pt, Lds<TT> &s) {
+    if (a.rd > 0) copy_to_lds(a.Vd + (size_t)pt.i0 * a.rd, pt.wj * a.rd / 8, s.vd);
+}
+
+// h of a part's rows from ml, s, U rows (LDS) and V^T x (vs): thread (p, i)
+// forms gate or up of a row for every token, rank term summed over k in order;
+// then thread (i, t) rounds h. Ends with a barrier.
+template <int TT>
+__device__ __forceinline__ void form_h(const MlpDec &a, const Part &pt, Lds<TT> &s) {
+    const int tid = threadIdx.x;
+    if (tid < 2 * kW) {
+        const int p = tid / kW, i = tid % kW;
+        if (i >= pt.r0 && i < pt.r0 + pt.n) {
+            const int r = p ? a.gu.ch[1].r : a.gu.ch[0].r;
+            const uint16_t *U = reinterpret_cast<const uint16_t *>(p ? s.uu : s.ug);
+            float rt[TT];
 #pragma unroll
-        for (int t = 0; t < TT; ++t) rt[t] = 0.f;
-        for (int k = 0; k < r; ++k) {
-            const float uk = bf16_f(U[min(i, wj - 1) * r + k]);
+            for (int t = 0; t < TT; ++t) rt[t] = 0.f;
+            if (r % 8 == 0) {
+                // 16-byte reads of the U row and of V^T x, products still added in k order
+                const u32x4 *Ur = reinterpret_cast<const u32x4 *>(U + i * r);
+                for (int k8 = 0; k8 < r / 8; ++k8) {
+                    const u32x4 u = lds_ld(Ur + k8);
+                    const float uk[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                                         bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
 #pragma unroll
-            for (int t = 0; t < TT; ++t) rt[t] += uk * s.vs[p][t][k];
+                    for (int t = 0; t < TT; ++t) {
+                        const f32x4 v0 = lds_ld(reinterpret_cast<const f32x4 *>(&s.vs[p][t][8 * k8]));
+                        const f32x4 v1 = lds_ld(reinterpret_cast<const f32x4 *>(&s.vs[p][t][8 * k8 + 4]));
+                        rt[t] += uk[0] * v0.x;
+                        rt[t] += uk[1] * v0.y;
+                        rt[t] += uk[2] * v0.z;
+                        rt[t] += uk[3] * v0.w;
+                        rt[t] += uk[4] * v1.x;
+                        rt[t] += uk[5] * v1.y;
+                        rt[t] += uk[6] * v1.z;
+                        rt[t] += uk[7] * v1.w;
+                    }
+                }
+            } else {
+                for (int k = 0; k < r; ++k) {
+                    const float uk = bf16_f(lds_ld(U + i * r + k));
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) rt[t] += uk * s.vs[p][t][k];
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TT; ++t) s.val[p][i][t] = s.sl[p][i] * s.ml[p][i][t] + rt[t];
         }
-#pragma unroll
-        for (int t = 0; t < TT; ++t) s.val[p][i][t] = s.sl[p][i] * s.ml[p][i][t] + rt[t];
     }
     __syncthreads();
-    for (int idx = tid; idx < W * TT; idx += kThreads) {
+    for (int idx = tid; idx < kW * TT; idx += kThreads) {
         const int i = idx / TT, t = idx % TT;
-        const float hv = i < wj ? gelu_tanh(s.val[0][i][t]) * s.val[1][i][t] : 0.f;
-        s.h[t][i] = f_bf16(hv);
+        if (i >= pt.r0 && i < pt.r0 + pt.n) s.h[t][i] = f_bf16(gelu_tanh(s.val[0][i][t]) * s.val[1][i][t]);
     }
     __syncthreads();
 }
 
-// vj[t][k] = sum over the slice's rows i (in order) of V_d[i][k] h[t][i].
-template <int TT, int W>
-__device__ __forceinline__ void form_vj(const MlpDec &a, int wj, Lds<TT, W> &s) {
-    const int tid = threadIdx.x, rd = a.rd;
+// ---- the exchange of h between the slice's workgroups ----
+
+// Word (j, i / 2, t): the tag beside the bf16 pair h[t][i], h[t][i + 1].
+__device__ __forceinline__ unsigned long long *hx_word(const MlpDec &a, int j, int i2, int t, int tt) {
+    return a.hx + ((size_t)j * (kW / 2) + i2) * tt + t;
+}
+template <int TT>
+__device__ __forceinline__ void publish_h(const MlpDec &a, const Part &pt, const Lds<TT> &s, unsigned long long tag) {
+    const int tn = min(TT, a.gu.T - a.gu.t0);
+    for (int idx = threadIdx.x; idx < (pt.n / 2) * tn; idx += kThreads) {
+        const int i2 = pt.r0 / 2 + idx / tn, t = idx % tn;
+        const uint32_t v = (uint32_t)s.h[t][2 * i2] | ((uint32_t)s.h[t][2 * i2 + 1] << 16);
+        __hip_atomic_store(hx_word(a, pt.j, i2, t, TT), tag | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+// The other parts' h rows of the slice from their words: thread per word,
+// read again while it lacks the tag, at most `retries` more times. False when
+// some wait ran out (the h rows stay incomplete).
+template <int TT>
+__device__ __forceinline__ bool fetch_h(const MlpDec &a, const Part &pt, Lds<TT> &s, uint32_t tag, int retries) {
+    const int tn = min(TT, a.gu.T - a.gu.t0);
+    bool ok = true;
+    for (int idx = threadIdx.x; idx < (pt.wj / 2) * tn; idx += kThreads) {
+        const int i2 = idx / tn, t = idx % tn;
+        if (2 * i2 >= pt.r0 && 2 * i2 < pt.r0 + pt.n) continue;   // this part's own rows
+        unsigned long long w = 0;
+        bool got = false;
+        for (int spin = 0; spin <= retries; ++spin) {
+            w = ld_word(hx_word(a, pt.j, i2, t, TT));
+            if (word_is(w, tag)) {
+                got = true;
+                break;
+            }
+        }
+        if (got) {
+            s.h[t][2 * i2] = (uint16_t)(w & 0xFFFFu);
+            s.h[t][2 * i2 + 1] = (uint16_t)((w >> 16) & 0xFFFFu);
+        }
+        ok = ok && got;
+    }
+    return ok;
+}
+
+// vj[t][k] = sum over the slice's rows i of V_d[i][k] h[t][i]. Thread (g, t, k)
+// adds the products of row group g (64 / G consecutive rows, in row order;
+// rows past the slice's end add +0), then thread (t, k) adds the G group sums
+// in group order. Ends with a barrier.
+template <int TT>
+__device__ __forceinline__ void form_vj(const MlpDec &a, const Part &pt, Lds<TT> &s) {
+    const int rd = a.rd, n = TT * rd, tid = threadIdx.x;
+    const int G = n <= kThreads / 8 ? 8 : n <= kThreads / 4 ? 4 : n <= kThreads / 2 ? 2 : 1;
+    const int R = kW / G;
     const uint16_t *V = reinterpret_cast<const uint16_t *>(s.vd);
-    for (int idx = tid; idx < TT * rd; idx += kThreads) {
-        const int t = idx / rd, k = idx % rd;
+    if (tid < G * n) {
+        const int g = tid / n, item = tid % n, t = item / rd, k = item % rd;
         float acc = 0.f;
-        for (int i = 0; i < wj; ++i) acc += bf16_f(V[i * rd + k]) * bf16_f(s.h[t][i]);
-        s.vj[t][k] = acc;
+#pragma unroll 8
+        for (int u = 0; u < R; ++u) {
+            const int i = g * R + u, ic = min(i, pt.wj - 1);
+            // a product of two bf16 values is exact in fp32
+            const float v = bf16_f(lds_ld(V + ic * rd + k)) * bf16_f(lds_ld(&s.h[t][ic]));
+            acc += i < pt.wj ? v : 0.f;
+        }
+        s.vjp[tid] = acc;
+    }
+    __syncthreads();
+    if (tid < n) {
+        float acc = s.vjp[tid];
+        for (int g = 1; g < G; ++g) acc += s.vjp[g * n + tid];
+        s.vj[tid / rd][tid % rd] = acc;
     }
     __syncthreads();
 }
 
 // ---- step 2: the slice's share of down ----
 
-// Lane (ro, c) of wave q takes down row o = pass * 4 RW + q * RW + ro of a
-// pass and the slice's 16-byte piece c (inputs i0 + 8c .. i0 + 8c + 7).
-template <int W>
+// Lane (ro, c) of wave q takes down row o = o0 + pass * 4 kRW + q * kRW + ro
+// of a pass and the slice's 16-byte piece c (inputs i0 + 8c .. i0 + 8c + 7).
 struct DownLane {
-    static constexpr int L = W / 8, RW = kWave / L;
     int c, ro, q;
     __device__ __forceinline__ DownLane() {
         const int lane = threadIdx.x & (kWave - 1);
-        c = lane % L;
-        ro = lane / L;
+        c = lane % kL;
+        ro = lane / kL;
         q = threadIdx.x / kWave;
     }
-    __device__ __forceinline__ int row(int pass) const { return pass * (kWaves * RW) + q * RW + ro; }
+    __device__ __forceinline__ int row(int o0, int pass) const { return o0 + pass * (kWaves * kRW) + q * kRW + ro; }
 };
 
-// The lane's piece of down row o from global memory (row and piece clamped).
-template <int W>
-__device__ __forceinline__ u32x4 load_down_piece(const MlpDec &a, int i0, int wj, int o) {
-    const DownLane<W> dl;
-    const int oc = min(o, a.D - 1), cc = min(dl.c, wj / 8 - 1);
-    return ld_stream(a.W0d + (size_t)oc * a.F + i0 + 8 * cc);
+// The lane's piece of down row o (row and piece clamped into the tensor).
+__device__ __forceinline__ u32x4 load_down_piece(const MlpDec &a, const Part &pt, int o) {
+    const DownLane dl;
+    return ld_stream(a.W0d + (size_t)min(o, a.D - 1) * a.F + pt.i0 + 8 * min(dl.c, pt.wj / 8 - 1));
 }
 
-// U_d[o][k] for the lane's rank entries: piece c of the row (entries 8c ..
-// 8c + 7) when rd is a multiple of 8 (rd <= 8 L), else (rd <= L) entry c.
-__device__ __forceinline__ u32x4 load_u_piece(const MlpDec &a, int c, int o) {
-    const int rd = a.rd, oc = min(o, a.D - 1);
-    const uint16_t *row = a.Ud + (size_t)oc * rd;
-    if (rd % 8 == 0) return ldg(reinterpret_cast<const u32x4 *>(row) + min(c, rd / 8 - 1));
-    return u32x4{ldg(row + min(c, rd - 1)), 0u, 0u, 0u};
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return bf16_f(w & 0xFFFFu); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return bf16_f(w >> 16); }
-
-// The lane's share of the rank term of token t (products added in k order).
-template <int TT, int W>
-__device__ __forceinline__ float lane_rank_term(const MlpDec &a, u32x4 u, const Lds<TT, W> &s, int t) {
-    const DownLane<W> dl;
-    const int rd = a.rd;
-    float acc = 0.f;
+// The lane's rank slots e = 0..7: k = 8c + e when rd is a multiple of 8, else
+// (rd < 8) slot 0 is k = c. Slots without an entry below rd hold zero, in U
+// and in vj alike, so every lane runs the same eight products.
+__device__ __forceinline__ bool rank_slot(int rd, int c, int e, int &k) {
     if (rd % 8 == 0) {
-        if (8 * dl.c < rd) {
-            const float *v = &s.vj[t][8 * dl.c];
-            acc += bf16_lo(u.x) * v[0];
-            acc += bf16_hi(u.x) * v[1];
-            acc += bf16_lo(u.y) * v[2];
-            acc += bf16_hi(u.y) * v[3];
-            acc += bf16_lo(u.z) * v[4];
-            acc += bf16_hi(u.z) * v[5];
-            acc += bf16_lo(u.w) * v[6];
-            acc += bf16_hi(u.w) * v[7];
-        }
-    } else if (dl.c < rd) {
-        acc += bf16_lo(u.x) * s.vj[t][dl.c];
+        k = 8 * c + e;
+        return k < rd;
     }
-    return acc;
+    k = c;
+    return e == 0 && c < rd;
 }
 
-// p_j[t][o] of one down row, on every lane of the row's L-lane group:
-// s[o] * (W0 h over the slice) + (U over the rank entries).
-template <int TT, int W>
-__device__ __forceinline__ void down_row(const MlpDec &a, int wj, u32x4 wd, u32x4 u, float so, const Lds<TT, W> &s,
-                                         float (&p)[TT]) {
-    constexpr int L = W / 8;
-    const DownLane<W> dl;
-    const bool in = 8 * dl.c < wj;
+// U_d[o][k] for the lane's rank slots (rd > 0): piece c of the row when rd is
+// a multiple of 8, else entry c in the low half of the first word; the piece
+// or entry is clamped into the row, so slots past rd hold copies that
+// down_row masks out (the mask is applied where the value is used, so that no
+// load has to have arrived when the next is issued).
+__device__ __forceinline__ u32x4 load_u_piece(const MlpDec &a, int c, int o) {
+    const int rd = a.rd;
+    const uint16_t *row = a.Ud + (size_t)min(o, a.D - 1) * rd;
+    if (rd % 8 == 0) return ldg(reinterpret_cast<const u32x4 *>(row) + min(c, rd / 8 - 1));
+    return u32x4{(uint32_t)ldg(row + min(c, rd - 1)), 0u, 0u, 0u};
+}
+
+// What every down row of the lane uses: its 16-byte piece of h and its vj
+// slots, per token.
+template <int TT>
+struct DownIn {
+    u32x4 h[TT];
+    float v[TT][8];
+    bool uok;   // the lane has rank slots below rd
+};
+template <int TT>
+__device__ __forceinline__ void load_down_in(const MlpDec &a, const Lds<TT> &s, DownIn<TT> &d) {
+    const DownLane dl;
+    int k0;
+    d.uok = rank_slot(a.rd, dl.c, 0, k0);
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-        const u32x4 hv = reinterpret_cast<const u32x4 *>(s.h[t])[dl.c];
-        const float m = group_sum_lanes<L>(in ? dot8(wd, hv, 0.f) : 0.f);
-        const float rt = a.rd > 0 ? group_sum_lanes<L>(lane_rank_term<TT, W>(a, u, s, t)) : 0.f;
-        p[t] = so * m + rt;
+        d.h[t] = lds_ld(reinterpret_cast<const u32x4 *>(s.h[t]) + dl.c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            int k;
+            const bool ok = rank_slot(a.rd, dl.c, e, k);
+            const float v = lds_ld(&s.vj[t][min(k, kMaxRank - 1)]);
+            d.v[t][e] = ok ? v : 0.f;
+        }
+    }
+}
+
+// p_j[t][o] of one down row, on every lane of the row's kL-lane group: the sum
+// over the group's lanes of s[o] * (W0 h over the lane's 8 inputs) + (U vj over
+// the lane's rank slots).
+template <int TT>
+__device__ __forceinline__ void down_row(const Part &pt, u32x4 wd, u32x4 u, float so, const DownIn<TT> &d,
+                                         float (&p)[TT]) {
+    const DownLane dl;
+    const bool in = 8 * dl.c < pt.wj;
+    const u32x4 z{0u, 0u, 0u, 0u};
+    u = d.uok ? u : z;
+    const float uk[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                         bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        float rt = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rt += uk[e] * d.v[t][e];
+        const float m = in ? dot8(wd, d.h[t], 0.f) : 0.f;
+        p[t] = group_sum_lanes<kL>(so * m + rt);
     }
 }
 
 __device__ __forceinline__ unsigned long long *part_word(const MlpDec &a, int q, int j, int t, int tt, int oo) {
-    return a.part + (((size_t)q * a.NS + j) * tt + t) * kMlpGroup + oo;
+    return a.part + ((q * a.NS + j) * tt + t) * kMlpGroup + oo;   // below 2^20 words
 }
 
-// The lane's down rows (every pass): W0 pieces of the slice, U pieces, s.
+// The part's down rows (every pass): W0 pieces of the slice, U pieces, s.
 struct DownRows {
     u32x4 wd[kPB];
     u32x4 u[kPB];
     float so[kPB];
 };
-template <int W>
-__device__ __forceinline__ void load_down_w0(const MlpDec &a, int i0, int wj, DownRows &b) {
-    const DownLane<W> dl;
+__device__ __forceinline__ void load_down_w0(const MlpDec &a, const Part &pt, int o0, DownRows &b) {
+    const DownLane dl;
 #pragma unroll
-    for (int m = 0; m < kPB; ++m) b.wd[m] = load_down_piece<W>(a, i0, wj, dl.row(m));
+    for (int m = 0; m < kPB; ++m) b.wd[m] = load_down_piece(a, pt, dl.row(o0, m));
 }
-template <int W>
-__device__ __forceinline__ void load_down_us(const MlpDec &a, DownRows &b) {
-    const DownLane<W> dl;
+// One wave-uniform branch each for the U layout and for s, outside the row
+// loops, so that every load of a loop is issued before any is waited for.
+__device__ __forceinline__ void load_down_us(const MlpDec &a, int o0, DownRows &b) {
+    const DownLane dl;
+    const int rd = a.rd;
+    if (rd > 0 && rd % 8 == 0) {
 #pragma unroll
-    for (int m = 0; m < kPB; ++m) {
-        const int o = min(dl.row(m), a.D - 1);
-        b.u[m] = a.rd > 0 ? load_u_piece(a, dl.c, o) : u32x4{0u, 0u, 0u, 0u};
-        b.so[m] = a.sd ? ldg(a.sd + o) : 1.f;
+        for (int m = 0; m < kPB; ++m) {
+            const int o = min(dl.row(o0, m), a.D - 1);
+            b.u[m] = ldg(reinterpret_cast<const u32x4 *>(a.Ud + (size_t)o * rd) + min(dl.c, rd / 8 - 1));
+        }
+    } else if (rd > 0) {
+#pragma unroll
+        for (int m = 0; m < kPB; ++m) {
+            const int o = min(dl.row(o0, m), a.D - 1);
+            b.u[m] = u32x4{(uint32_t)ldg(a.Ud + (size_t)o * rd + min(dl.c, rd - 1)), 0u, 0u, 0u};
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < kPB; ++m) b.u[m] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (a.sd) {
+#pragma unroll
+        for (int m = 0; m < kPB; ++m) b.so[m] = ldg(a.sd + min(dl.row(o0, m), a.D - 1));
+    } else {
+#pragma unroll
+        for (int m = 0; m < kPB; ++m) b.so[m] = 1.f;
     }
 }
 
-// Every down row of slice j as tagged words.
-template <int TT, int W>
-__device__ __forceinline__ void down_all_rows(const MlpDec &a, int j, int wj, const DownRows &b, const Lds<TT, W> &s,
-                                              unsigned long long tag) {
-    const DownLane<W> dl;
+// The part's down rows [o0, o1) of slice j as tagged words.
+template <int TT>
+__device__ __forceinline__ void down_part_rows(const MlpDec &a, const Part &pt, int o0, int o1, const DownRows &b,
+                                               const DownIn<TT> &d, unsigned long long tag) {
+    static_assert(kRW == kMlpGroup, "a wave's rows of one pass are one output group");
+    const DownLane dl;
     const int tn = min(TT, a.gu.T - a.gu.t0);
+    // o0 is a multiple of 8, so the lane's row of pass m is entry ro of output
+    // group o0 / 8 + kWaves m + q: its words lie a fixed stride apart per pass.
+    unsigned long long *w = part_word(a, o0 / kMlpGroup + dl.q, pt.j, 0, TT, dl.ro);
+    const int pass_words = kWaves * a.NS * TT * kMlpGroup;
 #pragma unroll
     for (int m = 0; m < kPB; ++m) {
-        const int o = dl.row(m);
-        if (o - dl.ro >= a.D) break;   // wave-uniform: no row of this pass exists
+        const int o = dl.row(o0, m);
+        if (o - dl.ro >= o1) break;   // wave-uniform: no row of this pass exists
         float p[TT];
-        down_row<TT, W>(a, wj, b.wd[m], b.u[m], b.so[m], s, p);
-        if (dl.c == 0 && o < a.D) {
-            const int q = o / kMlpGroup, oo = o % kMlpGroup;
-            for (int t = 0; t < tn; ++t)
-                __hip_atomic_store(part_word(a, q, j, t, TT, oo), tag | __float_as_uint(p[t]), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        down_row<TT>(pt, b.wd[m], b.u[m], b.so[m], d, p);
+        if (dl.c == 0 && o < o1) {
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+                if (t < tn)
+                    __hip_atomic_store(w + m * pass_words + t * kMlpGroup, tag | __float_as_uint(p[t]),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
 // p_j for the rows of output group q only (a reducer computing a slice whose
-// words did not come): wave 0, rows 8q .. 8q + 7, the same per-row arithmetic.
-template <int TT, int W>
-__device__ __forceinline__ void down_group_rows(const MlpDec &a, int j, int q, int i0, int wj, const Lds<TT, W> &s,
+// words did not come): wave 0, rows 8q .. 8q + 7 (one pass of kRW = 8 rows),
+// the same per-row arithmetic.
+template <int TT>
+__device__ __forceinline__ void down_group_rows(const MlpDec &a, const Part &pt, int q, const Lds<TT> &s,
                                                 unsigned long long tag) {
-    constexpr int RW = kWave / (W / 8);
-    const DownLane<W> dl;
+    static_assert(kRW == kMlpGroup, "one pass of a wave covers one output group");
+    const DownLane dl;
     const int tn = min(TT, a.gu.T - a.gu.t0);
     if (dl.q != 0) return;
-    for (int r0 = 0; r0 < kMlpGroup; r0 += RW) {
-        const int o = q * kMlpGroup + r0 + dl.ro;
-        const bool mine = r0 + dl.ro < kMlpGroup;
-        const u32x4 wd = load_down_piece<W>(a, i0, wj, o);
-        const u32x4 u = a.rd > 0 ? load_u_piece(a, dl.c, o) : u32x4{0u, 0u, 0u, 0u};
-        const float so = a.sd ? ldg(a.sd + min(o, a.D - 1)) : 1.f;
-        float p[TT];
-        down_row<TT, W>(a, wj, wd, u, so, s, p);
-        if (dl.c == 0 && mine && o < a.D)
-            for (int t = 0; t < tn; ++t)
-                __hip_atomic_store(part_word(a, q, j, t, TT, o % kMlpGroup), tag | __float_as_uint(p[t]),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int o = q * kMlpGroup + dl.ro;
+    const u32x4 wd = load_down_piece(a, pt, o);
+    const u32x4 u = a.rd > 0 ? load_u_piece(a, dl.c, o) : u32x4{0u, 0u, 0u, 0u};
+    const float so = a.sd ? ldg(a.sd + min(o, a.D - 1)) : 1.f;
+    DownIn<TT> d;
+    load_down_in<TT>(a, s, d);
+    float p[TT];
+    down_row<TT>(pt, wd, u, so, d, p);
+    if (dl.c == 0 && o < a.D)
+        for (int t = 0; t < tn; ++t)
+            __hip_atomic_store(part_word(a, q, pt.j, t, TT, o % kMlpGroup), tag | __float_as_uint(p[t]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- the gate/up V^T x from this launch's producers ----
+
+// Read ahead: thread per (child, token, k) item loads that item's tagged slice
+// words (at most kEarlyWords slices, when there are at most kThreads items);
+// early_check then adds them in the association of gather_tagged_full (one
+// group of 16 slices, padded with +0) if every word carries the tag.
+struct EarlyVtx {
+    unsigned long long w[kEarlyWords];
+};
+template <int TT>
+__device__ __forceinline__ void early_issue(const GemvF &g, int n_items, EarlyVtx &e) {
+    const int item = min((int)threadIdx.x, max(n_items - 1, 0));
+    int c, t, k;
+    vtx_item(g, TT, item, c, t, k);
+    const int r = ch_r(g, c);
+    const unsigned long long *base = tagged_base(g, c) + t * r + k;
+#pragma unroll
+    for (int u = 0; u < kEarlyWords; ++u) e.w[u] = ld_word(base + (size_t)min(u, g.S - 1) * (TT * r));
+}
+template <int TT>
+__device__ __forceinline__ bool early_check(const GemvF &g, int n_items, uint32_t tag, const EarlyVtx &e,
+                                            Lds<TT> &s) {
+    const int item = threadIdx.x;
+    if (item >= n_items) return true;
+    int c, t, k;
+    vtx_item(g, TT, item, c, t, k);
+    const bool need = g.t0 + t < g.T;
+    bool ok = true;
+    float gs = 0.f;
+#pragma unroll
+    for (int u = 0; u < kEarlyWords; ++u) {
+        ok = ok && (u >= g.S || !need || word_is(e.w[u], tag));
+        gs += u < g.S ? word_value(e.w[u]) : 0.f;
     }
+    float sum = 0.f;
+    sum += gs;
+    if (ok) s.vs[c][t][k] = sum;
+    return ok;
 }
 
-// Slice j's small operands: gate/up U rows and down V rows into LDS by
-// direct-to-LDS copies (the caller waits, wait_vm<0> and a barrier, before
-// using them); the thread's gate/up s value (threads below 2 W) is returned,
-// to be written to LDS with put_scale once it has arrived.
-template <int TT, int W>
-__device__ __forceinline__ float stage_slice(const MlpDec &a, int i0, int wj, Lds<TT, W> &s) {
-    const int rg = a.gu.ch[0].r, ru = a.gu.ch[1].r, rd = a.rd;
-    if (rg > 0) copy_to_lds(a.gu.ch[0].U + (size_t)i0 * rg, wj * rg / 8, s.ug);
-    if (ru > 0) copy_to_lds(a.gu.ch[1].U + (size_t)i0 * ru, wj * ru / 8, s.uu);
-    if (rd > 0) copy_to_lds(a.Vd + (size_t)i0 * rd, wj * rd / 8, s.vd);
-    const int tid = threadIdx.x, p = (tid / W) & 1, i = tid % W;
-    const float *sp = p ? a.gu.ch[1].s : a.gu.ch[0].s;
-    const float *sg = sp ? sp + i0 + min(i, wj - 1) : reinterpret_cast<const float *>(a.gu.x);
-    const float v = ldg(sg);
-    return sp ? v : 1.f;
-}
-template <int TT, int W>
-__device__ __forceinline__ void put_scale(float v, Lds<TT, W> &s) {
-    const int tid = threadIdx.x;
-    if (tid < 2 * W) s.sl[tid / W][tid % W] = v;
-}
-
-// Gate/up V^T x of the pass from this launch's producers (or computed here
-// when the wait runs out), into s.vs: one thread per (child, token, k) item
-// reads that item's tagged slice words, groups of 16 slices in order. (The
-// split mapping of the decode GEMV, thread per (item, group), computed wrong
-// sums at four tokens per pass when compiled into this kernel, with other
-// loads' registers live across it; it is not used here.) Ends with a barrier.
-template <int TT, int W>
-__device__ __forceinline__ void gather_gateup_vtx(const MlpDec &a, Lds<TT, W> &s) {
+// Gate/up V^T x into s.vs: from the words read ahead when they all carried the
+// tag, else by reading them again (bounded), else computed here. Ends with a
+// barrier.
+template <int TT>
+__device__ __forceinline__ void finish_gateup_vtx(const MlpDec &a, Lds<TT> &s, bool early, const EarlyVtx &e) {
     const GemvF &g = a.gu;
-    const int tid = threadIdx.x;
     const int n_items = vtx_items(g, TT);
     if (n_items == 0) return;
+    const bool ready = early && early_check<TT>(g, n_items, s.tag, e, s);
+    if (!__syncthreads_or(!ready)) return;
     const int retries = g.spin_limit - 1;
     const bool got = g.spin_limit > 0 && gather_tagged_full<TT>(g, n_items, s.tag, retries, s.vs);
-    const bool fallback = __syncthreads_or(!got);
-    if (fallback) {
-        if (tid == 0)
+    if (__syncthreads_or(!got)) {
+        if (threadIdx.x == 0)
             __hip_atomic_fetch_add(g.sync + kSyncFallbackWord, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         vtx_fallback<TT>(g, n_items, s.vs, s.vred, s.xstage, s.fgs);
     }
@@ -468,7 +657,7 @@ __device__ __forceinline__ void gather_gateup_vtx(const MlpDec &a, Lds<TT, W> &s
 // adds them in order. A word without this launch's tag is read again, at most
 // `retries` more times; outputs past d_out count as present. False when a wait
 // ran out.
-template <int TT, int W>
+template <int TT>
 __device__ __forceinline__ bool reduce_poll(const MlpDec &a, int q, int t, uint32_t tag, int retries, float &sum) {
     const int tid = threadIdx.x, oo = tid % kMlpGroup, js = tid / kMlpGroup;
     const bool real = q * kMlpGroup + oo < a.D;
@@ -478,10 +667,7 @@ __device__ __forceinline__ bool reduce_poll(const MlpDec &a, int q, int t, uint3
     for (int spin = 0;; ++spin) {
         bool ready = true;
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const int jj = min(js + 32 * m, a.NS - 1);
-            w[m] = ld_word(part_word(a, q, jj, t, TT, oo));
-        }
+        for (int m = 0; m < M; ++m) w[m] = ld_word(part_word(a, q, min(js + 32 * m, a.NS - 1), t, TT, oo));
 #pragma unroll
         for (int m = 0; m < M; ++m) ready = ready && (!real || js + 32 * m >= a.NS || word_is(w[m], tag));
         if (ready) {
@@ -497,62 +683,121 @@ __device__ __forceinline__ bool reduce_poll(const MlpDec &a, int q, int t, uint3
     return ok;
 }
 
-template <int TT, int W>
+// The whole slice j's h in LDS, computed here part by part (a reducer whose
+// wait for slice j's words ran out): U rows, s, gate/up rows and h of every
+// part, then the slice's V rows.
+template <int TT>
+__device__ void slice_h_here(const MlpDec &a, int j, Lds<TT> &s) {
+    for (int p = 0; p < a.P; ++p) {
+        const Part pt = make_part(a, j, p);
+        __syncthreads();
+        const float sv = stage_part<TT>(a, pt, s);
+        wait_vm<0>();
+        put_scale<TT>(sv, s);
+        __syncthreads();
+        gateup_rows<TT>(a, pt, s, []() {}, []() {});
+        __syncthreads();
+        form_h<TT>(a, pt, s);
+    }
+    stage_vd<TT>(a, make_part(a, j, 0), s);
+    wait_vm<0>();
+    __syncthreads();
+}
+
+template <int TT>
 __global__ __launch_bounds__(kThreads) void mlp_dec_kernel(MlpDec a) {
-    __shared__ Lds<TT, W> s;
+    __shared__ Lds<TT> s;
     const GemvF &g = a.gu;
     const int tid = threadIdx.x;
     if ((int)blockIdx.x < g.n_prod) {
         vtx_produce<TT>(g, s.vred, s.xstage, &s.tag, s.gsum, s.vs);
         return;
     }
-    const int j = slice_of_block(blockIdx.x, g.n_prod, a.NS);
-    const int i0 = j * W, wj = min(W, a.F - i0);
+    const int wg = blockIdx.x - g.n_prod;          // this workgroup among the slices' workgroups
+    const Part pt = make_part(a, wg / a.P, wg % a.P);
     const int tn = min(TT, g.T - g.t0);
+    const int o0 = pt.p * a.Dp, o1 = min(a.D, o0 + a.Dp);   // the part's down rows
+    const int n_items = vtx_items(g, TT);
+    const bool early = n_items <= kThreads && g.S <= kEarlyWords && g.spin_limit > 0;
 
-    // Issue order: the first gate/up batch (and its x), the ticket, the slice's
-    // down columns into LDS; they stream while gate/up is reduced.
-    // Issue order per wave: the first gate/up batch (and its x), the ticket
-    // (thread 0); once the wave's gate/up loads are used, the slice's down
-    // columns (into the registers the gate/up batch held), the small operands
-    // and the down U / s, all in flight while V^T x is gathered.
+    // Issue order per wave: the first gate/up batch (two row steps and their
+    // x), the ticket (thread 0), the part's down W0 pieces (registers); the
+    // first batch is then used while the rest streams. Behind the second batch
+    // (or right after the first when there is none): the slice's small operands
+    // (direct-to-LDS) and the read-ahead of the gate/up V^T x words.
     unsigned long long ticket;   // thread 0 only; left undefined elsewhere, so that no copy
                                  // of the atomic's result (and no wait for it) is needed here
-    gateup_stream<TT, W>(a, i0, wj, s, [&]() {
-        if (tid == 0) ticket = take_ticket(g);
-        if (blockIdx.x == 0) advance_empty_copies(g);
-    });
     DownRows dr;
-    load_down_w0<W>(a, i0, wj, dr);
-    __syncthreads();
+    EarlyVtx ev;
+    float sv = 0.f;
+    bool staged = false;
+    auto stage_and_peek = [&]() {
+        if (staged) return;
+        staged = true;
+        sv = stage_part<TT>(a, pt, s);
+        stage_vd<TT>(a, pt, s);
+        if (early) early_issue<TT>(g, n_items, ev);
+    };
+    gateup_rows<TT>(
+        a, pt, s,
+        [&]() {
+            if (tid == 0) ticket = take_ticket(g);
+            if (blockIdx.x == 0) advance_empty_copies(g);
+            load_down_w0(a, pt, o0, dr);
+        },
+        stage_and_peek);
+    stage_and_peek();   // when the part has one batch only
     if (tid == 0) s.tag = ticket_tag(ticket);
-    const float sv = stage_slice<TT, W>(a, i0, wj, s);
-    load_down_us<W>(a, dr);
     __syncthreads();
-    gather_gateup_vtx<TT, W>(a, s);
+    finish_gateup_vtx<TT>(a, s, early, ev);
     wait_vm<0>();
-    put_scale<TT, W>(sv, s);
+    load_down_us(a, o0, dr);   // in flight while h is formed and exchanged
+    put_scale<TT>(sv, s);
     __syncthreads();
-    form_h<TT, W>(a, wj, s);
-    if (a.rd > 0) form_vj<TT, W>(a, wj, s);
+    form_h<TT>(a, pt, s);
     const uint32_t tag32 = s.tag;
     const unsigned long long tag = (unsigned long long)tag32 << 32;
-    down_all_rows<TT, W>(a, j, wj, dr, s, tag);
+
+    // The other parts' h rows of the slice.
+    if (a.P > 1) {
+        publish_h<TT>(a, pt, s, tag);
+        const bool got = g.spin_limit > 0 && fetch_h<TT>(a, pt, s, tag32, g.spin_limit - 1);
+        if (__syncthreads_or(!got)) {
+            // Compute every other part's h rows here, with the same arithmetic.
+            for (int p = 0; p < a.P; ++p) {
+                if (p == pt.p) continue;
+                const Part op = make_part(a, pt.j, p);
+                __syncthreads();
+                const float svp = stage_part<TT>(a, op, s);
+                wait_vm<0>();
+                put_scale<TT>(svp, s);
+                __syncthreads();
+                gateup_rows<TT>(a, op, s, []() {}, []() {});
+                __syncthreads();
+                form_h<TT>(a, op, s);
+            }
+        }
+        __syncthreads();
+    }
+    if (a.rd > 0) form_vj<TT>(a, pt, s);
+    DownIn<TT> din;
+    load_down_in<TT>(a, s, din);
+    down_part_rows<TT>(a, pt, o0, o1, dr, din, tag);
 
     // ---- sums over slices for this workgroup's output groups ----
     const int retries = g.spin_limit - 1;
     const int oo = tid % kMlpGroup, js = tid / kMlpGroup;
-    for (int q = j; q < a.NG; q += a.NS) {
+    for (int q = wg; q < a.NG; q += a.NS * a.P) {
         for (int t = 0; t < tn; ++t) {
             float sum = 0.f;
-            const bool ok = g.spin_limit > 0 && reduce_poll<TT, W>(a, q, t, tag32, retries, sum);
+            const bool ok = g.spin_limit > 0 && reduce_poll<TT>(a, q, t, tag32, retries, sum);
             if (tid == 0) s.miss = 0;
             __syncthreads();
             if (!ok) atomicOr(&s.miss, 1);
             __syncthreads();
             if (s.miss) {
                 // Compute the words of this group that are not there (every
-                // slice's when the wait is switched off), one slice at a time
+                // slice's when the waits are switched off), one slice at a time
                 // with the slice workgroups' arithmetic, then read them back.
                 for (int jj = 0; jj < a.NS; ++jj) {
                     if (tid == 0) s.need = g.spin_limit == 0;
@@ -564,19 +809,12 @@ __global__ __launch_bounds__(kThreads) void mlp_dec_kernel(MlpDec a) {
                     const bool need = s.need;
                     __syncthreads();   // every thread has read s.need before thread 0 resets it
                     if (!need) continue;
-                    const int j0 = jj * W, wjj = min(W, a.F - j0);
-                    const float svj = stage_slice<TT, W>(a, j0, wjj, s);
-                    wait_vm<0>();
-                    put_scale<TT, W>(svj, s);
-                    __syncthreads();
-                    gateup_stream<TT, W>(a, j0, wjj, s, []() {});
-                    __syncthreads();
-                    form_h<TT, W>(a, wjj, s);
-                    if (a.rd > 0) form_vj<TT, W>(a, wjj, s);
-                    down_group_rows<TT, W>(a, jj, q, j0, wjj, s, tag);
+                    slice_h_here<TT>(a, jj, s);
+                    if (a.rd > 0) form_vj<TT>(a, make_part(a, jj, 0), s);
+                    down_group_rows<TT>(a, make_part(a, jj, 0), q, s, tag);
                     __syncthreads();
                 }
-                reduce_poll<TT, W>(a, q, t, tag32, kSpinLimit, sum);
+                reduce_poll<TT>(a, q, t, tag32, kSpinLimit, sum);
             }
             s.red[js][oo] = sum;
             __syncthreads();
@@ -592,39 +830,33 @@ __global__ __launch_bounds__(kThreads) void mlp_dec_kernel(MlpDec a) {
     if (blockIdx.x == 0 && tid == 0) sweep_tagged(g.sync, ticket, tag32);
 }
 
-template <int TT>
-hipError_t launch_w(const MlpDec &a, int W, int grid, hipStream_t stream) {
-    switch (W) {
-        case 32: hipLaunchKernelGGL((mlp_dec_kernel<TT, 32>), dim3(grid), dim3(kThreads), 0, stream, a); break;
-        case 64: hipLaunchKernelGGL((mlp_dec_kernel<TT, 64>), dim3(grid), dim3(kThreads), 0, stream, a); break;
-        default: hipLaunchKernelGGL((mlp_dec_kernel<TT, 128>), dim3(grid), dim3(kThreads), 0, stream, a); break;
-    }
-    return hipGetLastError();
-}
-
 }  // namespace
 
-// Slice width W: the smallest of 32, 64, 128 that keeps the slices within
-// kMlpMaxSlices, holds the down rank in one 16-byte piece per lane (rd a
-// multiple of 8 up to W, or rd up to W / 8) and keeps the slice's down columns
-// within the LDS block.
+// Workgroups per slice P: the fewest of 1, 2, 4, 8 that keep a part's down
+// rows in registers (kMlpDownPasses passes of 32 rows), within 256 slice
+// workgroups (one per compute unit). The down rank must fit one 16-byte piece
+// per lane (a multiple of 8 up to 64, or below 8); the gate/up V^T x read-ahead
+// holds up to 16 slices (d_model up to 2048).
 MlpPlan mlp_dec_plan(int d_model, int F, int d_out, int r_gate, int r_up, int r_down, int T) {
     MlpPlan p;
     const int tt = gemv_tokens_per_pass(d_model, T);
     if (tt == 0 || tt > kInLaunchMaxTok) return p;
-    int W = 0;
-    for (int w = 32; w <= 128 && W == 0; w *= 2) {
-        const bool rank_ok = r_down % 8 == 0 ? r_down <= w : r_down <= w / 8;
-        if ((F + w - 1) / w <= kMlpMaxSlices && rank_ok && (size_t)d_out * (w / 8) * 16 <= (size_t)kMlpDownBytes)
-            W = w;
-    }
-    if (W == 0) return p;
-    const int NS = (F + W - 1) / W;
+    if (r_down % 8 != 0 && r_down >= 8) return p;
+    const int NS = (F + kW - 1) / kW;
+    if (NS > kMlpMaxSlices) return p;
+    // A part's down rows start on a boundary of the output groups of 8.
+    auto part_rows = [&](int c) { return ((d_out + c - 1) / c + kMlpGroup - 1) / kMlpGroup * kMlpGroup; };
+    int P = 0;
+    for (int c = 1; c <= 8 && P == 0; c *= 2)
+        if (part_rows(c) <= kMlpDownPasses * kWaves * kRW && NS * c <= 256) P = c;
+    if (P == 0) return p;
     const int NG = (d_out + kMlpGroup - 1) / kMlpGroup;
     if ((size_t)NG * NS * tt * kMlpGroup > kSyncPartWords) return p;
+    if ((size_t)NS * (kW / 2) * tt > kSyncHxWords) return p;
     p.tt = tt;
-    p.W = W;
     p.NS = NS;
+    p.P = P;
+    p.Dp = part_rows(P);
     p.NG = NG;
     p.slice_len = gemv_slice_len(d_model);
     const int n_v = (r_gate > 0) + (r_up > 0);
@@ -641,13 +873,17 @@ hipError_t launch_mlp_dec(const MlpDec &a, const MlpPlan &p, hipStream_t stream)
     b.gu.vmode = p.n_prod > 0 ? kVtxInLaunch : kVtxNone;
     b.gu.two_level = 0;
     b.NS = p.NS;
+    b.P = p.P;
+    b.WR = kW / p.P;
+    b.Dp = p.Dp;
     b.NG = p.NG;
-    const int grid = p.n_prod + p.NS;
+    const int grid = p.n_prod + p.NS * p.P;
     switch (p.tt) {
-        case 4: return launch_w<4>(b, p.W, grid, stream);
-        case 2: return launch_w<2>(b, p.W, grid, stream);
-        default: return launch_w<1>(b, p.W, grid, stream);
+        case 4: hipLaunchKernelGGL((mlp_dec_kernel<4>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+        case 2: hipLaunchKernelGGL((mlp_dec_kernel<2>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+        default: hipLaunchKernelGGL((mlp_dec_kernel<1>), dim3(grid), dim3(kThreads), 0, stream, b); break;
     }
+    return hipGetLastError();
 }
 
 }  // namespace wl

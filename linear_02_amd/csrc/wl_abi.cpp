@@ -666,11 +666,13 @@ wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta 
     if (regime == 0 || regime == 1) {
         const wl::MlpPlan plan =
             wl::mlp_dec_plan(gate->d_in, d_ff, down->d_out, gate->r, up->r, down->r, T);
-        if (plan.tt > 0) {
+        // Passes of four tokens run faster as two launches (the one-launch
+        // kernel holds too many registers there); regime 1 still forces it.
+        if (plan.tt > 0 && (regime == 1 || plan.tt <= wl::kMlpAutoMaxTok)) {
             // One launch per pass: gate/up, GELU-tanh and down together.
             if (log_on())
-                fprintf(stderr, "wl: mlp d_model=%d d_ff=%d d_out=%d T=%d -> one launch (tt=%d, W=%d, slices=%d)\n",
-                        gate->d_in, d_ff, down->d_out, T, plan.tt, plan.W, plan.NS);
+                fprintf(stderr, "wl: mlp d_model=%d d_ff=%d d_out=%d T=%d -> one launch (tt=%d, slices=%d x %d)\n",
+                        gate->d_in, d_ff, down->d_out, T, plan.tt, plan.NS, plan.P);
             wl::MlpDec a{};
             wl::GemvF &g = a.gu;
             g.ch[0] = gu[0];
@@ -694,6 +696,7 @@ wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta 
             a.D = down->d_out;
             a.F = d_ff;
             a.y = static_cast<uint16_t *>(y);
+            a.hx = reinterpret_cast<unsigned long long *>(w + wl::kSyncHxOffset);
             a.part = reinterpret_cast<unsigned long long *>(w + wl::kSyncPartOffset);
             for (int t0 = 0; t0 < T; t0 += plan.tt) {
                 g.t0 = t0;

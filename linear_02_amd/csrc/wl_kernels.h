@@ -85,7 +85,9 @@ enum { kVtxNone = 0, kVtxPartials = 2, kVtxInLaunch = 3 };
 //   from kSyncFinalOffset     the tagged complete V^T x words, one per (child,
 //                             token, k) item (two-level hand-off),
 //                             kSyncFinalPerChild per child slot
-//   from kSyncPartOffset      the tagged partial outputs of the one-dispatch MLP
+//   from kSyncHxOffset        the one-launch MLP's h, exchanged between the
+//                             workgroups of a slice (kSyncHxWords)
+//   from kSyncPartOffset      the tagged partial outputs of the one-launch MLP
 //                             (kSyncPartWords)
 // Zero before first use (wl_workspace_init); never reset afterwards. Each
 // launch clears one word of the tagged areas that is not its own (walking
@@ -108,8 +110,9 @@ constexpr size_t kGemvTaggedPerChild = (size_t)kGemvMaxSlices * kInLaunchMaxTok 
 constexpr int kSyncTaggedChildren = 8;
 constexpr size_t kSyncFinalOffset = kSyncTaggedOffset + kSyncTaggedChildren * kGemvTaggedPerChild * 8;
 constexpr size_t kSyncFinalPerChild = (size_t)kInLaunchMaxTok * kMaxRank;
-constexpr size_t kSyncPartOffset =
-    (kSyncFinalOffset + kSyncTaggedChildren * kSyncFinalPerChild * 8 + 65535) / 65536 * 65536;
+constexpr size_t kSyncHxOffset = kSyncFinalOffset + kSyncTaggedChildren * kSyncFinalPerChild * 8;
+constexpr size_t kSyncHxWords = (size_t)1 << 15;
+constexpr size_t kSyncPartOffset = (kSyncHxOffset + kSyncHxWords * 8 + 65535) / 65536 * 65536;
 constexpr size_t kSyncPartWords = (size_t)1 << 20;
 constexpr size_t kSyncBytes = kSyncPartOffset + kSyncPartWords * 8;
 constexpr size_t kSweepWords = (kSyncBytes - kSyncTaggedOffset) / 8;
@@ -157,30 +160,35 @@ hipError_t launch_gemv(const GemvF &g, const GemvPlan &plan, int tt, hipStream_t
 // ---------------------------------------------------------------------------
 // The MLP at decode sizes (1 to kInLaunchMaxTok tokens per pass) in one launch.
 // The first n_prod workgroups produce the gate/up pair's V^T x slices (the
-// in-launch hand-off of GemvF). Then one workgroup per slice j of W
-// consecutive intermediate rows forms, for the pass's tokens,
-//   h[t][i]   = bf16( gelu_tanh(gate[t][i]) * up[t][i] )          i in slice j
+// in-launch hand-off of GemvF). The intermediate axis is cut into slices of
+// kMlpSlice rows, each taken by P workgroups: part p forms, for the pass's
+// tokens, h[t][i] = bf16( gelu_tanh(gate[t][i]) * up[t][i] ) for its kMlpSlice /
+// P rows of the slice, and the slice's workgroups exchange their h rows through
+// tagged words. Part p then forms the slice's share of down for its d_out / P
+// output rows o,
 //   p_j[t][o] = s_d[o] * sum_{i in j} W0_d[o][i] h[t][i]
-//               + sum_k U_d[o][k] * sum_{i in j} V_d[i][k] h[t][i]   every output o
-// (the down projection split along its input axis, so no workgroup needs
-// another's h), and stores p_j as tagged words. Each slice workgroup then adds,
-// for groups of kMlpGroup outputs, the words of every slice in slice order and
-// rounds once: y[t][o] = bf16( sum_j p_j[t][o] ). A wait that runs out
-// computes the missing slices itself, with the same arithmetic.
+//               + sum_k U_d[o][k] * sum_{i in j} V_d[i][k] h[t][i]
+// (down split along its input axis, 128-byte pieces of each row), stored as
+// tagged words; groups of kMlpGroup outputs are added over the slices in slice
+// order and rounded once: y[t][o] = bf16( sum_j p_j[t][o] ). A wait that runs
+// out computes what it waited for itself, with the same arithmetic.
+constexpr int kMlpSlice = 64;        // intermediate rows per slice (down inputs, 128 bytes)
 constexpr int kMlpGroup = 8;         // outputs per reduction group
-constexpr int kMlpMaxSlices = 256;   // slices (workgroups besides the producers)
-constexpr int kMlpDownBytes = 73728;   // a slice's down columns (d_out x W bf16), held in registers
+constexpr int kMlpMaxSlices = 256;   // slices
+constexpr int kMlpDownPasses = 18;   // down rows per workgroup <= kMlpDownPasses x 32 (held in registers)
+constexpr int kMlpAutoMaxTok = 2;    // widest pass the automatic regime gives the one-launch MLP
 struct MlpDec {
     GemvF gu;                        // gate (ch[0]) / up (ch[1]) pair: x, tokens, producers, hand-off
     const uint16_t *W0d, *Ud, *Vd;   // down: bf16 [D][F], [D][rd], [F][rd]
     const float *sd;                 // fp32 [D], or null: every s is 1
     int rd, D, F;
-    int NS, NG;                      // slices, output groups
+    int NS, P, WR, Dp, NG;           // slices, workgroups per slice, their rows, down rows per part, groups
     uint16_t *y;                     // bf16 [T][D]
-    unsigned long long *part;        // tagged words [NG][NS][tt][kMlpGroup]
+    unsigned long long *hx;          // tagged h words [NS][kMlpSlice / 2][tt]
+    unsigned long long *part;        // tagged partial words [NG][NS][tt][kMlpGroup]
 };
 struct MlpPlan {
-    int tt = 0, W = 0, NS = 0, NG = 0, S = 0, slice_len = 0, n_prod = 0;
+    int tt = 0, NS = 0, P = 0, Dp = 0, NG = 0, S = 0, slice_len = 0, n_prod = 0;
 };
 // tt = 0 when the one-launch MLP does not serve this shape.
 MlpPlan mlp_dec_plan(int d_model, int F, int d_out, int r_gate, int r_up, int r_down, int T);

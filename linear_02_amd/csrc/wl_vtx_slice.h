@@ -44,7 +44,7 @@ __device__ __forceinline__ void vtx_slice_sums(const uint16_t *__restrict__ V, i
             const int i = ib + u * G;
             const bool in = i < len;
             const int ic = min(i, len - 1);
-            const float vv = bf16_f(V[(size_t)(i0 + ic) * r + k]);
+            const float vv = bf16_f(ldg(V + (size_t)(i0 + ic) * r + k));
             v[u] = in ? vv : 0.f;
 #pragma unroll
             for (int t = 0; t < TB; ++t) xv[u][t] = x_at(ic, t);

@@ -26,7 +26,7 @@ ABI_VERSION = 5
 # The first SYNC_BYTES of a projection workspace are the library's sync area:
 # cleared by wl_workspace_init (new_workspace does it) before first use, then
 # written only by the library's calls.
-SYNC_BYTES = 9502720
+SYNC_BYTES = 9764864
 _FALLBACK_WORD = 511   # int64 word of the sync area counting decode workgroups that stopped waiting
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error", 4: "workspace too small"}
 

@@ -219,9 +219,9 @@ def test_workspace_starts_with_the_sync_area(wl):
         th = theta(d_in=d_in, d_out=d_out, r=r)
         arr = (ctypes.POINTER(wl.Theta) * 1)(ctypes.pointer(th))
         assert wl.lib.wl_workspace_bytes(0, arr, 1, 1) >= wl.SYNC_BYTES + 256
-    assert wl.SYNC_BYTES == wl.lib.wl_sync_bytes() == 9502720
+    assert wl.SYNC_BYTES == wl.lib.wl_sync_bytes() == 9764864
     text = open(HEADER).read()
-    assert re.search(r"#define WL_SYNC_BYTES 9502720\b", text)
+    assert re.search(r"#define WL_SYNC_BYTES 9764864\b", text)
     assert re.search(r"#define WL_ABI_VERSION 5\b", text)
 
 

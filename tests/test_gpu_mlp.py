@@ -3,12 +3,13 @@
 The launch splits the down projection along its input axis: each slice
 workgroup forms h for its rows of the intermediate axis and the slice's share
 of every down output, and groups of outputs are added over the slices in a
-fixed order. Checked here against the oracle on shapes that reach every slice
-width (32, 64, 128), ragged slices and output groups, d_out != d_model, down
-ranks held as whole 16-byte pieces or as single entries, no low-rank term, and
-s = None; bit for bit on integer cases; and bit for bit against its own forced
+fixed order. Checked here against the oracle on shapes that reach one, two, four
+and eight workgroups per slice, ragged slices (a part of the last slice empty)
+and output groups, d_out != d_model, down ranks held as whole 16-byte pieces or
+as single entries, no low-rank term, and s = None; bit for bit on integer cases; and bit for bit against its own forced
 fallback (spin limit 0: every workgroup computes the gate/up V^T x itself and
-every reduction recomputes every slice's share). The ticket counters show that
+every slice's workgroups compute each other's h rows, and every reduction
+recomputes every slice's share). The ticket counters show that
 the one-launch kernel ran: exactly one launch per pass of tokens.
 """
 from __future__ import annotations
@@ -27,7 +28,6 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 STRIDE = 1 << 24
 COPIES = 64
-DOWN_LDS_BYTES = 73728
 
 
 @pytest.fixture(scope="module")
@@ -49,12 +49,17 @@ def tokens_per_pass(T: int) -> int:
     return tt
 
 
-def slice_width(d_ff: int, d_out: int, r_down: int) -> int:
-    """The one-launch plan's slice width, or 0 when the shape takes two launches."""
-    for w in (32, 64, 128):
-        rank_ok = r_down <= w if r_down % 8 == 0 else r_down <= w // 8
-        if -(-d_ff // w) <= 256 and rank_ok and d_out * (w // 8) * 16 <= DOWN_LDS_BYTES:
-            return w
+def slice_workgroups(d_ff: int, d_out: int, r_down: int) -> int:
+    """Workgroups of the one-launch plan besides the producers (slices of 64
+    intermediate rows x parts per slice), or 0 when the shape takes two launches."""
+    if r_down % 8 != 0 and r_down >= 8:
+        return 0
+    n_slices = -(-d_ff // 64)
+    if n_slices > 256:
+        return 0
+    for parts in (1, 2, 4, 8):
+        if -(-d_out // parts) <= 18 * 32 and n_slices * parts <= 256:
+            return n_slices * parts
     return 0
 
 
@@ -67,10 +72,12 @@ CASES = [
     (1152, 6912, 1152, (32, 32, 32), False),   # s = None everywhere
     (264, 1000, 264, (16, 16, 3), True),       # ragged last slice (8 wide), down rank as entries
     (136, 520, 100, (17, 9, 24), True),        # d_out 100: ragged output group; d_model 136
-    (1152, 64, 1152, (8, 8, 8), True),         # two slices
-    (512, 16384, 512, (32, 32, 40), True),     # down rank 40: slices of 64
-    (256, 32768, 256, (8, 8, 64), True),       # slices of 128, down rank 64
-    (4096, 2048, 1024, (32, 32, 32), True),    # long gate/up rows: several load batches
+    (1152, 64, 1152, (8, 8, 8), True),         # one slice, two workgroups
+    (512, 16384, 512, (32, 32, 40), True),     # 256 slices of one workgroup, down rank 40
+    (256, 8192, 256, (8, 8, 64), True),        # one workgroup per slice, down rank 64
+    (2048, 2048, 2304, (32, 32, 32), True),    # four workgroups per slice; long gate/up rows
+    (1024, 1032, 4096, (16, 16, 16), True),    # eight workgroups per slice; last slice 8 rows wide
+    (4096, 2048, 1024, (32, 32, 32), True),    # 32 V^T x slices: the words are read after the stream
 ]
 
 
@@ -95,7 +102,7 @@ def counters(ws: torch.Tensor) -> np.ndarray:
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_one_launch_mlp_matches_oracle(wl, orc, case, T):
     d_model, d_ff, d_out, ranks, _ = CASES[case]
-    assert slice_width(d_ff, d_out, ranks[2]) > 0
+    assert slice_workgroups(d_ff, d_out, ranks[2]) > 0
     gate, up, down, x = make(case, T, seed=5000 + 10 * case + T)
     dths = [wl.theta_to(th, DEV) for th in (gate, up, down)]
     ws = wl.new_workspace(wl.workspace_bytes(wl.OP_MLP, dths, T), DEV)
@@ -110,7 +117,8 @@ def test_one_launch_mlp_matches_oracle(wl, orc, case, T):
     check(y, y_ref, bound, f"one-launch mlp {CASES[case]} T={T}")
 
 
-@pytest.mark.parametrize("case,T", [(0, 1), (0, 4), (1, 3), (2, 2), (3, 1), (5, 2), (6, 4), (8, 1), (9, 1), (10, 3)])
+@pytest.mark.parametrize("case,T", [(0, 1), (0, 4), (1, 3), (2, 2), (3, 1), (5, 2), (6, 4), (8, 1), (9, 1), (10, 3),
+                                    (11, 2), (12, 1)])
 def test_one_launch_mlp_fallback_is_bitwise(wl, case, T):
     gate, up, down, x = make(case, T, seed=5500 + 10 * case + T)
     dths = [wl.theta_to(th, DEV) for th in (gate, up, down)]
@@ -131,8 +139,7 @@ def test_one_launch_mlp_fallback_is_bitwise(wl, case, T):
     passes = -(-T // tokens_per_pass(T))
     assert (w[:COPIES] == 3 * passes * STRIDE).all()
     d_model, d_ff, d_out, ranks, _ = CASES[case]
-    n_slices = -(-d_ff // slice_width(d_ff, d_out, ranks[2]))
-    expect_fb = passes * n_slices if ranks[0] + ranks[1] > 0 else 0
+    expect_fb = passes * slice_workgroups(d_ff, d_out, ranks[2]) if ranks[0] + ranks[1] > 0 else 0
     assert w[511] == expect_fb, f"fallback count {w[511]}, expected {expect_fb}"
 
 
