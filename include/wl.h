@@ -95,6 +95,8 @@ extern "C" {
 
 /* Bytes at the start of a projection workspace that hold the sync area. */
 #define WL_SYNC_BYTES 9764864
+/* Bytes of the static workspace of wl_linear_static, per device. */
+#define WL_STATIC_SCRATCH_BYTES 33554432
 
 typedef enum {
     WL_OK = 0,
@@ -143,6 +145,22 @@ size_t wl_workspace_bytes(int32_t op, const wl_theta *const *th, int32_t n_th, i
  * weightless", "Set the fast path on NVIDIA") when W0 is a materialized W_eff. */
 wl_status wl_linear(const wl_theta *th, const void *x, void *y, int32_t T,
                     void *ws, size_t ws_bytes, void *hip_stream);
+
+/* wl_linear without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Arguments, result and errors as wl_linear; the
+ * workspace is a static device array of WL_STATIC_SCRATCH_BYTES that the
+ * library holds on each device it runs on until the process ends. The call
+ * allocates nothing. Its first call on a device looks the array up and
+ * enqueues on hip_stream a fill kernel that clears the array's sync area,
+ * ahead of its own kernels. Every call on a device shares that device's array
+ * and the array keeps the last call's contents, so calls that overlap on one
+ * device (other streams, other host threads) race and must be serialized by
+ * the caller; wl_linear with workspaces of its own does not share it. A call
+ * whose workspace would exceed WL_STATIC_SCRATCH_BYTES (the decode and
+ * few-token kernels of the Gemma-3 shapes fit; long prefill passes may not)
+ * fails with WL_ERR_WORKSPACE before launching anything. */
+wl_status wl_linear_static(const wl_theta *th, const void *x, void *y, int32_t T, void *hip_stream);
 
 /* Q/K/V fusion ("In-kernel reconstruction", "Q/K/V fusion"): the three
  * attention projections that read the same x, computed in one pass over the

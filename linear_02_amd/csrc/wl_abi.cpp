@@ -588,6 +588,25 @@ wl_status wl_linear(const wl_theta *th, const void *x, void *y, int32_t T, void 
     return ok();
 }
 
+static_assert(WL_STATIC_SCRATCH_BYTES == wl::kStaticScratchBytes, "static scratch size");
+static_assert(WL_STATIC_SCRATCH_BYTES >= wl::kSyncBytes, "the static scratch holds the sync area");
+
+wl_status wl_linear_static(const wl_theta *th, const void *x, void *y, int32_t T, void *hip_stream) {
+    wl_status st = check_theta(th, "theta");
+    if (st != WL_OK) return st;
+    if ((st = check_io(x, y, T, th->d_in, th->d_out)) != WL_OK) return st;
+    if (T == 0) return ok();
+    const wl_theta *ths[1] = {th};
+    const size_t need = layout(WL_OP_LINEAR, ths, T).total;
+    if (need > wl::kStaticScratchBytes)
+        return fail(WL_ERR_WORKSPACE, "this call needs %zu bytes of workspace; the static scratch holds %zu", need,
+                    (size_t)wl::kStaticScratchBytes);
+    void *ws = nullptr;
+    const hipError_t e = wl::static_scratch(static_cast<hipStream_t>(hip_stream), &ws);
+    if (e != hipSuccess) return fail(WL_ERR_HIP, "static scratch set-up failed: %s", hipGetErrorString(e));
+    return wl_linear(th, x, y, T, ws, wl::kStaticScratchBytes, hip_stream);
+}
+
 wl_status wl_qkv_fused(const wl_theta *q, const wl_theta *k, const wl_theta *v, const void *x, void *y_qkv,
                        int32_t T, void *ws, size_t ws_bytes, void *hip_stream) {
     const wl_theta *ths[3] = {q, k, v};

@@ -120,6 +120,12 @@ constexpr size_t kSweepWords = (kSyncBytes - kSyncTaggedOffset) / 8;
 // Clears the sync area (n_words 64-bit words at sync) with a fill kernel.
 hipError_t launch_sync_clear(unsigned long long *sync, size_t n_words, hipStream_t stream);
 
+// The static workspace of wl_linear_static: its size per device, and its
+// address on the current device. The first request on a device looks the
+// address up and enqueues, on `stream`, a fill kernel that clears the sync area.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(hipStream_t stream, void **out);
+
 struct GemvF {
     Child ch[kMaxChildren];
     int n_ch;

@@ -27,8 +27,11 @@ ABI_VERSION = 5
 # cleared by wl_workspace_init (new_workspace does it) before first use, then
 # written only by the library's calls.
 SYNC_BYTES = 9764864
+# Bytes of the static workspace wl_linear_static uses on each device.
+STATIC_SCRATCH_BYTES = 33554432
 _FALLBACK_WORD = 511   # int64 word of the sync area counting decode workgroups that stopped waiting
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error", 4: "workspace too small"}
+WL_OK, WL_ERR_INVALID_ARG, WL_ERR_UNSUPPORTED, WL_ERR_HIP, WL_ERR_WORKSPACE = 0, 1, 2, 3, 4
 
 
 class WlError(RuntimeError):
@@ -56,10 +59,11 @@ def _load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.wl_workspace_bytes.argtypes = [i32, ctypes.POINTER(P), i32, i32]
     lib.wl_workspace_bytes.restype = sz
     lib.wl_linear.argtypes = [P, vp, vp, i32, vp, sz, vp]
+    lib.wl_linear_static.argtypes = [P, vp, vp, i32, vp]
     lib.wl_qkv_fused.argtypes = [P, P, P, vp, vp, i32, vp, sz, vp]
     lib.wl_mlp_fused.argtypes = [P, P, P, vp, vp, i32, vp, sz, vp]
     lib.wl_materialize_weff.argtypes = [P, vp, vp]
-    for name in ("wl_linear", "wl_qkv_fused", "wl_mlp_fused", "wl_materialize_weff"):
+    for name in ("wl_linear", "wl_linear_static", "wl_qkv_fused", "wl_mlp_fused", "wl_materialize_weff"):
         getattr(lib, name).restype = ctypes.c_int
     lib.wl_set_regime.argtypes = [i32]
     lib.wl_set_regime.restype = i32
@@ -190,6 +194,17 @@ def wl_linear(th: dict, x: torch.Tensor, y: torch.Tensor | None = None, ws: torc
     ws = ws if ws is not None else WORKSPACE.get(x.device, need)
     _check(lib.wl_linear(ctypes.byref(st), _ptr(x), _ptr(y), T, _ptr(ws),
                          0 if ws is None else ws.numel() * ws.element_size(), _stream(x.device)))
+    return y
+
+
+def wl_linear_static(th: dict, x: torch.Tensor, y: torch.Tensor | None = None):
+    """wl_linear with the library's static workspace (no workspace argument;
+    the C call allocates no device memory). y is allocated here when not given."""
+    T = _io(x, int(th["d_in"]), th["W0"].dtype)
+    st = make_theta(th)
+    if y is None:
+        y = torch.empty(T, int(th["d_out"]), dtype=th["W0"].dtype, device=x.device)
+    _check(lib.wl_linear_static(ctypes.byref(st), _ptr(x), _ptr(y), T, _stream(x.device)))
     return y
 
 

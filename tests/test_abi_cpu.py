@@ -222,6 +222,7 @@ def test_workspace_starts_with_the_sync_area(wl):
     assert wl.SYNC_BYTES == wl.lib.wl_sync_bytes() == 9764864
     text = open(HEADER).read()
     assert re.search(r"#define WL_SYNC_BYTES 9764864\b", text)
+    assert re.search(rf"#define WL_STATIC_SCRATCH_BYTES {wl.STATIC_SCRATCH_BYTES}\b", text)
     assert re.search(r"#define WL_ABI_VERSION 5\b", text)
 
 
