@@ -7,7 +7,10 @@
  *
  * Plain, slow, obviously correct: fp64 arithmetic on the exact values of the
  * bf16 / fp32 inputs, sequential loops in the index order of the definitions,
- * no blocking, no fusion, no reordering. Nothing here is shared with the HIP
+ * no blocking, no fusion, no reordering. Independent results (output elements,
+ * V^T x entries, h entries, W_eff entries) are shared out over OpenMP threads;
+ * each is still one thread's sequential loop, so the values do not depend on
+ * the number of threads. Nothing here is shared with the HIP
  * library (no header, helper, table or constant), and this file includes none
  * of its files.
  *
@@ -25,6 +28,7 @@
  * "In-kernel reconstruction" page); s is always binary32.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -95,6 +99,15 @@ static double elem(const void *p, int64_t dtype, int64_t j)
     return bf16_value(((const uint16_t *)p)[j]);
 }
 
+/* Threads used by the loops below: n > 0 sets it, n <= 0 leaves it; returns
+ * the count now in force (by default every core the process may run on). */
+int orc_threads(int n)
+{
+    if (n > 0)
+        omp_set_num_threads(n);
+    return omp_get_max_threads();
+}
+
 /* tanh-approximated GELU (Hendrycks & Gimpel, 2016):
  *   gelu(z) = 0.5 * z * (1 + tanh(sqrt(2/pi) * (z + 0.044715 * z^3)))
  * The pages name an activation between gate/up and down ("In-kernel
@@ -118,18 +131,27 @@ double orc_gelu_tanh(double z)
 int orc_linear(const orc_theta *th, int64_t T, const void *x, double *y, double *bound)
 {
     const int64_t d_in = th->d_in, d_out = th->d_out, r = th->r, dt = th->dtype;
-    double *vtx = (double *)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
-    if (!vtx)
+    /* token t's vtx[k] at vtx_all[t * r + k], every token first */
+    double *vtx_all = (double *)malloc(sizeof(double) * (size_t)(T * r > 0 ? T * r : 1));
+    if (!vtx_all)
         return -1;
-    for (int64_t t = 0; t < T; ++t) {
-        const int64_t x0 = t * d_in;   /* token t's row of x */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = 0; t < T; ++t)
         for (int64_t k = 0; k < r; ++k) {
+            const int64_t x0 = t * d_in;   /* token t's row of x */
+            double *vtx = vtx_all + t * r;
             double acc = 0.0;
             for (int64_t i = 0; i < d_in; ++i)
                 acc += elem(th->V, dt, i * r + k) * elem(x, dt, x0 + i);
             vtx[k] = acc;
         }
-        for (int64_t o = 0; o < d_out; ++o) {
+    /* output rows outer, tokens inner: a W0 row is read once per thread pass
+     * while x stays in cache (the order of independent elements only) */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t o = 0; o < d_out; ++o)
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t x0 = t * d_in;
+            const double *vtx = vtx_all + t * r;
             double m = 0.0, m_abs = 0.0;
             for (int64_t i = 0; i < d_in; ++i) {
                 double p = elem(th->W0, dt, o * d_in + i) * elem(x, dt, x0 + i);
@@ -147,8 +169,7 @@ int orc_linear(const orc_theta *th, int64_t T, const void *x, double *y, double 
             if (bound)
                 bound[t * d_out + o] = fabs(so) * m_abs + delta_abs;
         }
-    }
-    free(vtx);
+    free(vtx_all);
     return 0;
 }
 
@@ -215,6 +236,7 @@ int orc_mlp(const orc_theta *gate, const orc_theta *up, const orc_theta *down, i
         goto done;
     if (orc_linear(gate, T, x, g, NULL) != 0 || orc_linear(up, T, x, u, NULL) != 0)
         goto done;
+#pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < T * d_ff; ++j) {
         double h = orc_gelu_tanh(g[j]) * u[j];
         if (dt == ORC_F32)
@@ -244,6 +266,7 @@ done:
 int orc_weff(const orc_theta *th, double *W_eff, double *bound)
 {
     const int64_t d_in = th->d_in, d_out = th->d_out, r = th->r, dt = th->dtype;
+#pragma omp parallel for schedule(static)
     for (int64_t o = 0; o < d_out; ++o) {
         double so = th->s ? (double)th->s[o] : 1.0;
         for (int64_t i = 0; i < d_in; ++i) {

@@ -21,9 +21,10 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(HERE, "oracle.c")
 LIBRARY = os.path.join(HERE, "liboracle.so")
-# Plain IEEE double arithmetic: no contraction into fused multiply-adds, no fast-math.
+# Plain IEEE double arithmetic: no contraction into fused multiply-adds, no
+# fast-math; OpenMP shares independent results out over threads.
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-D_GNU_SOURCE",
-          "-fPIC", "-shared"]
+          "-fopenmp", "-fPIC", "-shared"]
 
 
 def build(source: str = SOURCE, out: str = LIBRARY) -> str:
@@ -110,6 +111,8 @@ class Oracle:
         lib.orc_bf16_rne.restype = ctypes.c_uint16
         lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
         lib.orc_bf16_value.restype = ctypes.c_double
+        lib.orc_threads.argtypes = [ctypes.c_int]
+        lib.orc_threads.restype = ctypes.c_int
         self.lib = lib
 
     # -- marshalling ----------------------------------------------------------------
@@ -187,6 +190,10 @@ class Oracle:
         R = np.ascontiguousarray(R, dtype=np.float64)
         assert W.size == R.size
         return float(self.lib.orc_rel_frob(W.size, _ptr(W), _ptr(R)))
+
+    def threads(self, n: int = 0) -> int:
+        """Sets the OpenMP thread count when n > 0; returns the count in force."""
+        return int(self.lib.orc_threads(int(n)))
 
     def gelu(self, z: float) -> float:
         return float(self.lib.orc_gelu_tanh(float(z)))

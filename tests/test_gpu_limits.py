@@ -99,3 +99,39 @@ def test_largest_weff(wl, orc):
     check(w[rows], w_ref, bound, "largest W_eff")
     del W0, w
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [3, 4])
+def test_widest_input_staged_x(wl, orc, T):
+    # Passes of 3 and 4 tokens stage each producer's x slice in LDS; at d_in =
+    # 32768 the slice is its longest (512 inputs). The in-launch hand-off, its
+    # forced fallback (spin limit 0) and the separate V^T x launch (regime 3)
+    # agree bit for bit, and sampled rows match the oracle.
+    d_in, d_out, r = 32768, 65535, 64
+    g = torch.Generator().manual_seed(2200 + T)
+    W0 = pattern(d_out, d_in, torch.bfloat16, 7, 13, 17, 2.0 ** -6)
+    s = (1 + 0.01 * torch.randn(d_out, generator=g)).to(DEV)
+    U = (0.01 * torch.randn(d_out, r, generator=g)).to(torch.bfloat16).to(DEV)
+    V = (0.01 * torch.randn(d_in, r, generator=g)).to(torch.bfloat16).to(DEV)
+    x_host = inputs.activations(g, T, d_in)
+    th = dict(W0=W0, s=s, U=U, V=V, d_in=d_in, d_out=d_out, r=r)
+    xd = x_host.to(DEV)
+    prev = wl.set_regime(1)
+    try:
+        y_hand = wl.wl_linear(th, xd).clone()
+        spin = wl.set_spin_limit(0)
+        try:
+            y_fb = wl.wl_linear(th, xd).clone()
+        finally:
+            wl.set_spin_limit(spin)
+        wl.set_regime(3)
+        y_sep = wl.wl_linear(th, xd).clone()
+        torch.cuda.synchronize()
+    finally:
+        wl.set_regime(prev)
+    assert torch.equal(y_hand.view(torch.int16), y_fb.view(torch.int16)), "forced fallback differs"
+    assert torch.equal(y_hand.view(torch.int16), y_sep.view(torch.int16)), "separate V^T x launch differs"
+    rows = [0, 1, 511, 512, 32767, d_out - 1]
+    sampled_check(orc, th, x_host, y_hand, rows, torch.bfloat16, f"widest input T={T}")
+    del W0, y_hand, y_fb, y_sep
+    torch.cuda.empty_cache()
