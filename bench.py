@@ -11,7 +11,7 @@ Workloads (``--workload``; the default is the one the headline metric is quoted 
                   1152. A step is one layer (wl_qkv_fused, wl_linear,
                   wl_mlp_fused); steps cycle over 26 resident layers with their
                   own W0, so the 1.4 GB weight set streams from HBM rather than
-                  from the 256 MB last-level cache.
+                  from the 256 MB last-level cache. Tokens/s are per layer.
   single          one 1152 -> 1152 projection, r = 4, T = 1; steps cycle over 400
                   resident copies (about 1.07 GB).
   batched-decode  the same layer shapes, 26 layers, T = 32 tokens (32 concurrent
@@ -39,8 +39,12 @@ graphs, since at decode sizes a call is shorter than the host cost of its
 launches. The roofline record covers the dominant library call (the fused MLP):
 its algorithmic bytes (decode) or flops (prefill, large at T = 512) over its
 average duration, timed with HIP events on the stream the library launches on.
-The oracle (plain fp64 C, single thread) is timed on a bounded sample of the
-same work. One JSON line is printed.
+The oracle (plain fp64 C) is timed on a bounded sample of the same work, on
+the host's OpenMP threads and on one thread. The default workload's line also
+carries records of the decode layer at r = 4, the MLP at T = 2048 (its MFMA
+roofline) and batched decode over 26 layers that share one W0 (G = 1). A timed
+region is one replay of a HIP graph holding exactly the timed steps. One JSON
+line is printed.
 """
 from __future__ import annotations
 
@@ -60,7 +64,7 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix cores
 MFMA_F32_PEAK_TFS = 157.3      # MI355X dense fp32 matrix cores
 METRIC = "tokens/s + achieved HBM GB/s (T=1) / MFMA TFLOP/s (T=2048) per rank"
 WORKLOADS = ("layer-decode", "single", "batched-decode", "prefill", "large", "copy")
-DEFAULT_STEPS = {"layer-decode": 2600, "single": 4000, "batched-decode": 200, "prefill": 260, "large": 40}
+DEFAULT_STEPS = {"layer-decode": 520, "single": 800, "batched-decode": 20, "prefill": 52, "large": 20}
 
 
 def parse_args():
@@ -73,6 +77,8 @@ def parse_args():
     p.add_argument("--tokens", type=int, default=None, help="T for the large workload (1 or 512)")
     p.add_argument("--shared-w0", action="store_true", help="batched-decode: one W0 for all layers (G=1)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0 skips it)")
+    p.add_argument("--no-records", action="store_true",
+                   help="layer-decode: skip the r=4 decode, T=2048 MLP and shared-W0 batched-decode records")
     p.add_argument("--dominant-only", action="store_true",
                    help="run only the dominant call (for hardware-counter passes) and print the call count")
     p.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -134,7 +140,7 @@ def _regime_sources(tokens: int, dtype: str = "bf16") -> tuple:
     if dtype == "f32":
         return ("k_f32.hip",)
     if tokens <= 8:
-        return ("k_gemv.hip", "k_vtx.hip", "wl_vtx_slice.h")
+        return ("k_gemv.hip", "k_vtx.hip", "wl_vtx_slice.h", "wl_handoff.h", "k_mlp.hip")
     if tokens <= 64:
         return ("k_skinny.hip",)
     return ("k_gemm.hip", "k_vtxmm.hip")
@@ -181,73 +187,96 @@ def stored_traffic(workload: str, rank: int, tokens: int):
 
 # -- timing -------------------------------------------------------------------------------
 
-class GraphSet:
-    """HIP graphs over a list of per-index callables: one graph holding all of them
-    in order and one per index, so that exactly K steps can be replayed."""
+class StepGraph:
+    """One HIP graph holding exactly k steps, step i running fns[i % len(fns)], so
+    that a timed region is one replay whatever k is (no host gaps between steps
+    and none that depend on k)."""
 
-    def __init__(self, torch, fns):
-        self.torch = torch
+    def __init__(self, torch, fns, k: int):
         for fn in fns:      # eager pass: allocations and workspace before capture
             fn()
         torch.cuda.synchronize()
-        self.all = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.all):
-            for fn in fns:
-                fn()
-        self.one = []
-        for fn in fns:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                fn()
-            self.one.append(g)
-        self.n = len(fns)
+        self.k = k
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for i in range(k):
+                fns[i % len(fns)]()
 
-    def run(self, k: int):
-        for _ in range(k // self.n):
-            self.all.replay()
-        for i in range(k % self.n):
-            self.one[i].replay()
+    def replay(self):
+        self.graph.replay()
 
 
-def time_steps(torch, gs: GraphSet, steps: int, warmup: int):
-    gs.run(warmup)
+def time_steps(torch, fns, steps: int, warmup: int):
+    """(ms, wall s) of exactly `steps` steps replayed as one graph, after `warmup`
+    steps replayed as another; HIP events on the stream the library launches on
+    (torch's current stream, which the graphs are replayed on)."""
+    timed = StepGraph(torch, fns, steps)
+    if warmup > 0:
+        StepGraph(torch, fns, warmup).replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall = time.perf_counter()
     e0.record()
-    gs.run(steps)
+    timed.replay()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall
     return e0.elapsed_time(e1), wall
 
 
-def time_calls(torch, gs: GraphSet, calls: int) -> float:
-    """Average ms per call of the graph set's callables, replayed `calls` times in total."""
-    reps = max(1, calls // gs.n)
-    gs.all.replay()
+def time_calls(torch, fns, calls: int) -> float:
+    """Average ms per call over `calls` calls (cycling over fns) in one graph,
+    replayed once to warm up and once timed."""
+    g = StepGraph(torch, fns, calls)
+    g.replay()
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
-        gs.all.replay()
+    g.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (reps * gs.n)
+    return e0.elapsed_time(e1) / calls
 
 
-def oracle_sample(budget_s: float, fn, units_per_call: float, unit: str, what: str):
-    """Time the oracle: call fn() until the budget is spent (at least once)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_sample(orc, budget_s: float, fn, units_per_call: float, unit: str, what: str):
+    """Time the oracle on the host's cores (its OpenMP threads: OMP_NUM_THREADS
+    when set, else every core the process may run on) and on one thread, each
+    for half the budget (at least one call each)."""
     if budget_s <= 0:
         return None
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        fn()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": reps * units_per_call / el, "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": f"{reps} x {what} in {el:.1f} s, single-threaded fp64 C oracle"}
+
+    def rate(seconds):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return reps, el
+
+    threads = orc.threads()
+    reps, el = rate(budget_s / 2)
+    orc.threads(1)
+    try:
+        reps1, el1 = rate(budget_s / 2)
+    finally:
+        orc.threads(threads)
+    return {"value": reps * units_per_call / el, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{reps} x {what} in {el:.1f} s, fp64 C oracle on {threads} OpenMP threads",
+            "affine_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "single_thread": {"value": reps1 * units_per_call / el1, "unit": unit, "cores": 1,
+                              "sample": f"{reps1} x {what} in {el1:.1f} s on one thread"}}
 
 
 def rel_l2(np, y_gpu, y_ref) -> float:
@@ -257,62 +286,100 @@ def rel_l2(np, y_gpu, y_ref) -> float:
 
 # -- workloads ----------------------------------------------------------------------------
 
-def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_std, seed, workload,
-               bound):
-    """Decoder-layer workloads: steps of one layer (or of all layers for batched decode)."""
+def build_layers(args, torch, wl, inputs, *, dims, r, n_layers, G, w0_std, seed):
+    """Seeded synthetic layers on the host and on the device (W0 blocks shared
+    between layers stay shared on the device)."""
     dev = torch.device("cuda:0")
     gen = torch.Generator().manual_seed(seed)
-    t_gen = time.perf_counter()
     dt = torch.float32 if args.dtype == "f32" else torch.bfloat16
     host_layers = inputs.layers(gen, dims, r, n_layers, G, w0_std=w0_std, dtype=dt)
-    acts = inputs.layer_inputs(gen, dims, T, dtype=dt)
     layers = [{f: wl.theta_to(lay[f], dev) for f in inputs.FAMILIES} for lay in host_layers]
-    # W0 blocks shared between layers stay shared on the device.
     if G < n_layers:
         band = -(-n_layers // G)
         for l in range(n_layers):
             for f in inputs.FAMILIES:
                 layers[l][f]["W0"] = layers[(l // band) * band][f]["W0"]
-    xa = {k: v.to(dev) for k, v in acts.items()}
+    return gen, host_layers, layers
+
+
+class LayerCalls:
+    """The three library calls of a decoder layer at T tokens, on preallocated
+    outputs and one workspace."""
+
+    def __init__(self, torch, wl, inputs, gen, layers, dims, T, dt):
+        dev = torch.device("cuda:0")
+        self.wl, self.layers = wl, layers
+        self.acts = inputs.layer_inputs(gen, dims, T, dtype=dt)
+        self.xa = {k: v.to(dev) for k, v in self.acts.items()}
+        d, width = dims["d_model"], dims["q"] + 2 * dims["kv"]
+        self.y_qkv = torch.empty(T, width, dtype=dt, device=dev)
+        self.y_o = torch.empty(T, d, dtype=dt, device=dev)
+        self.y_mlp = torch.empty(T, d, dtype=dt, device=dev)
+        l0 = layers[0]
+        ws_bytes = max(wl.workspace_bytes(wl.OP_QKV, [l0["q"], l0["k"], l0["v"]], T),
+                       wl.workspace_bytes(wl.OP_LINEAR, [l0["o"]], T),
+                       wl.workspace_bytes(wl.OP_MLP, [l0["gate"], l0["up"], l0["down"]], T))
+        self.ws = wl.new_workspace(ws_bytes, dev)
+
+    def qkv(self, l):
+        lay = self.layers[l]
+        self.wl.wl_qkv_fused(lay["q"], lay["k"], lay["v"], self.xa["x_attn"], y=self.y_qkv, ws=self.ws)
+
+    def o(self, l):
+        self.wl.wl_linear(self.layers[l]["o"], self.xa["x_o"], y=self.y_o, ws=self.ws)
+
+    def mlp(self, l):
+        lay = self.layers[l]
+        self.wl.wl_mlp_fused(lay["gate"], lay["up"], lay["down"], self.xa["x_mlp"], y=self.y_mlp, ws=self.ws)
+
+    def step(self, l):
+        self.qkv(l)
+        self.o(l)
+        self.mlp(l)
+
+
+def hbm_roof(bytes_per_launch, ms, traffic, kernel):
+    achieved = bytes_per_launch / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel,
+            "bytes_per_launch": bytes_per_launch, "us_per_launch": ms * 1e3}
+
+
+def mfma_roof(flops_per_launch, ms, traffic, kernel, peak):
+    achieved = flops_per_launch / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": traffic, "kernel": kernel,
+            "flops_per_launch": flops_per_launch, "us_per_launch": ms * 1e3}
+
+
+def mlp_kernel_name(T: int) -> str:
+    if T <= 2:
+        return "wl_mlp_fused: one launch (gate/up, GELU-tanh and down together)"
+    return "wl_mlp_fused (all of its kernels, back to back)"
+
+
+def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_std, seed, workload,
+               bound):
+    """Decoder-layer workloads: steps of one layer (or of all layers for batched decode)."""
+    t_gen = time.perf_counter()
+    dt = torch.float32 if args.dtype == "f32" else torch.bfloat16
+    gen, host_layers, layers = build_layers(args, torch, wl, inputs, dims=dims, r=r, n_layers=n_layers, G=G,
+                                            w0_std=w0_std, seed=seed)
+    calls = LayerCalls(torch, wl, inputs, gen, layers, dims, T, dt)
+    acts = calls.acts
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
-
-    d, width = dims["d_model"], dims["q"] + 2 * dims["kv"]
-    y_qkv = torch.empty(T, width, dtype=dt, device=dev)
-    y_o = torch.empty(T, d, dtype=dt, device=dev)
-    y_mlp = torch.empty(T, d, dtype=dt, device=dev)
-    l0 = layers[0]
-    ws_bytes = max(wl.workspace_bytes(wl.OP_QKV, [l0["q"], l0["k"], l0["v"]], T),
-                   wl.workspace_bytes(wl.OP_LINEAR, [l0["o"]], T),
-                   wl.workspace_bytes(wl.OP_MLP, [l0["gate"], l0["up"], l0["down"]], T))
-    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
-
-    def qkv(l):
-        lay = layers[l]
-        wl.wl_qkv_fused(lay["q"], lay["k"], lay["v"], xa["x_attn"], y=y_qkv, ws=ws)
-
-    def o(l):
-        wl.wl_linear(layers[l]["o"], xa["x_o"], y=y_o, ws=ws)
-
-    def mlp(l):
-        lay = layers[l]
-        wl.wl_mlp_fused(lay["gate"], lay["up"], lay["down"], xa["x_mlp"], y=y_mlp, ws=ws)
-
-    def layer_step(l):
-        qkv(l)
-        o(l)
-        mlp(l)
 
     if args.dominant_only:
         n = args.steps if args.steps is not None else n_layers
         for i in range(n):
-            mlp(i % n_layers)
+            calls.mlp(i % n_layers)
         torch.cuda.synchronize()
         print(json.dumps({"dominant_calls": n, "call": "wl_mlp_fused", "workload": workload}))
         return None
 
     # Parity spot check of layer 0 against the oracle (eager, outside the timed region).
-    layer_step(0)
+    calls.step(0)
     torch.cuda.synchronize()
     h0 = host_layers[0]
     parity = {}
@@ -320,44 +387,35 @@ def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_
         # At prefill sizes the oracle takes a slice of the tokens: the first 16.
         n_chk = min(T, 16)
         sl = slice(0, n_chk)
-        parity["qkv"] = rel_l2(np, y_qkv[sl], orc.qkv(h0["q"], h0["k"], h0["v"], acts["x_attn"][sl])[0])
-        parity["o"] = rel_l2(np, y_o[sl], orc.linear(h0["o"], acts["x_o"][sl])[0])
-        parity["mlp"] = rel_l2(np, y_mlp[sl], orc.mlp(h0["gate"], h0["up"], h0["down"], acts["x_mlp"][sl])[0])
+        parity["qkv"] = rel_l2(np, calls.y_qkv[sl], orc.qkv(h0["q"], h0["k"], h0["v"], acts["x_attn"][sl])[0])
+        parity["o"] = rel_l2(np, calls.y_o[sl], orc.linear(h0["o"], acts["x_o"][sl])[0])
+        parity["mlp"] = rel_l2(np, calls.y_mlp[sl],
+                               orc.mlp(h0["gate"], h0["up"], h0["down"], acts["x_mlp"][sl])[0])
         parity["tokens_checked"] = n_chk
 
     if workload == "batched-decode":
-        steps_fns = [lambda: [layer_step(l) for l in range(n_layers)]]
-        tokens_per_step = T
+        steps_fns = [lambda: [calls.step(l) for l in range(n_layers)]]
         unit_layers = n_layers
     else:
-        steps_fns = [lambda l=l: layer_step(l) for l in range(n_layers)]
-        tokens_per_step = T
+        steps_fns = [lambda l=l: calls.step(l) for l in range(n_layers)]
         unit_layers = 1
-    gs = GraphSet(torch, steps_fns)
-    gs_mlp = GraphSet(torch, [lambda l=l: mlp(l) for l in range(n_layers)])
+    mlp_fns = [lambda l=l: calls.mlp(l) for l in range(n_layers)]
 
     K = args.steps if args.steps is not None else DEFAULT_STEPS[workload]
     W = args.warmup if args.warmup is not None else max(1, K // 10)
-    ms_total, wall = time_steps(torch, gs, K, W)
+    ms_total, wall = time_steps(torch, steps_fns, K, W)
     ms_per_step = ms_total / K
-    mlp_ms = time_calls(torch, gs_mlp, max(n_layers, K * unit_layers))
+    mlp_ms = time_calls(torch, mlp_fns, max(10 * n_layers, 260))
 
     lay_b, lay_f = layer_work(h0, dims, T)
     mlp_b, mlp_f = mlp_work(h0, dims, T)
     step_b, step_f = lay_b * unit_layers, lay_f * unit_layers
+    traffic = stored_traffic(traffic_key(args, workload), r, T)
     if bound == "hbm":
-        achieved = mlp_b / (mlp_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(traffic_key(args, workload), r, T),
-                "kernel": "wl_mlp_fused (all of its kernels, back to back)", "bytes_per_launch": mlp_b,
-                "us_per_launch": mlp_ms * 1e3}
+        roof = hbm_roof(mlp_b, mlp_ms, traffic, mlp_kernel_name(T))
     else:
         peak = MFMA_F32_PEAK_TFS if args.dtype == "f32" else MFMA_BF16_PEAK_TFS
-        achieved = mlp_f / (mlp_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": stored_traffic(traffic_key(args, workload), r, T),
-                "kernel": "wl_mlp_fused (all of its kernels, back to back)", "flops_per_launch": mlp_f,
-                "us_per_launch": mlp_ms * 1e3}
+        roof = mfma_roof(mlp_f, mlp_ms, traffic, mlp_kernel_name(T), peak)
 
     # Oracle sample: whole layers at decode sizes, a few tokens of a layer otherwise.
     n_tok = T if T <= 32 else (8 if T <= 512 else 4)
@@ -368,20 +426,26 @@ def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_
         orc.linear(h0["o"], acts["x_o"][sl])
         orc.mlp(h0["gate"], h0["up"], h0["down"], acts["x_mlp"][sl])
 
-    cpu = oracle_sample(args.cpu_seconds, oracle_layer, n_tok, "tokens/s",
+    cpu = oracle_sample(orc, args.cpu_seconds, oracle_layer, n_tok, "tokens/s",
                         f"one layer (QKV + O + MLP) at {n_tok} token(s), r={r}")
 
     extra = {}
     if workload == "prefill":
-        extra.update(materialize_and_dense(torch, wl, layers, xa, dims, T, ws))
+        extra.update(materialize_and_dense(torch, wl, layers, calls.xa, dims, T, calls.ws))
+    if workload == "layer-decode" and args.dtype == "bf16" and not args.no_records:
+        records = {}
+        records["decode_r4"] = record_decode(args, torch, wl, inputs, dims, n_layers, 4, K, W)
+        records["prefill_mlp_T2048_r32"] = record_prefill_mlp(args, torch, wl, inputs, gen, layers, h0, dims)
+        records["batched_decode_G1_T32_r32"] = record_batched_g1(args, torch, wl, inputs, dims)
+        extra["records"] = records
 
     out = {
-        "value": K * tokens_per_step / (ms_total * 1e-3),
+        "value": K * T / (ms_total * 1e-3),
         "unit": "tokens/s",
         "steps": K, "warmup": W, "ms_per_step": ms_per_step,
         "config": {"workload": workload_name(workload, dims, r, T, n_layers, G)
                    + (", fp32 weights and activations" if args.dtype == "f32" else ""),
-                   "T": T, "rank": r, "layers": n_layers, "G": G, "d_model": d, "q": dims["q"],
+                   "T": T, "rank": r, "layers": n_layers, "G": G, "d_model": dims["d_model"], "q": dims["q"],
                    "kv": dims["kv"], "d_ff": dims["ff"], "parallelism": "single-gpu"},
         "roofline": roof,
         "step_hbm_gbs": step_b / (ms_per_step * 1e-3) / 1e9,
@@ -394,6 +458,76 @@ def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_
     }
     out.update(extra)
     return out
+
+
+def record_decode(args, torch, wl, inputs, dims, n_layers, r, K, W):
+    """The decode layer at another rank: tokens/s per layer over the same step
+    count, and the MLP call's HBM roofline."""
+    dt = torch.bfloat16
+    gen, host_layers, layers = build_layers(args, torch, wl, inputs, dims=dims, r=r, n_layers=n_layers,
+                                            G=n_layers, w0_std=0.02, seed=0)
+    calls = LayerCalls(torch, wl, inputs, gen, layers, dims, 1, dt)
+    ms_total, _ = time_steps(torch, [lambda l=l: calls.step(l) for l in range(n_layers)], K, W)
+    mlp_ms = time_calls(torch, [lambda l=l: calls.mlp(l) for l in range(n_layers)], max(10 * n_layers, 260))
+    mlp_b, _ = mlp_work(host_layers[0], dims, 1)
+    lay_b, _ = layer_work(host_layers[0], dims, 1)
+    rec = {"workload": f"gemma3-1b-shaped layer decode, T=1, r={r}, per layer, 26 resident layers",
+           "tokens_per_s": K / (ms_total * 1e-3), "us_per_layer": ms_total * 1e3 / K, "steps": K,
+           "layer_hbm_gbs": lay_b / (ms_total * 1e-3 / K) / 1e9,
+           "roofline": hbm_roof(mlp_b, mlp_ms, stored_traffic("layer-decode", r, 1), mlp_kernel_name(1))}
+    del layers, calls
+    torch.cuda.empty_cache()
+    return rec
+
+
+def record_prefill_mlp(args, torch, wl, inputs, gen, layers, h0, dims):
+    """The MLP call at T = 2048 (r = 32, the headline's 26 layers): its MFMA
+    roofline, timed over 26 calls, one per layer."""
+    T = 2048
+    calls = LayerCalls(torch, wl, inputs, gen, layers, dims, T, torch.bfloat16)
+    n = len(layers)
+    mlp_ms = time_calls(torch, [lambda l=l: calls.mlp(l) for l in range(n)], 2 * n)
+    lay_ms = time_calls(torch, [lambda l=l: calls.step(l) for l in range(n)], n)
+    mlp_b, mlp_f = mlp_work(h0, dims, T)
+    lay_b, lay_f = layer_work(h0, dims, T)
+    rec = {"workload": "gemma3-1b-shaped MLP prefill, T=2048, r=32 (gate/up 1152 -> 6912, down 6912 -> 1152)",
+           "tokens_per_s_mlp": T / (mlp_ms * 1e-3),
+           "layer_us": lay_ms * 1e3, "layer_tflops": lay_f / (lay_ms * 1e-3) / 1e12,
+           "roofline": mfma_roof(mlp_f, mlp_ms, stored_traffic("prefill", 32, T), mlp_kernel_name(T),
+                                 MFMA_BF16_PEAK_TFS)}
+    del calls
+    torch.cuda.empty_cache()
+    return rec
+
+
+def record_batched_g1(args, torch, wl, inputs, dims):
+    """Batched decode (T = 32) over 26 layers that share one W0 per family (G = 1):
+    tokens/s of a 26-layer step, and its algorithmic bytes (every call's operands
+    counted), unique bytes (the one W0 set once, every layer's s, U, V, every
+    call's x and y) and the counter bytes of the MLP call from its traffic record."""
+    T, n_layers, r = 32, 26, 32
+    gen, host_layers, layers = build_layers(args, torch, wl, inputs, dims=dims, r=r, n_layers=n_layers, G=1,
+                                            w0_std=0.02, seed=0)
+    calls = LayerCalls(torch, wl, inputs, gen, layers, dims, T, torch.bfloat16)
+    step = [lambda: [calls.step(l) for l in range(n_layers)]]
+    ms, _ = time_steps(torch, step, 4, 1)
+    ms /= 4
+    mlp_ms = time_calls(torch, [lambda l=l: calls.mlp(l) for l in range(n_layers)], 2 * n_layers)
+    h0 = host_layers[0]
+    lay_b, _ = layer_work(h0, dims, T)
+    w0_once = sum(h0[f]["W0"].numel() * h0[f]["W0"].element_size() for f in inputs.FAMILIES)
+    unique = n_layers * lay_b - (n_layers - 1) * w0_once
+    mlp_b, _ = mlp_work(h0, dims, T)
+    mlp_w0 = sum(h0[f]["W0"].numel() * h0[f]["W0"].element_size() for f in ("gate", "up", "down"))
+    rec = {"workload": "gemma3-1b-shaped 26 layers sharing one W0 per family (G=1), batched decode T=32, r=32",
+           "tokens_per_s": T / (ms * 1e-3), "ms_per_26_layer_step": ms,
+           "algorithmic_bytes_per_step": n_layers * lay_b, "unique_bytes_per_step": unique,
+           "mlp_call": {"us": mlp_ms * 1e3, "algorithmic_bytes": mlp_b,
+                        "unique_bytes_26_calls": n_layers * mlp_b - (n_layers - 1) * mlp_w0,
+                        "counter_bytes": stored_traffic("batched-decode-G1", r, T)}}
+    del layers, calls
+    torch.cuda.empty_cache()
+    return rec
 
 
 def materialize_and_dense(torch, wl, layers, xa, dims, T, ws):
@@ -421,10 +555,8 @@ def materialize_and_dense(torch, wl, layers, xa, dims, T, ws):
         wl.wl_linear(dense["o"], xa["x_o"], y=y_o, ws=ws)
         wl.wl_mlp_fused(dense["gate"], dense["up"], dense["down"], xa["x_mlp"], y=y_mlp, ws=ws)
 
-    gm = GraphSet(torch, [materialize])
-    gd = GraphSet(torch, [dense_layer])
-    m_ms = time_calls(torch, gm, 20)
-    d_ms = time_calls(torch, gd, 20)
+    m_ms = time_calls(torch, [materialize], 20)
+    d_ms = time_calls(torch, [dense_layer], 20)
     e = lay["q"]["W0"].element_size()
     w_bytes = sum(2 * e * lay[f]["d_out"] * lay[f]["d_in"] + 4 * lay[f]["d_out"]
                   + e * lay[f]["r"] * (lay[f]["d_in"] + lay[f]["d_out"]) for f in lay)
@@ -435,12 +567,13 @@ def materialize_and_dense(torch, wl, layers, xa, dims, T, ws):
 
 def workload_name(workload, dims, r, T, n_layers, G):
     if workload == "large":
-        return f"hidden-5376 layer (QKV fused + O + MLP fused), T={T}, r={r}"
+        return f"hidden-5376 layer (QKV fused + O + MLP fused), T={T}, r={r}, per layer"
     if workload == "batched-decode":
         return f"gemma3-1b-shaped {n_layers} layers, batched decode T={T}, r={r}, G={G}"
     if workload == "prefill":
-        return f"gemma3-1b-shaped layer prefill T={T}, r={r}"
-    return f"gemma3-1b-shaped layer decode (QKV fused + O + MLP fused), T={T}, r={r}"
+        return f"gemma3-1b-shaped layer prefill T={T}, r={r}, per layer ({n_layers} resident layers)"
+    return (f"gemma3-1b-shaped layer decode (QKV fused + O + MLP fused), T={T}, r={r}, per layer "
+            f"({n_layers} resident layers)")
 
 
 def run_single(args, torch, np, wl, inputs, orc):
@@ -459,7 +592,7 @@ def run_single(args, torch, np, wl, inputs, orc):
         ths.append(th)
     x = x_host.to(dev)
     y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
-    ws = torch.zeros(wl.workspace_bytes(wl.OP_LINEAR, [ths[0]], T), dtype=torch.uint8, device=dev)
+    ws = wl.new_workspace(wl.workspace_bytes(wl.OP_LINEAR, [ths[0]], T), dev)
     if args.dominant_only:
         n = args.steps if args.steps is not None else copies
         for i in range(n):
@@ -470,14 +603,14 @@ def run_single(args, torch, np, wl, inputs, orc):
     wl.wl_linear(ths[0], x, y=y, ws=ws)
     torch.cuda.synchronize()
     parity = {"linear": rel_l2(np, y, orc.linear(host, x_host)[0])}
-    gs = GraphSet(torch, [lambda c=c: wl.wl_linear(ths[c], x, y=y, ws=ws) for c in range(copies)])
+    fns = [lambda c=c: wl.wl_linear(ths[c], x, y=y, ws=ws) for c in range(copies)]
     K = args.steps if args.steps is not None else DEFAULT_STEPS["single"]
     W = args.warmup if args.warmup is not None else max(1, K // 10)
-    ms_total, wall = time_steps(torch, gs, K, W)
+    ms_total, wall = time_steps(torch, fns, K, W)
     ms = ms_total / K
     b = call_bytes([host], T, d, d)
     achieved = b / (ms * 1e-3) / 1e9
-    cpu = oracle_sample(args.cpu_seconds, lambda: orc.linear(host, x_host), 1, "tokens/s",
+    cpu = oracle_sample(orc, args.cpu_seconds, lambda: orc.linear(host, x_host), 1, "tokens/s",
                         f"one 1152->1152 projection at T=1, r={r}")
     return {
         "value": K * T / (ms_total * 1e-3), "unit": "tokens/s", "steps": K, "warmup": W, "ms_per_step": ms,
