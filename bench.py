@@ -43,8 +43,8 @@ The oracle (plain fp64 C) is timed on a bounded sample of the same work, on
 the host's OpenMP threads and on one thread. The default workload's line also
 carries records of the decode layer at r = 4, the MLP at T = 2048 (its MFMA
 roofline) and batched decode over 26 layers that share one W0 (G = 1). A timed
-region is one replay of a HIP graph holding exactly the timed steps. One JSON
-line is printed.
+region is one launch of a library step (wl_step_create: one HIP graph the library
+records) holding exactly the timed steps. One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -130,10 +130,11 @@ def mlp_work(lay: dict, dims: dict, T: int):
     return b, fl
 
 
-# Sources of the kernels each token-count range runs (the ABI and the shared
-# headers always count): the decode GEMV with its V^T x launch, the skinny path,
-# the matrix-core GEMM with its V^T x launch.
-_COMMON_SOURCES = ("wl_abi.cpp", "wl_kernels.h", "wl_device.h")
+# Sources of the kernels each token-count range runs (the shared device headers
+# always count; the host dispatcher does not, so host-only changes such as a new
+# entry point leave the records valid): the decode GEMV with its V^T x launch and
+# the one-launch MLP, the skinny path, the matrix-core GEMM with its V^T x launch.
+_COMMON_SOURCES = ("wl_kernels.h", "wl_device.h")
 
 
 def _regime_sources(tokens: int, dtype: str = "bf16") -> tuple:
@@ -204,24 +205,6 @@ class StepGraph:
 
     def replay(self):
         self.graph.replay()
-
-
-def time_steps(torch, fns, steps: int, warmup: int):
-    """(ms, wall s) of exactly `steps` steps replayed as one graph, after `warmup`
-    steps replayed as another; HIP events on the stream the library launches on
-    (torch's current stream, which the graphs are replayed on)."""
-    timed = StepGraph(torch, fns, steps)
-    if warmup > 0:
-        StepGraph(torch, fns, warmup).replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall = time.perf_counter()
-    e0.record()
-    timed.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall
-    return e0.elapsed_time(e1), wall
 
 
 def time_calls(torch, fns, calls: int) -> float:
@@ -337,6 +320,40 @@ class LayerCalls:
         self.o(l)
         self.mlp(l)
 
+    # the same calls as (op, thetas, x, y) tuples for a library step
+    def call_mlp(self, l):
+        lay = self.layers[l]
+        return (self.wl.OP_MLP, [lay["gate"], lay["up"], lay["down"]], self.xa["x_mlp"], self.y_mlp)
+
+    def calls(self, l):
+        lay = self.layers[l]
+        return [(self.wl.OP_QKV, [lay["q"], lay["k"], lay["v"]], self.xa["x_attn"], self.y_qkv),
+                (self.wl.OP_LINEAR, [lay["o"]], self.xa["x_o"], self.y_o),
+                self.call_mlp(l)]
+
+
+def time_library_steps(torch, wl, step_calls, steps: int, warmup: int, ws):
+    """(ms, wall s) of exactly `steps` steps made into one library step (one HIP
+    graph recorded by wl_step_create and launched by wl_step_launch), after
+    `warmup` steps in another; step_calls(i) lists step i's calls."""
+    timed = wl.Step([c for i in range(steps) for c in step_calls(i)], ws=ws)
+    if warmup > 0:
+        warm = wl.Step([c for i in range(warmup) for c in step_calls(i)], ws=ws)
+        warm.launch()
+        torch.cuda.synchronize()
+        warm.close()
+    timed.launch()   # first launch of the graph: upload, outside the timed region
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall = time.perf_counter()
+    e0.record()
+    timed.launch()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall
+    timed.close()
+    return e0.elapsed_time(e1), wall
+
 
 def hbm_roof(bytes_per_launch, ms, traffic, kernel):
     achieved = bytes_per_launch / (ms * 1e-3) / 1e9
@@ -394,16 +411,18 @@ def run_layers(args, torch, np, wl, inputs, orc, *, dims, r, T, n_layers, G, w0_
         parity["tokens_checked"] = n_chk
 
     if workload == "batched-decode":
-        steps_fns = [lambda: [calls.step(l) for l in range(n_layers)]]
+        def step_calls(i):
+            return [c for l in range(n_layers) for c in calls.calls(l)]
         unit_layers = n_layers
     else:
-        steps_fns = [lambda l=l: calls.step(l) for l in range(n_layers)]
+        def step_calls(i):
+            return calls.calls(i % n_layers)
         unit_layers = 1
     mlp_fns = [lambda l=l: calls.mlp(l) for l in range(n_layers)]
 
     K = args.steps if args.steps is not None else DEFAULT_STEPS[workload]
     W = args.warmup if args.warmup is not None else max(1, K // 10)
-    ms_total, wall = time_steps(torch, steps_fns, K, W)
+    ms_total, wall = time_library_steps(torch, wl, step_calls, K, W, calls.ws)
     ms_per_step = ms_total / K
     mlp_ms = time_calls(torch, mlp_fns, max(10 * n_layers, 260))
 
@@ -467,7 +486,7 @@ def record_decode(args, torch, wl, inputs, dims, n_layers, r, K, W):
     gen, host_layers, layers = build_layers(args, torch, wl, inputs, dims=dims, r=r, n_layers=n_layers,
                                             G=n_layers, w0_std=0.02, seed=0)
     calls = LayerCalls(torch, wl, inputs, gen, layers, dims, 1, dt)
-    ms_total, _ = time_steps(torch, [lambda l=l: calls.step(l) for l in range(n_layers)], K, W)
+    ms_total, _ = time_library_steps(torch, wl, lambda i: calls.calls(i % n_layers), K, W, calls.ws)
     mlp_ms = time_calls(torch, [lambda l=l: calls.mlp(l) for l in range(n_layers)], max(10 * n_layers, 260))
     mlp_b, _ = mlp_work(host_layers[0], dims, 1)
     lay_b, _ = layer_work(host_layers[0], dims, 1)
@@ -504,14 +523,33 @@ def record_batched_g1(args, torch, wl, inputs, dims):
     """Batched decode (T = 32) over 26 layers that share one W0 per family (G = 1):
     tokens/s of a 26-layer step, and its algorithmic bytes (every call's operands
     counted), unique bytes (the one W0 set once, every layer's s, U, V, every
-    call's x and y) and the counter bytes of the MLP call from its traffic record."""
+    call's x and y) and the counter bytes of the MLP call from its traffic record.
+    The step is timed in the given layer order and, with every layer's calls
+    given outputs of their own (so that they are independent), regrouped so the
+    26 calls sharing a W0 run back to back (WL_STEP_GROUP_SHARED_W0)."""
     T, n_layers, r = 32, 26, 32
     gen, host_layers, layers = build_layers(args, torch, wl, inputs, dims=dims, r=r, n_layers=n_layers, G=1,
                                             w0_std=0.02, seed=0)
     calls = LayerCalls(torch, wl, inputs, gen, layers, dims, T, torch.bfloat16)
-    step = [lambda: [calls.step(l) for l in range(n_layers)]]
-    ms, _ = time_steps(torch, step, 4, 1)
+    all_layers = [c for l in range(n_layers) for c in calls.calls(l)]
+    ms, _ = time_library_steps(torch, wl, lambda i: all_layers, 4, 1, calls.ws)
     ms /= 4
+    # independent calls: outputs of their own per layer
+    own = []
+    for l in range(n_layers):
+        for op, ths, x, y in calls.calls(l):
+            own.append((op, ths, x, torch.empty_like(y)))
+    grouped = wl.Step(own * 1, ws=calls.ws, group_shared_w0=True)
+    grouped.launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(4):
+        grouped.launch()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_grouped = e0.elapsed_time(e1) / 4
+    grouped.close()
     mlp_ms = time_calls(torch, [lambda l=l: calls.mlp(l) for l in range(n_layers)], 2 * n_layers)
     h0 = host_layers[0]
     lay_b, _ = layer_work(h0, dims, T)
@@ -521,11 +559,12 @@ def record_batched_g1(args, torch, wl, inputs, dims):
     mlp_w0 = sum(h0[f]["W0"].numel() * h0[f]["W0"].element_size() for f in ("gate", "up", "down"))
     rec = {"workload": "gemma3-1b-shaped 26 layers sharing one W0 per family (G=1), batched decode T=32, r=32",
            "tokens_per_s": T / (ms * 1e-3), "ms_per_26_layer_step": ms,
+           "ms_per_26_layer_step_grouped_by_w0": ms_grouped,
            "algorithmic_bytes_per_step": n_layers * lay_b, "unique_bytes_per_step": unique,
            "mlp_call": {"us": mlp_ms * 1e3, "algorithmic_bytes": mlp_b,
                         "unique_bytes_26_calls": n_layers * mlp_b - (n_layers - 1) * mlp_w0,
                         "counter_bytes": stored_traffic("batched-decode-G1", r, T)}}
-    del layers, calls
+    del layers, calls, own
     torch.cuda.empty_cache()
     return rec
 
@@ -603,10 +642,9 @@ def run_single(args, torch, np, wl, inputs, orc):
     wl.wl_linear(ths[0], x, y=y, ws=ws)
     torch.cuda.synchronize()
     parity = {"linear": rel_l2(np, y, orc.linear(host, x_host)[0])}
-    fns = [lambda c=c: wl.wl_linear(ths[c], x, y=y, ws=ws) for c in range(copies)]
     K = args.steps if args.steps is not None else DEFAULT_STEPS["single"]
     W = args.warmup if args.warmup is not None else max(1, K // 10)
-    ms_total, wall = time_steps(torch, fns, K, W)
+    ms_total, wall = time_library_steps(torch, wl, lambda i: [(wl.OP_LINEAR, [ths[i % copies]], x, y)], K, W, ws)
     ms = ms_total / K
     b = call_bytes([host], T, d, d)
     achieved = b / (ms * 1e-3) / 1e9

@@ -197,6 +197,60 @@ wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta 
  * Needs no workspace. */
 wl_status wl_materialize_weff(const wl_theta *th, void *W_eff, void *hip_stream);
 
+/* Decode steps ("Throughput" page, "Versus vanilla MAX": at batch 1 a step's
+ * dispatches, not its arithmetic, dominate; "Serve and generate with
+ * weightless", "Current limits": shared-W0 (G = 1) configurations). A step is a
+ * fixed list of wl_linear / wl_qkv_fused / wl_mlp_fused calls that the library
+ * records once into a HIP graph and launches with one call.
+ *   op   WL_OP_LINEAR (th[0]), WL_OP_QKV (th = Q, K, V) or WL_OP_MLP (th =
+ *        gate, up, down); unused th entries are ignored
+ *   x, y, T   as in the op's own call (QKV: y is [T][dq + dk + dv]) */
+typedef struct {
+    int32_t op;
+    const wl_theta *th[3];
+    const void *x;
+    void *y;
+    int32_t T;
+} wl_call;
+
+/* wl_step_create flag: launch the calls that share their first theta's W0 back
+ * to back (groups in order of first appearance, given order within a group),
+ * so that a W0 shared by several layers (G = 1) is read while it is still in
+ * the caches. Allowed only when no call reads or overwrites another call's
+ * output (else WL_ERR_INVALID_ARG); results are the same as in given order. */
+enum { WL_STEP_GROUP_SHARED_W0 = 1 };
+
+typedef struct wl_step_s *wl_step;
+
+/* Workspace bytes of a step: the largest of its calls' wl_workspace_bytes
+ * (the calls run one after another on one workspace). 0 for invalid calls. */
+size_t wl_step_workspace_bytes(const wl_call *calls, int32_t n_calls);
+
+/* Records the calls (1 <= n_calls <= 65536) into a HIP graph, in the given
+ * order or as WL_STEP_GROUP_SHARED_W0 regroups them, each exactly as its own
+ * entry point would launch it (the regime switch is read now), and
+ * instantiates it. Every call is checked as by its own entry point, before
+ * anything runs; on an error no step is made and the message names the call.
+ * The theta structs and the call array are read only here; the device buffers
+ * they and x, y, ws point at must stay allocated while the step exists, and
+ * their contents are read or written at each launch (new x values between
+ * launches are used). ws: ws_bytes >= wl_step_workspace_bytes, 256-byte
+ * aligned, prepared by wl_workspace_init; it may be shared with other calls
+ * and steps that never overlap this step's launches. Creating a step makes
+ * host-side objects (a capture stream, the graph); launching allocates
+ * nothing. A call may read an earlier call's output (given order only). */
+wl_status wl_step_create(const wl_call *calls, int32_t n_calls, int32_t flags, void *ws, size_t ws_bytes,
+                         wl_step *step);
+
+/* One launch of the step's graph on hip_stream (every call, in order). Two
+ * launches of one step, or of steps sharing a workspace, must not overlap:
+ * they share the workspace. */
+wl_status wl_step_launch(wl_step step, void *hip_stream);
+
+/* Frees the step's graph. NULL is accepted. The caller makes sure no launch
+ * of the step is still running (for example by synchronizing its stream). */
+wl_status wl_step_destroy(wl_step step);
+
 /* Size of a set of theta bundles against the dense weights they replace
  * ("What weightless inference costs", "Compression": the ratio of the theta
  * bundle, W0 + s + U + V across every layer and family, to the original

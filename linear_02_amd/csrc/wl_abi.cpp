@@ -13,6 +13,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "wl_kernels.h"
 
@@ -829,3 +830,169 @@ wl_status wl_relative_frobenius_error(const void *W, const void *R, int64_t n, d
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode steps: a fixed list of projection calls recorded once into a HIP graph
+// ("Throughput" page, "Versus vanilla MAX": at batch 1 the extra dispatches,
+// not the arithmetic, dominate), launched with one call.
+
+struct wl_step_s {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+constexpr int kMaxStepCalls = 1 << 16;
+
+int step_thetas(int32_t op) { return op == WL_OP_LINEAR ? 1 : 3; }
+
+// x and y of a call whose thetas passed check_theta.
+void call_ranges(const wl_call &c, Range &x, Range &y) {
+    const size_t es = elem_bytes(c.th[0]);
+    size_t width = 0;
+    if (c.op == WL_OP_QKV)
+        width = (size_t)c.th[0]->d_out + c.th[1]->d_out + c.th[2]->d_out;
+    else if (c.op == WL_OP_MLP)
+        width = (size_t)c.th[2]->d_out;
+    else
+        width = (size_t)c.th[0]->d_out;
+    x = {c.x, (size_t)(c.T > 0 ? c.T : 0) * c.th[0]->d_in * es};
+    y = {c.y, (size_t)(c.T > 0 ? c.T : 0) * width * es};
+}
+
+wl_status run_call(const wl_call &c, void *ws, size_t ws_bytes, hipStream_t s) {
+    switch (c.op) {
+        case WL_OP_LINEAR: return wl_linear(c.th[0], c.x, c.y, c.T, ws, ws_bytes, s);
+        case WL_OP_QKV: return wl_qkv_fused(c.th[0], c.th[1], c.th[2], c.x, c.y, c.T, ws, ws_bytes, s);
+        default: return wl_mlp_fused(c.th[0], c.th[1], c.th[2], c.x, c.y, c.T, ws, ws_bytes, s);
+    }
+}
+
+// The calls' own checks that need no launch: op, thetas, a workspace size.
+wl_status check_calls(const wl_call *calls, int32_t n_calls) {
+    if (!calls) return fail(WL_ERR_INVALID_ARG, "calls is NULL");
+    if (n_calls <= 0 || n_calls > kMaxStepCalls)
+        return fail(WL_ERR_INVALID_ARG, "n_calls=%d is outside [1, %d]", n_calls, kMaxStepCalls);
+    for (int i = 0; i < n_calls; ++i) {
+        const wl_call &c = calls[i];
+        if (c.op != WL_OP_LINEAR && c.op != WL_OP_QKV && c.op != WL_OP_MLP)
+            return fail(WL_ERR_INVALID_ARG, "call %d: op=%d is not WL_OP_LINEAR, WL_OP_QKV or WL_OP_MLP", i, c.op);
+        for (int j = 0; j < step_thetas(c.op); ++j) {
+            char name[32];
+            snprintf(name, sizeof name, "call %d theta %d", i, j);
+            const wl_status st = check_theta(c.th[j], name);
+            if (st != WL_OK) return st;
+        }
+        if (c.T < 0) return fail(WL_ERR_INVALID_ARG, "call %d: T=%d is negative", i, c.T);
+        if (wl_workspace_bytes(c.op, c.th, step_thetas(c.op), c.T) == 0)
+            return fail(WL_ERR_INVALID_ARG, "call %d: invalid thetas for the op", i);
+    }
+    return WL_OK;
+}
+
+}  // namespace
+
+size_t wl_step_workspace_bytes(const wl_call *calls, int32_t n_calls) {
+    if (!calls || n_calls <= 0 || n_calls > kMaxStepCalls) return 0;
+    size_t need = 0;
+    for (int i = 0; i < n_calls; ++i) {
+        const wl_call &c = calls[i];
+        if (c.op != WL_OP_LINEAR && c.op != WL_OP_QKV && c.op != WL_OP_MLP) return 0;
+        const size_t b = wl_workspace_bytes(c.op, c.th, step_thetas(c.op), c.T);
+        if (b == 0) return 0;
+        need = b > need ? b : need;
+    }
+    return need;
+}
+
+wl_status wl_step_create(const wl_call *calls, int32_t n_calls, int32_t flags, void *ws, size_t ws_bytes,
+                         wl_step *step) {
+    if (!step) return fail(WL_ERR_INVALID_ARG, "step is NULL");
+    *step = nullptr;
+    wl_status st = check_calls(calls, n_calls);
+    if (st != WL_OK) return st;
+    if (flags & ~WL_STEP_GROUP_SHARED_W0) return fail(WL_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    if ((st = check_ws(wl_step_workspace_bytes(calls, n_calls), ws, ws_bytes)) != WL_OK) return st;
+
+    // Launch order: as given, or (WL_STEP_GROUP_SHARED_W0) the calls that share
+    // their first theta's W0 back to back, groups in order of first appearance,
+    // calls in their given order within a group. Reordering needs calls that do
+    // not read or overwrite one another's outputs.
+    std::vector<int> order(n_calls);
+    for (int i = 0; i < n_calls; ++i) order[i] = i;
+    if (flags & WL_STEP_GROUP_SHARED_W0) {
+        for (int i = 0; i < n_calls; ++i) {
+            Range xi, yi;
+            call_ranges(calls[i], xi, yi);
+            for (int j = 0; j < n_calls; ++j) {
+                Range xj, yj;
+                call_ranges(calls[j], xj, yj);
+                if (overlaps(yi, xj))
+                    return fail(WL_ERR_INVALID_ARG, "call %d reads the output of call %d: the calls cannot be "
+                                "regrouped (WL_STEP_GROUP_SHARED_W0)", j, i);
+                if (j != i && overlaps(yi, yj))
+                    return fail(WL_ERR_INVALID_ARG, "calls %d and %d write overlapping outputs: the calls cannot be "
+                                "regrouped (WL_STEP_GROUP_SHARED_W0)", i, j);
+            }
+        }
+        std::vector<int> grouped;
+        std::vector<bool> taken(n_calls, false);
+        for (int i = 0; i < n_calls; ++i) {
+            if (taken[i]) continue;
+            for (int j = i; j < n_calls; ++j)
+                if (!taken[j] && calls[j].th[0]->W0 == calls[i].th[0]->W0) {
+                    grouped.push_back(j);
+                    taken[j] = true;
+                }
+        }
+        order = grouped;
+    }
+
+    hipStream_t cs = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e != hipSuccess) return fail(WL_ERR_HIP, "capture stream: %s", hipGetErrorString(e));
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+        hipStreamDestroy(cs);
+        return fail(WL_ERR_HIP, "begin capture: %s", hipGetErrorString(e));
+    }
+    for (int k : order) {
+        st = run_call(calls[k], ws, ws_bytes, cs);
+        if (st != WL_OK) {
+            const std::string msg = "call " + std::to_string(k) + ": " + g_error;
+            hipGraph_t g = nullptr;
+            hipStreamEndCapture(cs, &g);
+            if (g) hipGraphDestroy(g);
+            hipStreamDestroy(cs);
+            return fail(st, "%s", msg.c_str());
+        }
+    }
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    hipStreamDestroy(cs);
+    if (e != hipSuccess || !graph) return fail(WL_ERR_HIP, "end capture: %s", hipGetErrorString(e));
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        hipGraphDestroy(graph);
+        return fail(WL_ERR_HIP, "graph instantiation: %s", hipGetErrorString(e));
+    }
+    *step = new wl_step_s{graph, exec};
+    return ok();
+}
+
+wl_status wl_step_launch(wl_step step, void *hip_stream) {
+    if (!step) return fail(WL_ERR_INVALID_ARG, "step is NULL");
+    const hipError_t e = hipGraphLaunch(step->exec, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(WL_ERR_HIP, "graph launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+wl_status wl_step_destroy(wl_step step) {
+    if (!step) return ok();
+    if (step->exec) hipGraphExecDestroy(step->exec);
+    if (step->graph) hipGraphDestroy(step->graph);
+    delete step;
+    return ok();
+}

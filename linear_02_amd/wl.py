@@ -50,6 +50,14 @@ class Theta(ctypes.Structure):
                 ("r", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+class Call(ctypes.Structure):
+    _fields_ = [("op", ctypes.c_int32), ("th", ctypes.POINTER(Theta) * 3), ("x", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("T", ctypes.c_int32)]
+
+
+STEP_GROUP_SHARED_W0 = 1
+
+
 def _load(path: str = LIBRARY) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run `python -m linear_02_amd.build`")
@@ -81,6 +89,14 @@ def _load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.wl_rel_frob_workspace_bytes.restype = sz
     lib.wl_relative_frobenius_error.argtypes = [vp, vp, ctypes.c_int64, vp, vp, sz, vp]
     lib.wl_relative_frobenius_error.restype = ctypes.c_int
+    lib.wl_step_workspace_bytes.argtypes = [ctypes.POINTER(Call), i32]
+    lib.wl_step_workspace_bytes.restype = sz
+    lib.wl_step_create.argtypes = [ctypes.POINTER(Call), i32, i32, vp, sz, ctypes.POINTER(vp)]
+    lib.wl_step_create.restype = ctypes.c_int
+    lib.wl_step_launch.argtypes = [vp, vp]
+    lib.wl_step_launch.restype = ctypes.c_int
+    lib.wl_step_destroy.argtypes = [vp]
+    lib.wl_step_destroy.restype = ctypes.c_int
     lib.wl_workspace_init.argtypes = [vp, sz, vp]
     lib.wl_workspace_init.restype = ctypes.c_int
     lib.wl_sync_bytes.argtypes = []
@@ -306,3 +322,55 @@ def fallback_count(ws: torch.Tensor) -> int:
 
 def abi_version() -> int:
     return int(lib.wl_abi_version())
+
+
+class Step:
+    """A decode step: a fixed list of calls that the library records once into a
+    HIP graph (wl_step_create) and launches with one call.
+
+    calls: (op, thetas, x, y) tuples, op one of OP_LINEAR (one theta), OP_QKV
+    (Q, K, V), OP_MLP (gate, up, down); device tensors, which must stay alive
+    while the step exists (the step keeps references). group_shared_w0 launches
+    calls that share their first theta's W0 back to back (independent calls
+    only)."""
+
+    def __init__(self, calls, ws: torch.Tensor | None = None, group_shared_w0: bool = False):
+        n = len(calls)
+        arr = (Call * n)()
+        self._keep = []
+        device = None
+        for i, (op, thetas, x, y) in enumerate(calls):
+            if len(thetas) != (1 if op == OP_LINEAR else 3):
+                raise ValueError(f"call {i}: {len(thetas)} thetas for op {op}")
+            T = _io(x, int(thetas[0]["d_in"]), thetas[0]["W0"].dtype)
+            structs = [make_theta(t) for t in thetas]
+            self._keep += [structs, thetas, x, y]
+            arr[i].op = op
+            for j, st in enumerate(structs):
+                arr[i].th[j] = ctypes.pointer(st)
+            arr[i].x, arr[i].y, arr[i].T = _ptr(x), _ptr(y), T
+            device = x.device
+        need = int(lib.wl_step_workspace_bytes(arr, n))
+        if need == 0:
+            raise ValueError("invalid calls for a step")
+        self.ws = ws if ws is not None else new_workspace(need, device)
+        self.device = device
+        h = ctypes.c_void_p()
+        _check(lib.wl_step_create(arr, n, STEP_GROUP_SHARED_W0 if group_shared_w0 else 0, _ptr(self.ws),
+                                  self.ws.numel() * self.ws.element_size(), ctypes.byref(h)))
+        self.handle = h
+
+    def launch(self) -> None:
+        _check(lib.wl_step_launch(self.handle, _stream(self.device)))
+
+    def close(self) -> None:
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            torch.cuda.current_stream(self.device).synchronize()
+            lib.wl_step_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

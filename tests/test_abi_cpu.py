@@ -350,3 +350,57 @@ def test_rel_frob_checks(wl):
     assert f(A, B, 64, C + 4, D, need, None) == 1                # misaligned result
     assert f(A, B, 64, C, D, 0, None) == 4                       # workspace too small
     assert f(A, B, 64, A + 8, D, need, None) == 1                # result on top of W
+
+
+def _calls(wl, specs):
+    """ctypes call array from (op, [theta structs], x, y, T) tuples; keeps the structs alive."""
+    arr = (wl.Call * len(specs))()
+    keep = []
+    for i, (op, ths, x, y, T) in enumerate(specs):
+        keep.append(ths)
+        arr[i].op = op
+        for j, t in enumerate(ths):
+            arr[i].th[j] = ctypes.pointer(t)
+        arr[i].x, arr[i].y, arr[i].T = x, y, T
+    return arr, keep
+
+
+def _create(wl, arr, n, flags=0, ws=D + 0x2000000, ws_bytes=1 << 30):
+    h = ctypes.c_void_p()
+    st = wl.lib.wl_step_create(arr, n, flags, ws, ws_bytes, ctypes.byref(h))
+    return st, h
+
+
+def test_step_validation_before_any_launch(wl):
+    lin = theta(d_in=64, d_out=32)
+    arr, keep = _calls(wl, [(wl.OP_LINEAR, [lin], D, D + 0x100000, 2)])
+    need = wl.lib.wl_step_workspace_bytes(arr, 1)
+    assert need >= wl.SYNC_BYTES
+    assert wl.lib.wl_step_workspace_bytes(arr, 0) == 0
+    assert _create(wl, arr, 0)[0] == wl.WL_ERR_INVALID_ARG                 # no calls
+    assert wl.lib.wl_step_create(arr, 1, 0, D + 0x2000000, 1 << 30, None) == wl.WL_ERR_INVALID_ARG
+    assert _create(wl, arr, 1, flags=4)[0] == wl.WL_ERR_INVALID_ARG        # unknown flag
+    assert _create(wl, arr, 1, ws_bytes=need - 256)[0] == wl.WL_ERR_WORKSPACE
+    assert _create(wl, arr, 1, ws=D + 0x2000000 + 8)[0] == wl.WL_ERR_INVALID_ARG   # misaligned
+    bad, keep2 = _calls(wl, [(7, [lin], D, D + 0x100000, 2)])
+    st, h = _create(wl, bad, 1)
+    assert st == wl.WL_ERR_INVALID_ARG and h.value is None
+    assert b"call 0" in wl.lib.wl_last_error()
+    nul = (wl.Call * 1)()
+    nul[0].op = wl.OP_MLP
+    assert _create(wl, nul, 1)[0] == wl.WL_ERR_INVALID_ARG                  # NULL thetas
+    assert wl.lib.wl_step_destroy(None) == 0
+    assert wl.lib.wl_step_launch(None, None) == wl.WL_ERR_INVALID_ARG
+
+
+def test_step_grouping_needs_independent_calls(wl):
+    a, b = theta(W0=A, d_in=64, d_out=64), theta(W0=A, d_in=64, d_out=64)
+    y1, y2 = D + 0x100000, D + 0x200000
+    # call 1 reads call 0's output: fine in given order, refused when regrouping
+    arr, keep = _calls(wl, [(wl.OP_LINEAR, [a], D, y1, 2), (wl.OP_LINEAR, [b], y1, y2, 2)])
+    st, h = _create(wl, arr, 2, flags=wl.STEP_GROUP_SHARED_W0)
+    assert st == wl.WL_ERR_INVALID_ARG and b"reads the output" in wl.lib.wl_last_error()
+    # two calls writing overlapping outputs
+    arr, keep = _calls(wl, [(wl.OP_LINEAR, [a], D, y1, 2), (wl.OP_LINEAR, [b], D, y1 + 64, 2)])
+    st, h = _create(wl, arr, 2, flags=wl.STEP_GROUP_SHARED_W0)
+    assert st == wl.WL_ERR_INVALID_ARG and b"overlapping outputs" in wl.lib.wl_last_error()
