@@ -27,11 +27,15 @@
 // Memory (measured: reading 64-byte pieces of each down row streams at less
 // than half the rate of whole 128-byte lines, hence slices of 64 inputs shared
 // by P workgroups): the gate/up rows are read by 16-lane row groups, 16 bytes
-// per lane, in batches of two row steps whose loads are all issued before any
-// is used; the workgroup's down rows (128-byte pieces, 8 lanes per row) go into
-// registers right behind the first batch, so the whole workgroup's bytes are
-// in flight together. The down U rows and s, the same for every slice, come
-// from L2. Direct-to-LDS loads are kept to the slice's small operands.
+// per lane, in batches of row steps whose loads are all issued before any is
+// used (at one token per pass one batch holds the part's rows); the
+// workgroup's down rows (128-byte pieces, 8 lanes per row) go into registers,
+// right behind the first batch at two or four tokens, once the gate/up rows
+// are in at one token (the faster order for each, measured). The down U rows
+// and s, the same for every slice, come from L2. Direct-to-LDS loads are kept
+// to the slice's small operands. The down rows of a part are computed as one
+// branch-free block (every pass, then the stores), so that their independent
+// chains interleave.
 #include "wl_device.h"
 #include "wl_kernels.h"
 #include "wl_vtx_slice.h"
@@ -48,7 +52,8 @@ constexpr int kL = kW / 8;                // lanes per down row (one 16-byte pie
 constexpr int kRW = kWave / kL;           // down rows per wave per pass
 constexpr int kPB = kMlpDownPasses;       // down passes per workgroup (kWaves x kRW rows each)
 constexpr int kUB = 9;                    // 16-byte pieces per lane per gate/up row in one batch
-constexpr int kSB = 2;                    // gate/up row steps (4 rows each) per batch
+template <int TT>
+constexpr int kSB = TT == 1 ? 4 : 2;      // gate/up row steps (4 rows each) per batch
 constexpr int kEarlyWords = 16;           // tagged V^T x words per thread read ahead
 
 // 16-byte load through the global address space, not kept in the caches
@@ -136,8 +141,8 @@ __device__ __forceinline__ Part make_part(const MlpDec &a, int j, int p) {
 // (from L2).
 template <int TT>
 struct GateUp {
-    u32x4 wv[kSB][kUB], xv[kUB][TT];
-    float acc[kSB][TT];
+    u32x4 wv[kSB<TT>][kUB], xv[kUB][TT];
+    float acc[kSB<TT>][TT];
 };
 
 template <int TT>
@@ -150,7 +155,7 @@ __device__ __forceinline__ void gu_issue(const MlpDec &a, const Part &pt, int sb
     const u32x4 *xg = reinterpret_cast<const u32x4 *>(a.gu.x + (size_t)a.gu.t0 * D);
     const int nr = max(pt.n, 1);
 #pragma unroll
-    for (int st = 0; st < kSB; ++st) {
+    for (int st = 0; st < kSB<TT>; ++st) {
         const int i = q * (a.WR / 4) + 2 * (sb + st) + (rho >> 1);
         const uint16_t *base = Wrow + (size_t)(pt.i0 + pt.r0 + min(i, nr - 1)) * D;
 #pragma unroll
@@ -178,7 +183,7 @@ __device__ __forceinline__ void gu_compute(const MlpDec &a, int ub, GateUp<TT> &
 #pragma unroll
     for (int u = 0; u < kUB; ++u)
 #pragma unroll
-        for (int st = 0; st < kSB; ++st)
+        for (int st = 0; st < kSB<TT>; ++st)
 #pragma unroll
             for (int t = 0; t < TT; ++t) b.acc[st][t] = dot8(b.wv[st][u], b.xv[u][t], b.acc[st][t]);
 }
@@ -188,7 +193,7 @@ __device__ __forceinline__ void gu_finish(const MlpDec &a, const Part &pt, int s
     const int lane = threadIdx.x & (kWave - 1), q = threadIdx.x / kWave;
     const int rho = lane >> 4, l16 = lane & 15;
 #pragma unroll
-    for (int st = 0; st < kSB; ++st) {
+    for (int st = 0; st < kSB<TT>; ++st) {
         const int i = q * (a.WR / 4) + 2 * (sb + st) + (rho >> 1);
         const bool real = sb + st < a.WR / 8 && i < pt.n;
 #pragma unroll
@@ -202,40 +207,32 @@ __device__ __forceinline__ void gu_finish(const MlpDec &a, const Part &pt, int s
 template <int TT>
 __device__ __forceinline__ void gu_zero(GateUp<TT> &b) {
 #pragma unroll
-    for (int st = 0; st < kSB; ++st)
+    for (int st = 0; st < kSB<TT>; ++st)
 #pragma unroll
         for (int t = 0; t < TT; ++t) b.acc[st][t] = 0.f;
 }
 
-// W0 x of a part's gate/up rows into ml. first_issued() runs once in every
-// thread right after the first batch's loads are issued, later_issued() after
-// each later batch's (the first batch is peeled out of the loops, so what they
-// do stays straight-line code). The caller ends it with a barrier.
-template <int TT, class Hook1, class Hook2>
+// W0 x of a part's gate/up rows into ml, in batches of kSB<TT> row steps.
+// first_issued() runs in every thread right after the first batch's loads are
+// issued, last_issued() right after the last batch's (both after the one batch
+// when there is only one). The first and last batches are peeled out of the
+// loop, so the hooks are straight-line code and the waits of each batch count
+// exactly the loads issued after it. The caller ends it with a barrier.
+// ONE: the part has a single batch (4 or 8 workgroups per slice), fixed at
+// compile time so that each kernel has one code path (two paths would be merged
+// with register copies that wait for the last hook's loads).
+template <int TT, bool ONE, class Hook1, class HookLast>
 __device__ __forceinline__ void gateup_rows(const MlpDec &a, const Part &pt, Lds<TT> &s, Hook1 first_issued,
-                                            Hook2 later_issued) {
+                                            HookLast last_issued) {
     const int nu = ((a.gu.d_in >> 3) + 15) >> 4;
     const int steps = a.WR / 8;
-    {
-        GateUp<TT> b;
-        gu_issue<TT>(a, pt, 0, 0, b);
-        __builtin_amdgcn_sched_barrier(0);
-        first_issued();
-        __builtin_amdgcn_sched_barrier(0);
-        gu_zero<TT>(b);
-        gu_compute<TT>(a, 0, b);
-        for (int ub = kUB; ub < nu; ub += kUB) {
-            gu_issue<TT>(a, pt, 0, ub, b);
-            gu_compute<TT>(a, ub, b);
-        }
-        gu_finish<TT>(a, pt, 0, b, s);
-    }
-    for (int sb = kSB; sb < steps; sb += kSB) {
+    const int nb = ONE ? 1 : (steps + kSB<TT> - 1) / kSB<TT>;
+    auto batch = [&](int sb, auto &&hook) {
         GateUp<TT> b;
         gu_zero<TT>(b);
         gu_issue<TT>(a, pt, sb, 0, b);
         __builtin_amdgcn_sched_barrier(0);
-        later_issued();
+        hook();
         __builtin_amdgcn_sched_barrier(0);
         gu_compute<TT>(a, 0, b);
         for (int ub = kUB; ub < nu; ub += kUB) {
@@ -243,7 +240,17 @@ __device__ __forceinline__ void gateup_rows(const MlpDec &a, const Part &pt, Lds
             gu_compute<TT>(a, ub, b);
         }
         gu_finish<TT>(a, pt, sb, b, s);
+    };
+    if constexpr (ONE) {
+        batch(0, [&]() {
+            first_issued();
+            last_issued();
+        });
+        return;
     }
+    batch(0, first_issued);
+    for (int sb = kSB<TT>; sb < (nb - 1) * kSB<TT>; sb += kSB<TT>) batch(sb, []() {});
+    batch((nb - 1) * kSB<TT>, last_issued);
 }
 
 // The part's gate/up U rows into LDS (direct-to-LDS), and the thread's gate/up
@@ -490,7 +497,8 @@ __device__ __forceinline__ void down_row(const Part &pt, u32x4 wd, u32x4 u, floa
         float rt = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) rt += uk[e] * d.v[t][e];
-        const float m = in ? dot8(wd, d.h[t], 0.f) : 0.f;
+        float m = dot8(wd, d.h[t], 0.f);
+        m = in ? m : 0.f;   // a select, not a branch (a lane past a ragged slice's end)
         p[t] = group_sum_lanes<kL>(so * m + rt);
     }
 }
@@ -551,17 +559,20 @@ __device__ __forceinline__ void down_part_rows(const MlpDec &a, const Part &pt, 
     // group o0 / 8 + kWaves m + q: its words lie a fixed stride apart per pass.
     unsigned long long *w = part_word(a, o0 / kMlpGroup + dl.q, pt.j, 0, TT, dl.ro);
     const int pass_words = kWaves * a.NS * TT * kMlpGroup;
+    // Every pass first, as one block without branches (rows past o1 read
+    // clamped pieces and are not stored), so that the passes' independent
+    // chains interleave; then the stores.
+    float p[kPB][TT];
+#pragma unroll
+    for (int m = 0; m < kPB; ++m) down_row<TT>(pt, b.wd[m], b.u[m], b.so[m], d, p[m]);
 #pragma unroll
     for (int m = 0; m < kPB; ++m) {
         const int o = dl.row(o0, m);
-        if (o - dl.ro >= o1) break;   // wave-uniform: no row of this pass exists
-        float p[TT];
-        down_row<TT>(pt, b.wd[m], b.u[m], b.so[m], d, p);
         if (dl.c == 0 && o < o1) {
 #pragma unroll
             for (int t = 0; t < TT; ++t)
                 if (t < tn)
-                    __hip_atomic_store(w + m * pass_words + t * kMlpGroup, tag | __float_as_uint(p[t]),
+                    __hip_atomic_store(w + m * pass_words + t * kMlpGroup, tag | __float_as_uint(p[m][t]),
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
@@ -695,7 +706,7 @@ __device__ void slice_h_here(const MlpDec &a, int j, Lds<TT> &s) {
         wait_vm<0>();
         put_scale<TT>(sv, s);
         __syncthreads();
-        gateup_rows<TT>(a, pt, s, []() {}, []() {});
+        gateup_rows<TT, false>(a, pt, s, []() {}, []() {});
         __syncthreads();
         form_h<TT>(a, pt, s);
     }
@@ -704,7 +715,7 @@ __device__ void slice_h_here(const MlpDec &a, int j, Lds<TT> &s) {
     __syncthreads();
 }
 
-template <int TT>
+template <int TT, bool ONE>
 __global__ __launch_bounds__(kThreads) void mlp_dec_kernel(MlpDec a) {
     __shared__ Lds<TT> s;
     const GemvF &g = a.gu;
@@ -720,38 +731,40 @@ __global__ __launch_bounds__(kThreads) void mlp_dec_kernel(MlpDec a) {
     const int n_items = vtx_items(g, TT);
     const bool early = n_items <= kThreads && g.S <= kEarlyWords && g.spin_limit > 0;
 
-    // Issue order per wave: the first gate/up batch (two row steps and their
-    // x), the ticket (thread 0), the part's down W0 pieces (registers); the
-    // first batch is then used while the rest streams. Behind the second batch
-    // (or right after the first when there is none): the slice's small operands
-    // (direct-to-LDS) and the read-ahead of the gate/up V^T x words.
+    // Issue order per wave (measured best of the orders tried): the first
+    // gate/up batch, then down's W0 pieces of the part (registers), so that
+    // the whole workgroup's bytes are in flight together; behind the last
+    // batch, the slice's small operands (direct-to-LDS), the read-ahead of the
+    // gate/up V^T x words and the ticket of thread 0 (last: the compiler may
+    // wait for the atomic's result at once, and a wait for any load also
+    // waits for every load issued before it).
     unsigned long long ticket;   // thread 0 only; left undefined elsewhere, so that no copy
                                  // of the atomic's result (and no wait for it) is needed here
     DownRows dr;
     EarlyVtx ev;
     float sv = 0.f;
-    bool staged = false;
-    auto stage_and_peek = [&]() {
-        if (staged) return;
-        staged = true;
-        sv = stage_part<TT>(a, pt, s);
-        stage_vd<TT>(a, pt, s);
-        if (early) early_issue<TT>(g, n_items, ev);
-    };
-    gateup_rows<TT>(
+    gateup_rows<TT, ONE>(
         a, pt, s,
         [&]() {
-            if (tid == 0) ticket = take_ticket(g);
             if (blockIdx.x == 0) advance_empty_copies(g);
-            load_down_w0(a, pt, o0, dr);
+            if constexpr (TT > 1) load_down_w0(a, pt, o0, dr);
         },
-        stage_and_peek);
-    stage_and_peek();   // when the part has one batch only
+        [&]() {
+            sv = stage_part<TT>(a, pt, s);
+            stage_vd<TT>(a, pt, s);
+            early_issue<TT>(g, n_items, ev);   // safe addresses whether or not it is used
+            // Last: the compiler may wait for the atomic's result at once, and
+            // such a wait also waits for everything issued before it.
+            if (tid == 0) ticket = take_ticket(g);
+        });
+    // One token per pass: the whole part's gate/up rows are one batch, and
+    // down's W0 follows once they have arrived (measured faster there).
+    if constexpr (TT == 1) load_down_w0(a, pt, o0, dr);
     if (tid == 0) s.tag = ticket_tag(ticket);
     __syncthreads();
     finish_gateup_vtx<TT>(a, s, early, ev);
-    wait_vm<0>();
-    load_down_us(a, o0, dr);   // in flight while h is formed and exchanged
+    wait_vm<0>();   // the slice's small operands (direct-to-LDS), issued with the last batch
+    load_down_us(a, o0, dr);   // L2 reads, in flight while h is formed and exchanged
     put_scale<TT>(sv, s);
     __syncthreads();
     form_h<TT>(a, pt, s);
@@ -772,7 +785,7 @@ __global__ __launch_bounds__(kThreads) void mlp_dec_kernel(MlpDec a) {
                 wait_vm<0>();
                 put_scale<TT>(svp, s);
                 __syncthreads();
-                gateup_rows<TT>(a, op, s, []() {}, []() {});
+                gateup_rows<TT, false>(a, op, s, []() {}, []() {});
                 __syncthreads();
                 form_h<TT>(a, op, s);
             }
@@ -878,10 +891,14 @@ hipError_t launch_mlp_dec(const MlpDec &a, const MlpPlan &p, hipStream_t stream)
     b.Dp = p.Dp;
     b.NG = p.NG;
     const int grid = p.n_prod + p.NS * p.P;
-    switch (p.tt) {
-        case 4: hipLaunchKernelGGL((mlp_dec_kernel<4>), dim3(grid), dim3(kThreads), 0, stream, b); break;
-        case 2: hipLaunchKernelGGL((mlp_dec_kernel<2>), dim3(grid), dim3(kThreads), 0, stream, b); break;
-        default: hipLaunchKernelGGL((mlp_dec_kernel<1>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+    const bool one = (kW / p.P) / 8 <= (p.tt == 1 ? kSB<1> : kSB<2>);   // one batch of gate/up row steps per part
+    switch (p.tt * 2 + one) {
+        case 8: hipLaunchKernelGGL((mlp_dec_kernel<4, false>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+        case 9: hipLaunchKernelGGL((mlp_dec_kernel<4, true>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+        case 4: hipLaunchKernelGGL((mlp_dec_kernel<2, false>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+        case 5: hipLaunchKernelGGL((mlp_dec_kernel<2, true>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+        case 3: hipLaunchKernelGGL((mlp_dec_kernel<1, true>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+        default: hipLaunchKernelGGL((mlp_dec_kernel<1, false>), dim3(grid), dim3(kThreads), 0, stream, b); break;
     }
     return hipGetLastError();
 }
