@@ -408,7 +408,9 @@ __global__ __launch_bounds__(kThreads) void skinny_main(Skinny g) {
 constexpr int kEpiRows = 32;
 constexpr int kEpiGroups = kThreads / kEpiRows;     // 8 token groups
 
-template <int P, int J, int SMAX, int RB>
+// NVS: a bucket (4 or kSkMaxDin / kSkVtxSlice) holding the call's V^T x slices;
+// the slice loads past n_vsl re-read the last slice and are not added.
+template <int P, int J, int SMAX, int RB, int NVS>
 __global__ __launch_bounds__(kThreads) void skinny_epilogue(Skinny g) {
     __shared__ float vs[kMaxChildren][kSkMaxTok][kMaxRank];
     const int tid = threadIdx.x;
@@ -473,13 +475,13 @@ __global__ __launch_bounds__(kThreads) void skinny_epilogue(Skinny g) {
             const int t = item / q4, k = 4 * (item - t * q4);
             const float *src = g.vpart + ((size_t)c * g.T + t) * kMaxRank + k;
             const size_t sl_stride = (size_t)g.n_ch * g.T * kMaxRank;
-            f32x4 v[kSkMaxDin / kSkVtxSlice];
+            f32x4 v[NVS];
 #pragma unroll
-            for (int sl = 0; sl < kSkMaxDin / kSkVtxSlice; ++sl)
+            for (int sl = 0; sl < NVS; ++sl)
                 v[sl] = ldg(reinterpret_cast<const f32x4 *>(src + (size_t)min(sl, g.n_vsl - 1) * sl_stride));
             f32x4 sum = v[0];
 #pragma unroll
-            for (int sl = 1; sl < kSkMaxDin / kSkVtxSlice; ++sl)
+            for (int sl = 1; sl < NVS; ++sl)
                 if (sl < g.n_vsl) sum += v[sl];
             *reinterpret_cast<f32x4 *>(&vs[c][t][k]) = sum;
         }
@@ -518,17 +520,24 @@ __global__ __launch_bounds__(kThreads) void skinny_epilogue(Skinny g) {
     }
 }
 
-template <int P, int J, int SMAX>
-void launch_epi(const Skinny &g, int max_r, hipStream_t stream) {
+template <int P, int J, int SMAX, int NVS>
+void launch_epi_r(const Skinny &g, int max_r, hipStream_t stream) {
     const dim3 grid((g.rows + kEpiRows - 1) / kEpiRows);
     if (max_r <= 8)
-        hipLaunchKernelGGL((skinny_epilogue<P, J, SMAX, 8>), grid, dim3(kThreads), 0, stream, g);
+        hipLaunchKernelGGL((skinny_epilogue<P, J, SMAX, 8, NVS>), grid, dim3(kThreads), 0, stream, g);
     else if (max_r <= 16)
-        hipLaunchKernelGGL((skinny_epilogue<P, J, SMAX, 16>), grid, dim3(kThreads), 0, stream, g);
+        hipLaunchKernelGGL((skinny_epilogue<P, J, SMAX, 16, NVS>), grid, dim3(kThreads), 0, stream, g);
     else if (max_r <= 32)
-        hipLaunchKernelGGL((skinny_epilogue<P, J, SMAX, 32>), grid, dim3(kThreads), 0, stream, g);
+        hipLaunchKernelGGL((skinny_epilogue<P, J, SMAX, 32, NVS>), grid, dim3(kThreads), 0, stream, g);
     else
-        hipLaunchKernelGGL((skinny_epilogue<P, J, SMAX, 64>), grid, dim3(kThreads), 0, stream, g);
+        hipLaunchKernelGGL((skinny_epilogue<P, J, SMAX, 64, NVS>), grid, dim3(kThreads), 0, stream, g);
+}
+template <int P, int J, int SMAX>
+void launch_epi(const Skinny &g, int max_r, hipStream_t stream) {
+    if (g.n_vsl <= 4)
+        launch_epi_r<P, J, SMAX, 4>(g, max_r, stream);
+    else
+        launch_epi_r<P, J, SMAX, kSkMaxDin / kSkVtxSlice>(g, max_r, stream);
 }
 
 template <int MT, int P>
