@@ -295,16 +295,20 @@ __device__ void vtx_quads(const Skinny &g, float *smem, int c, int t0, int tn, i
             }
         }
     }
-    // Row sums; lane 0 of each 16-lane row stores its row's 32 values.
+    // Row sums (all 32 first, so that their DPP chains interleave); lane 0 of
+    // each 16-lane row stores its row's 32 values.
     float *red = smem;                                                    // [16 rows][kVtxRedLd]
     const int row16 = tid >> 4;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int t = 0; t < kSkVtxTok; ++t) {
-            const float v = row_sum16(acc[e][t]);
-            if ((tid & 15) == 0) red[row16 * kVtxRedLd + e * kSkVtxTok + t] = v;
-        }
+        for (int t = 0; t < kSkVtxTok; ++t) acc[e][t] = row_sum16(acc[e][t]);
+    if ((tid & 15) == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int t = 0; t < kSkVtxTok; ++t) red[row16 * kVtxRedLd + e * kSkVtxTok + t] = acc[e][t];
+    }
     __syncthreads();
     for (int it = tid; it < r * tn; it += kThreads) {
         const int t = it / r, k = it - t * r, q = k >> 2, e = k & 3;
