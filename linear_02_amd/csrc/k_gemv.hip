@@ -37,13 +37,15 @@
 //   tensor is absent) and the value is masked afterwards, and per-child fields
 //   are chosen with selects rather than by indexing the kernel-argument array
 //   with a per-lane index (which becomes a chain of dependent vector loads).
-// Epilogue. The wave sums (DPP butterflies) meet in LDS; the rank term
-//   sum_k U[o,k] vtx[t,k] of each output is one wave's sum (lane k takes one
-//   product); then one thread per (row, token) forms
+// Epilogue. The wave sums (DPP butterflies) meet in LDS with U and s; then one
+//   thread per (row, token) forms
 //     y[t,o] = s[o] * (W0 x)[t,o] + sum_k U[o,k] vtx[t,k]
-//   adding row segments in order, and rounds once to bf16. Pair mode (gate/up
-//   of the MLP) streams the gate row and the up row together and writes
-//   bf16(gelu_tanh(g) * u).
+//   adding row segments in order and the rank term as four interleaved partial
+//   sums (k mod 4) added pairwise, and rounds once to bf16. The steps after
+//   the stream are few and short: each is a chain of dependent instructions of
+//   a single wave, so each barrier-separated step costs a few tenths of a
+//   microsecond. Pair mode (gate/up of the MLP) streams the gate row and the up
+//   row together and writes bf16(gelu_tanh(g) * u).
 #include "wl_device.h"
 #include "wl_kernels.h"
 #include "wl_vtx_slice.h"
@@ -72,11 +74,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
     __shared__ float fgs[INL ? kMaxChildren * TT * kMaxRank : 1];  // fallback group sums
     __shared__ uint32_t tag_lds;
     __shared__ u32x4 xstage[INL && TT > 2 ? TT * kXStageMax / 8 : 1];   // producer / fallback x slice
-    __shared__ float vs[kMaxChildren][TT][kMaxRank];
-    __shared__ float ulds[kMaxRowsG][P][kMaxRank];
+    __shared__ __attribute__((aligned(16))) float vs[kMaxChildren][TT][kMaxRank];
+    __shared__ __attribute__((aligned(16))) float ulds[kMaxRowsG][P][kMaxRank];
     __shared__ float slds[kMaxRowsG][P];
     __shared__ float gsum[kThreads];
-    __shared__ float rterm[kMaxRowsG][P][TT];
 
     // The wave index is uniform: keep it (and what derives from it) in scalar registers.
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -188,6 +189,20 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
                 }
     }
 
+    // ---- epilogue operands into LDS (loaded before the stream) ----
+#pragma unroll
+    for (int u = 0; u < kUPerThread; ++u) {
+        const int item = tid + u * kThreads;
+        if (item < kMaxRowsG * P * kMaxRank) (&ulds[0][0][0])[item] = upre[u];
+    }
+    if (tid < rows_g * P) (&slds[0][0])[tid] = spre;
+    // Split mapping with one group of slices: thread `item` holds its entry's
+    // whole sum and writes it into vs itself. Its (child, token, rank), worked
+    // out while the words may still be on their way.
+    const bool own_entry = split && n_groups == 1;
+    int vc = 0, vt = 0, vk = 0;
+    if (own_entry) vtx_item(g, TT, min(tid, max(n_items - 1, 0)), vc, vt, vk);
+
     // ---- V^T x from this launch's producers ----
     bool have = false, fallback = false;
     if constexpr (INL) {
@@ -206,23 +221,21 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
         }
     }
 
-    // ---- epilogue ----
-#pragma unroll
-    for (int u = 0; u < kUPerThread; ++u) {
-        const int item = tid + u * kThreads;
-        if (item < kMaxRowsG * P * kMaxRank) (&ulds[0][0][0])[item] = upre[u];
-    }
-    if (tid < rows_g * P) (&slds[0][0])[tid] = spre;
-    if (parts || (have && !g.two_level)) {
-        if (split)
-            gsum[tid] = gather_finish(gv, gn);
-        else if (parts)
-            gather_full(g, n_items, vs);
+    // ---- V^T x into vs: each entry is 0 + its group sums in order ----
+    const bool sums = (parts || (have && !g.two_level)) && split;
+    if (sums) {
+        const float v = gather_finish(gv, gn);
+        if (!own_entry)
+            gsum[tid] = v;
+        else if (tid < n_items)
+            vs[vc][vt][vk] = 0.f + v;
+    } else if (parts) {
+        gather_full(g, n_items, vs);
     }
     if constexpr (INL)
         if (fallback) vtx_fallback<TT>(g, n_items, vs, vred, xstage, fgs);
     __syncthreads();
-    if ((parts || (have && !g.two_level)) && split)
+    if (sums && !own_entry) {
         for (int item = tid; item < n_items; item += kThreads) {
             float sum = 0.f;
             for (int j = 0; j < n_groups; ++j) sum += gsum[item * n_groups + j];
@@ -230,24 +243,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
             vtx_item(g, TT, item, c, t, k);
             vs[c][t][k] = sum;
         }
-    __syncthreads();
-
-    // Rank term of each (row, p, token): one wave per output, lane k takes
-    // U[o,k] vtx[t,k], and a wave sum (fixed butterfly order) adds them.
-    if (n_items > 0) {
-        const int n_out = rows_g * P * TT;
-        for (int oi = wave; oi < n_out; oi += kWaves) {
-            const int jr = oi / (P * TT), p = (oi / TT) % P, t = oi % TT;
-            const int row = min(rowbase + jr, g.rows - 1);
-            const int ci = P == 2 ? p : child_index(g, row);
-            const int r = ch_r(g, ci);
-            const float prod = lane < r ? ulds[jr][p][lane] * vs[ci][t][lane] : 0.f;
-            const float sum = wave_sum(prod);
-            if (lane == 0) rterm[jr][p][t] = sum;
-        }
         __syncthreads();
     }
 
+    // ---- outputs ----
+    // One thread per (row, token): the row segments in order, scaled by s, plus
+    // the rank term sum_k U[o,k] vtx[t,k] as four interleaved partial sums (k
+    // mod 4) added pairwise; one RNE cast to bf16.
     for (int idx = tid; idx < rows_g * TT; idx += kThreads) {
         const int jr = idx / TT, t = idx - jr * TT;
         const int rbi = jr / R, j = jr - rbi * R;
@@ -259,7 +261,23 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
         for (int p = 0; p < P; ++p) {
             float m = 0.f;
             for (int sg = 0; sg < nseg; ++sg) m += mbuf[rbi * nseg + sg][j][p][t];
-            val[p] = slds[jr][p] * m + (n_items > 0 ? rterm[jr][p][t] : 0.f);
+            float rt = 0.f;
+            if (n_items > 0) {
+                const int ci = P == 2 ? p : child_index(g, row);
+                const int r = ch_r(g, ci);
+                float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+                for (int k0 = 0; k0 < r; k0 += 4) {
+                    // U past r is zero (masked at its load); vs past r was never written
+                    const f32x4 u = *reinterpret_cast<const f32x4 *>(&ulds[jr][p][k0]);
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(&vs[ci][t][k0]);
+                    a0 += u.x * v.x;
+                    a1 += u.y * (k0 + 1 < r ? v.y : 0.f);
+                    a2 += u.z * (k0 + 2 < r ? v.z : 0.f);
+                    a3 += u.w * (k0 + 3 < r ? v.w : 0.f);
+                }
+                rt = (a0 + a1) + (a2 + a3);
+            }
+            val[p] = slds[jr][p] * m + rt;
         }
         const float out = P == 2 ? gelu_tanh(val[0]) * val[P - 1] : val[0];
         g.y[(size_t)tok * g.ldy + row] = f_bf16(out);
