@@ -130,18 +130,23 @@ def mlp_work(lay: dict, dims: dict, T: int):
     return b, fl
 
 
-# Sources of the kernels each token-count range runs (the shared device headers
-# always count; the host dispatcher does not, so host-only changes such as a new
-# entry point leave the records valid): the decode GEMV with its V^T x launch and
-# the one-launch MLP, the skinny path, the matrix-core GEMM with its V^T x launch.
+# Sources of the kernels that the dominant call (the MLP) runs at each token
+# count, which the traffic records measure (the shared device headers always
+# count; the host dispatcher does not, so host-only changes such as a new entry
+# point leave the records valid): the one-launch MLP (at most 2 tokens), the
+# decode GEMV with its V^T x launch, the skinny path, the matrix-core GEMM with
+# its V^T x launch.
 _COMMON_SOURCES = ("wl_kernels.h", "wl_device.h")
+_MLP_ONE_LAUNCH_MAX_TOK = 2
 
 
 def _regime_sources(tokens: int, dtype: str = "bf16") -> tuple:
     if dtype == "f32":
         return ("k_f32.hip",)
+    if tokens <= _MLP_ONE_LAUNCH_MAX_TOK:
+        return ("k_mlp.hip", "wl_vtx_slice.h", "wl_handoff.h")
     if tokens <= 8:
-        return ("k_gemv.hip", "k_vtx.hip", "wl_vtx_slice.h", "wl_handoff.h", "k_mlp.hip")
+        return ("k_gemv.hip", "k_vtx.hip", "wl_vtx_slice.h", "wl_handoff.h")
     if tokens <= 64:
         return ("k_skinny.hip",)
     return ("k_gemm.hip", "k_vtxmm.hip")
