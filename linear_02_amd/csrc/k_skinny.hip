@@ -246,19 +246,22 @@ __device__ __forceinline__ void load_x_run(const uint16_t *p, uint32_t (&w)[N / 
     }
 }
 
-// Rank r = 4 NQ (NQ a power of two up to 16). Thread (rank quad kc, group grp)
-// takes the M = 2 NQ consecutive inputs [grp M, grp M + M) of the slice: it loads
-// V[i][4kc .. 4kc+4) of each as an 8-byte piece and the 8 tokens' x values of
-// the run as whole vectors, all in flight together (in chunks of at most 16
+// Ranks [k_off, k_off + 4 NQ) of a child of rank rs (NQ a power of two up to
+// 16; the whole rank, or one half of rank 32 or 64 when the V^T x work of a
+// slice is split over two workgroups). Thread (rank quad kc, group grp) takes
+// the M = 2 NQ consecutive inputs [grp M, grp M + M) of the slice: it loads
+// V[i][k_off + 4kc .. + 4) of each as an 8-byte piece and the 8 tokens' x values
+// of the run as whole vectors, all in flight together (in chunks of at most 16
 // inputs), with no LDS staging. The G = 256 / NQ group sums of each (rank,
 // token) are added in a fixed order: 16-lane row sums (DPP), then the rows of a
 // rank quad in row order through LDS.
 template <int NQ>
-__device__ void vtx_quads(const Skinny &g, float *smem, int c, int t0, int tn, int i0, int len, int sl) {
+__device__ void vtx_quads(const Skinny &g, float *smem, int c, int t0, int tn, int i0, int len, int sl, int k_off,
+                          int rs) {
     constexpr int r = 4 * NQ, G = kThreads / NQ, M = kSkVtxSlice / G, MC = M < 16 ? M : 16;
     constexpr int RPQ = G / 16;                                           // 16-lane rows per rank quad
     const int tid = threadIdx.x, kc = tid / G, grp = tid % G;
-    const uint16_t *V = g.ch[c].V + (size_t)i0 * r + 4 * kc;
+    const uint16_t *V = g.ch[c].V + (size_t)i0 * rs + k_off + 4 * kc;
     float acc[4][kSkVtxTok];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -272,7 +275,7 @@ __device__ void vtx_quads(const Skinny &g, float *smem, int c, int t0, int tn, i
         const int ibc = min(ib, ((len - 1) / MC) * MC);
         u32x2 vq[MC];
 #pragma unroll
-        for (int u = 0; u < MC; ++u) vq[u] = ldg(reinterpret_cast<const u32x2 *>(V + (size_t)min(ib + u, len - 1) * r));
+        for (int u = 0; u < MC; ++u) vq[u] = ldg(reinterpret_cast<const u32x2 *>(V + (size_t)min(ib + u, len - 1) * rs));
         uint32_t xw[kSkVtxTok][MC / 2];
 #pragma unroll
         for (int t = 0; t < kSkVtxTok; ++t)
@@ -315,7 +318,7 @@ __device__ void vtx_quads(const Skinny &g, float *smem, int c, int t0, int tn, i
         float sum = red[(q * RPQ) * kVtxRedLd + e * kSkVtxTok + t];
 #pragma unroll
         for (int sub = 1; sub < RPQ; ++sub) sum += red[(q * RPQ + sub) * kVtxRedLd + e * kSkVtxTok + t];
-        g.vpart[(((size_t)sl * g.n_ch + c) * g.T + t0 + t) * kMaxRank + k] = sum;
+        g.vpart[(((size_t)sl * g.n_ch + c) * g.T + t0 + t) * kMaxRank + k_off + k] = sum;
     }
 }
 
@@ -363,19 +366,34 @@ __device__ void vtx_any(const Skinny &g, float *smem, int c, int r, int t0, int 
     }
 }
 
+// Workgroup (child, token block, slice[, rank half]): with vsplit == 2 (every
+// child with V^T x has rank 32 or 64) two workgroups share a slice, each taking
+// half of the rank quads, so that each has half the vector-ALU work.
 __device__ void vtx_wg(const Skinny &g, float *smem, int wgi) {
     const int n_tb = (g.T + kSkVtxTok - 1) / kSkVtxTok;
+    const int hs = wgi % g.vsplit;
+    wgi /= g.vsplit;
     const int sl = wgi % g.n_vsl, tb = (wgi / g.n_vsl) % n_tb, cj = wgi / (g.n_vsl * n_tb);
     const int c = cj == 0 ? g.vtx_ch[0] : cj == 1 ? g.vtx_ch[1] : g.vtx_ch[2];   // uniform
     const int r = g.ch[c].r;
     const int t0 = tb * kSkVtxTok, tn = min(kSkVtxTok, g.T - t0);
     const int i0 = sl * kSkVtxSlice, len = min(kSkVtxSlice, g.d_in - i0);
     switch (r) {
-        case 4: vtx_quads<1>(g, smem, c, t0, tn, i0, len, sl); break;
-        case 8: vtx_quads<2>(g, smem, c, t0, tn, i0, len, sl); break;
-        case 16: vtx_quads<4>(g, smem, c, t0, tn, i0, len, sl); break;
-        case 32: vtx_quads<8>(g, smem, c, t0, tn, i0, len, sl); break;
-        case 64: vtx_quads<16>(g, smem, c, t0, tn, i0, len, sl); break;
+        case 4: vtx_quads<1>(g, smem, c, t0, tn, i0, len, sl, 0, 4); break;
+        case 8: vtx_quads<2>(g, smem, c, t0, tn, i0, len, sl, 0, 8); break;
+        case 16: vtx_quads<4>(g, smem, c, t0, tn, i0, len, sl, 0, 16); break;
+        case 32:
+            if (g.vsplit == 2)
+                vtx_quads<4>(g, smem, c, t0, tn, i0, len, sl, 16 * hs, 32);
+            else
+                vtx_quads<8>(g, smem, c, t0, tn, i0, len, sl, 0, 32);
+            break;
+        case 64:
+            if (g.vsplit == 2)
+                vtx_quads<8>(g, smem, c, t0, tn, i0, len, sl, 32 * hs, 64);
+            else
+                vtx_quads<16>(g, smem, c, t0, tn, i0, len, sl, 0, 64);
+            break;
         default: vtx_any(g, smem, c, r, t0, tn, i0, len, sl); break;
     }
 }

@@ -348,7 +348,11 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
         g.n_rowblk = p.n_rowblk;
         g.kb_per_split = p.kb_per_split;
         g.n_vsl = p.n_vsl;
-        g.n_vtx_wg = p.n_vtx_wg;
+        // Ranks 32 and 64 split their V^T x work over two workgroups per slice.
+        g.vsplit = nv > 0 ? 2 : 1;
+        for (int c = 0; c < n_ch; ++c)
+            if (ch[c].r > 0 && ch[c].r != 32 && ch[c].r != 64) g.vsplit = 1;
+        g.n_vtx_wg = p.n_vtx_wg * g.vsplit;
         e = wl::launch_skinny(g, stream);
     } else if (kind == kKindGemv) {
         wl::GemvF g{};

@@ -224,6 +224,8 @@ struct Skinny {
     float *vpart;         // fp32 [n_vsl][n_ch][T][kMaxRank]
     // plan
     int S, n_rowblk, kb_per_split, n_vsl, n_vtx_wg;
+    int vsplit;                 // V^T x workgroups per (child, token block, slice): 1, or 2
+                                // when every child with r > 0 has r = 32 or 64
     int vtx_ch[kMaxChildren];   // children with r > 0, in order
 };
 struct SkinnyPlan {
