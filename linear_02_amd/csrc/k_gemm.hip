@@ -282,84 +282,169 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         const Child &Cp = *ch[p];
+        // The loads of this child's epilogue are issued before their first use
+        // (s of the lane's outputs, then per batch of two 16-wide rank steps
+        // the V^T x rows of its tokens and the U pieces of its outputs), as
+        // straight-line code with clamped addresses and masks applied
+        // afterwards, so the epilogue waits once per batch instead of once per
+        // load.
+        float sv[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int o = n0 + (wn * TN + j) * 32 + fr;
-            const float sv = Cp.s ? ldg(Cp.s + min(o, d_out - 1)) : 1.0f;
-#pragma unroll
-            for (int i = 0; i < TM; ++i) acc[p][i][j] *= sv;
+            const float *sp = Cp.s ? Cp.s + min(o, d_out - 1) : reinterpret_cast<const float *>(Cp.W0);
+            const float v = ldg(sp);
+            sv[j] = Cp.s ? v : 1.0f;
         }
+        const int r = Cp.r;
         // The rank term is added once: by split 0 when the input axis is split.
-        if constexpr (NV > 0) if (split == 0) {
-            const int r = Cp.r, S = Cp.vtx_splits;
-            const size_t ss = (size_t)g.T * r;        // split stride of the partials
-            for (int k0 = 0; k0 < r; k0 += 16) {
-                const int kb = k0 + 8 * fk;
-                u32x4 ahi[TM], alo[TM], bu[TN];
+        auto scale = [&]() {
 #pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    // vtx[t][kb .. kb+8) for this lane's token row, its split partials
-                    // added in split order; every load unconditional at a clamped
-                    // address, values past T or r masked to zero.
-                    const int t = m0 + (wm * TM + i) * 32 + fr;
-                    const float *src = Cp.vtx + (size_t)min(t, g.T - 1) * r;
-                    float v[8];
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int i = 0; i < TM; ++i) acc[p][i][j] *= sv[j];
+        };
+        if constexpr (NV > 0) {
+            if (split == 0 && r > 0) {
+                const int S = Cp.vtx_splits;
+                const size_t ss = (size_t)g.T * r;        // split stride of the partials
+                // Batches of two 16-wide rank steps (one batch holds r <= 32, NV = 1).
+#pragma unroll
+                for (int b = 0; b < NV; ++b) {
+                    if (b > 0 && 32 * b >= r) break;
+                    f32x4 va[2][TM][2];   // vtx[t][kb .. kb + 8) per step and token block, masked
+                    u32x4 ub[2][TN];      // U[o][kb .. kb + 8) per step and output block, masked
                     if ((r & 3) == 0) {
-                        const int ka = min(kb, r - 4), kc = min(kb + 4, r - 4);
-                        f32x4 s0 = ldg(reinterpret_cast<const f32x4 *>(src + ka));
-                        f32x4 s1 = ldg(reinterpret_cast<const f32x4 *>(src + kc));
+                        // Split 0 of every step's V^T x rows, and the U pieces: every
+                        // address clamped into the tensors, the masks applied after
+                        // the other splits are added in split order.
+#pragma unroll
+                        for (int kq = 0; kq < 2; ++kq) {
+                            const int kb = 32 * b + 16 * kq + 8 * fk;
+#pragma unroll
+                            for (int i = 0; i < TM; ++i) {
+                                const int t = m0 + (wm * TM + i) * 32 + fr;
+                                const float *src = Cp.vtx + (size_t)min(t, g.T - 1) * r;
+                                va[kq][i][0] = ldg(reinterpret_cast<const f32x4 *>(src + min(kb, r - 4)));
+                                va[kq][i][1] = ldg(reinterpret_cast<const f32x4 *>(src + min(kb + 4, r - 4)));
+                            }
+#pragma unroll
+                            for (int j = 0; j < TN; ++j) {
+                                const int o = n0 + (wn * TN + j) * 32 + fr;
+                                const uint16_t *urow = Cp.U + (size_t)min(o, d_out - 1) * r;
+                                if ((r & 7) == 0) {
+                                    ub[kq][j] = ldg(reinterpret_cast<const u32x4 *>(urow + min(kb, r - 8)));
+                                } else {
+                                    // rows 8-byte aligned only: four words of two entries each
+                                    const uint32_t *uw = reinterpret_cast<const uint32_t *>(urow);
+                                    const int w0 = kb / 2, wl = r / 2 - 1;
+                                    ub[kq][j] = u32x4{ldg(uw + min(w0, wl)), ldg(uw + min(w0 + 1, wl)),
+                                                      ldg(uw + min(w0 + 2, wl)), ldg(uw + min(w0 + 3, wl))};
+                                }
+                            }
+                        }
                         for (int q = 1; q < S; ++q) {
-                            s0 += ldg(reinterpret_cast<const f32x4 *>(src + q * ss + ka));
-                            s1 += ldg(reinterpret_cast<const f32x4 *>(src + q * ss + kc));
+#pragma unroll
+                            for (int kq = 0; kq < 2; ++kq) {
+                                const int kb = 32 * b + 16 * kq + 8 * fk;
+#pragma unroll
+                                for (int i = 0; i < TM; ++i) {
+                                    const int t = m0 + (wm * TM + i) * 32 + fr;
+                                    const float *src = Cp.vtx + q * ss + (size_t)min(t, g.T - 1) * r;
+                                    va[kq][i][0] += ldg(reinterpret_cast<const f32x4 *>(src + min(kb, r - 4)));
+                                    va[kq][i][1] += ldg(reinterpret_cast<const f32x4 *>(src + min(kb + 4, r - 4)));
+                                }
+                            }
                         }
-                        const bool ok0 = kb < r, ok1 = kb + 4 < r;
-                        v[0] = ok0 ? s0.x : 0.f; v[1] = ok0 ? s0.y : 0.f; v[2] = ok0 ? s0.z : 0.f; v[3] = ok0 ? s0.w : 0.f;
-                        v[4] = ok1 ? s1.x : 0.f; v[5] = ok1 ? s1.y : 0.f; v[6] = ok1 ? s1.z : 0.f; v[7] = ok1 ? s1.w : 0.f;
+#pragma unroll
+                        for (int kq = 0; kq < 2; ++kq) {
+                            const int kb = 32 * b + 16 * kq + 8 * fk;
+                            const f32x4 z{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int i = 0; i < TM; ++i) {
+                                va[kq][i][0] = kb < r ? va[kq][i][0] : z;
+                                va[kq][i][1] = kb + 4 < r ? va[kq][i][1] : z;
+                            }
+#pragma unroll
+                            for (int j = 0; j < TN; ++j) {
+                                // entries past d_out or r are zero (r even: a word holds
+                                // two entries that are both present or both absent)
+                                const bool ok = n0 + (wn * TN + j) * 32 + fr < d_out;
+                                const u32x4 u = ub[kq][j];
+                                ub[kq][j] = u32x4{ok && kb < r ? u.x : 0u, ok && kb + 2 < r ? u.y : 0u,
+                                                  ok && kb + 4 < r ? u.z : 0u, ok && kb + 6 < r ? u.w : 0u};
+                            }
+                        }
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int kk = min(kb + e, r - 1);
-                            float a = ldg(src + kk);
-                            for (int q = 1; q < S; ++q) a += ldg(src + q * ss + kk);
-                            v[e] = kb + e < r ? a : 0.f;
+                        for (int kq = 0; kq < 2; ++kq) {
+                            const int kb = 32 * b + 16 * kq + 8 * fk;
+#pragma unroll
+                            for (int i = 0; i < TM; ++i) {
+                                // vtx[t][kb .. kb+8) for this lane's token row, its split
+                                // partials added in split order; values past T or r masked to
+                                // zero.
+                                const int t = m0 + (wm * TM + i) * 32 + fr;
+                                const float *src = Cp.vtx + (size_t)min(t, g.T - 1) * r;
+                                float v[8];
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) {
+                                    const int kk = min(kb + e, r - 1);
+                                    float a = ldg(src + kk);
+                                    for (int q = 1; q < S; ++q) a += ldg(src + q * ss + kk);
+                                    v[e] = kb + e < r ? a : 0.f;
+                                }
+                                va[kq][i][0] = f32x4{v[0], v[1], v[2], v[3]};
+                                va[kq][i][1] = f32x4{v[4], v[5], v[6], v[7]};
+                            }
+#pragma unroll
+                            for (int j = 0; j < TN; ++j) {
+                                const int o = n0 + (wn * TN + j) * 32 + fr;
+                                const uint16_t *urow = Cp.U + (size_t)min(o, d_out - 1) * r;
+                                uint32_t h[8];
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) {
+                                    const uint32_t bb = ldg(urow + min(kb + e, r - 1));
+                                    h[e] = (o < d_out && kb + e < r) ? bb : 0u;
+                                }
+                                ub[kq][j] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                                  h[6] | (h[7] << 16)};
+                            }
                         }
                     }
-                    float hi[8], lo[8];
+                    if (b == 0) scale();
+                    // vtx = head + remainder, both bf16, run against U on the matrix cores.
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        hi[e] = bf16_f(f_bf16(v[e]));
-                        lo[e] = v[e] - hi[e];
-                    }
-                    ahi[i] = pack8(hi);
-                    alo[i] = pack8(lo);
-                }
-                // U[o][kb .. kb+8): every load unconditional at a clamped address, the
-                // values past d_out or r masked to zero.
+                    for (int kq = 0; kq < 2; ++kq) {
+                        if (32 * b + 16 * kq >= r) break;
+                        u32x4 ahi[TM], alo[TM];
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int o = n0 + (wn * TN + j) * 32 + fr;
-                    const uint16_t *urow = Cp.U + (size_t)min(o, d_out - 1) * r;
-                    if ((r & 7) == 0) {
-                        const u32x4 v = ldg(reinterpret_cast<const u32x4 *>(urow + min(kb, r - 8)));
-                        bu[j] = (o < d_out && kb < r) ? v : u32x4{0u, 0u, 0u, 0u};
-                    } else {
-                        uint32_t h[8];
+                        for (int i = 0; i < TM; ++i) {
+                            const float v[8] = {va[kq][i][0].x, va[kq][i][0].y, va[kq][i][0].z, va[kq][i][0].w,
+                                                va[kq][i][1].x, va[kq][i][1].y, va[kq][i][1].z, va[kq][i][1].w};
+                            float hi[8], lo[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const uint32_t b = ldg(urow + min(kb + e, r - 1));
-                            h[e] = (o < d_out && kb + e < r) ? b : 0u;
+                            for (int e = 0; e < 8; ++e) {
+                                hi[e] = bf16_f(f_bf16(v[e]));
+                                lo[e] = v[e] - hi[e];
+                            }
+                            ahi[i] = pack8(hi);
+                            alo[i] = pack8(lo);
                         }
-                        bu[j] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+#pragma unroll
+                        for (int i = 0; i < TM; ++i)
+#pragma unroll
+                            for (int j = 0; j < TN; ++j) {
+                                acc[p][i][j] = mfma(ahi[i], ub[kq][j], acc[p][i][j]);
+                                acc[p][i][j] = mfma(alo[i], ub[kq][j], acc[p][i][j]);
+                            }
                     }
                 }
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        acc[p][i][j] = mfma(ahi[i], bu[j], acc[p][i][j]);
-                        acc[p][i][j] = mfma(alo[i], bu[j], acc[p][i][j]);
-                    }
+            } else {
+                scale();
             }
+        } else {
+            scale();
         }
     }
 
@@ -392,7 +477,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
             for (int e = 0; e < 16; ++e) {
                 const int t = m0 + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * fk + (e & 3);
                 if (t < g.T) {
-                    const float v = P == 2 ? gelu_tanh(acc[0][i][j][e]) * acc[P - 1][i][j][e] : acc[0][i][j][e];
+                    const float v = P == 2 ? gelu_tanh_bf16out(acc[0][i][j][e]) * acc[P - 1][i][j][e] : acc[0][i][j][e];
                     g.y[(size_t)t * g.ldy + col0 + o] = f_bf16(v);
                 }
             }
@@ -444,7 +529,8 @@ hipError_t launch_nv(const Gemm &g, hipStream_t stream) {
     int max_r = 0;
     for (int c = 0; c < (g.pair ? 2 : g.n_ch); ++c) max_r = g.ch[c].r > max_r ? g.ch[c].r : max_r;
     if (max_r == 0) return launch_cfg<WM, WN, TM, TN, BK, D, P, 0>(g, stream);
-    return launch_cfg<WM, WN, TM, TN, BK, D, P, 1>(g, stream);
+    if (max_r <= 32) return launch_cfg<WM, WN, TM, TN, BK, D, P, 1>(g, stream);
+    return launch_cfg<WM, WN, TM, TN, BK, D, P, 2>(g, stream);
 }
 
 }  // namespace

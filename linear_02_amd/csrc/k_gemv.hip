@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvF g) {
             }
             val[p] = slds[jr][p] * m + rt;
         }
-        const float out = P == 2 ? gelu_tanh(val[0]) * val[P - 1] : val[0];
+        const float out = P == 2 ? gelu_tanh_bf16out(val[0]) * val[P - 1] : val[0];
         g.y[(size_t)tok * g.ldy + row] = f_bf16(out);
     }
 }

@@ -330,7 +330,7 @@ __device__ __forceinline__ void form_h(const MlpDec &a, const Part &pt, Lds<TT> 
     __syncthreads();
     for (int idx = tid; idx < kW * TT; idx += kThreads) {
         const int i = idx / TT, t = idx % TT;
-        if (i >= pt.r0 && i < pt.r0 + pt.n) s.h[t][i] = f_bf16(gelu_tanh(s.val[0][i][t]) * s.val[1][i][t]);
+        if (i >= pt.r0 && i < pt.r0 + pt.n) s.h[t][i] = f_bf16(gelu_tanh_bf16out(s.val[0][i][t]) * s.val[1][i][t]);
     }
     __syncthreads();
 }

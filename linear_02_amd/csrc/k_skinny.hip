@@ -537,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void skinny_epilogue(Skinny g) {
             }
             val[p] = sv[p] * m + d;
         }
-        const float out = P == 2 ? gelu_tanh(val[0]) * val[P - 1] : val[0];
+        const float out = P == 2 ? gelu_tanh_bf16out(val[0]) * val[P - 1] : val[0];
         g.y[(size_t)t * g.ldy + row] = f_bf16(out);
     }
 }
