@@ -467,20 +467,41 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
         return;
     }
     const int col0 = g.pair ? 0 : C0.col0;
+    const size_t ldy = g.ldy;
+    auto out_value = [&](int i, int j, int e) {
+        return P == 2 ? gelu_tanh_bf16out(acc[0][i][j][e]) * acc[P - 1][i][j][e] : acc[0][i][j][e];
+    };
+    // Element e of block (i, j) sits 8 (e / 4) + e % 4 rows below the lane's first
+    // row of the block: one row pointer per block, row offsets common to all lanes.
+    if (m0 + BM <= g.T) {
+        // Every token row of the tile is present: no per-element checks.
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int o = n0 + (wn * TN + j) * 32 + fr;
+            if (o >= d_out) continue;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                uint16_t *yr = g.y + (size_t)(m0 + (wm * TM + i) * 32 + 4 * fk) * ldy + col0 + o;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) yr[(8 * (e >> 2) + (e & 3)) * ldy] = f_bf16(out_value(i, j, e));
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int o = n0 + (wn * TN + j) * 32 + fr;
         if (o >= d_out) continue;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+            const int tr = m0 + (wm * TM + i) * 32 + 4 * fk;
+            uint16_t *yr = g.y + (size_t)tr * ldy + col0 + o;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int t = m0 + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * fk + (e & 3);
-                if (t < g.T) {
-                    const float v = P == 2 ? gelu_tanh_bf16out(acc[0][i][j][e]) * acc[P - 1][i][j][e] : acc[0][i][j][e];
-                    g.y[(size_t)t * g.ldy + col0 + o] = f_bf16(v);
-                }
+                const int dr = 8 * (e >> 2) + (e & 3);
+                if (tr + dr < g.T) yr[dr * ldy] = f_bf16(out_value(i, j, e));
             }
+        }
     }
 }
 
