@@ -572,7 +572,7 @@ hipError_t launch_nv(const Gemm &g, hipStream_t stream) {
 #define WL_GEMM_TILE_PAIR 2, 2, 2, 2, 64, 2
 #endif
 #ifndef WL_GEMM_TILE_SMALL
-#define WL_GEMM_TILE_SMALL 2, 2, 2, 1, 64, 2
+#define WL_GEMM_TILE_SMALL 2, 2, 2, 1, 64, 3
 #endif
 #ifndef WL_GEMM_TILE_SMALL_PAIR
 #define WL_GEMM_TILE_SMALL_PAIR 2, 2, 2, 1, 64, 2

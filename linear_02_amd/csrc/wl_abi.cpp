@@ -958,7 +958,7 @@ wl_status wl_step_create(const wl_call *calls, int32_t n_calls, int32_t flags, v
     if (e != hipSuccess) return fail(WL_ERR_HIP, "capture stream: %s", hipGetErrorString(e));
     e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) {
-        hipStreamDestroy(cs);
+        (void)hipStreamDestroy(cs);
         return fail(WL_ERR_HIP, "begin capture: %s", hipGetErrorString(e));
     }
     for (int k : order) {
@@ -966,20 +966,20 @@ wl_status wl_step_create(const wl_call *calls, int32_t n_calls, int32_t flags, v
         if (st != WL_OK) {
             const std::string msg = "call " + std::to_string(k) + ": " + g_error;
             hipGraph_t g = nullptr;
-            hipStreamEndCapture(cs, &g);
-            if (g) hipGraphDestroy(g);
-            hipStreamDestroy(cs);
+            (void)hipStreamEndCapture(cs, &g);
+            if (g) (void)hipGraphDestroy(g);
+            (void)hipStreamDestroy(cs);
             return fail(st, "%s", msg.c_str());
         }
     }
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
-    hipStreamDestroy(cs);
+    (void)hipStreamDestroy(cs);
     if (e != hipSuccess || !graph) return fail(WL_ERR_HIP, "end capture: %s", hipGetErrorString(e));
     hipGraphExec_t exec = nullptr;
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
     if (e != hipSuccess) {
-        hipGraphDestroy(graph);
+        (void)hipGraphDestroy(graph);
         return fail(WL_ERR_HIP, "graph instantiation: %s", hipGetErrorString(e));
     }
     *step = new wl_step_s{graph, exec};
@@ -995,8 +995,8 @@ wl_status wl_step_launch(wl_step step, void *hip_stream) {
 
 wl_status wl_step_destroy(wl_step step) {
     if (!step) return ok();
-    if (step->exec) hipGraphExecDestroy(step->exec);
-    if (step->graph) hipGraphDestroy(step->graph);
+    if (step->exec) (void)hipGraphExecDestroy(step->exec);
+    if (step->graph) (void)hipGraphDestroy(step->graph);
     delete step;
     return ok();
 }
