@@ -91,7 +91,7 @@
 extern "C" {
 #endif
 
-#define WL_ABI_VERSION 5
+#define WL_ABI_VERSION 6
 
 /* Bytes at the start of a projection workspace that hold the sync area. */
 #define WL_SYNC_BYTES 9764864
@@ -196,6 +196,16 @@ wl_status wl_mlp_fused(const wl_theta *gate, const wl_theta *up, const wl_theta 
  * fp32 result), written; must not overlap any input.
  * Needs no workspace. */
 wl_status wl_materialize_weff(const wl_theta *th, void *W_eff, void *hip_stream);
+
+/* The effective weight of the precompute-outside path ("Serve and generate
+ * with weightless", "Set the fast path on NVIDIA") for n projections (a
+ * layer's seven, say): wl_materialize_weff for each, in one launch per eight
+ * of them instead of one each; the same values, bit for bit.
+ * th[j], W_eff[j] for j < n as in wl_materialize_weff, all thetas of one
+ * dtype (fp32: one launch per projection); no W_eff may overlap another or
+ * any theta's tensors. Every argument is checked before anything is
+ * launched. n = 0: nothing to do. Needs no workspace. */
+wl_status wl_materialize_weff_batch(const wl_theta *const *th, void *const *W_eff, int32_t n, void *hip_stream);
 
 /* Decode steps ("Throughput" page, "Versus vanilla MAX": at batch 1 a step's
  * dispatches, not its arithmetic, dominate; "Serve and generate with

@@ -773,6 +773,63 @@ wl_status wl_materialize_weff(const wl_theta *th, void *W_eff, void *hip_stream)
     return ok();
 }
 
+wl_status wl_materialize_weff_batch(const wl_theta *const *th, void *const *W_eff, int32_t n, void *hip_stream) {
+    if (n < 0) return fail(WL_ERR_INVALID_ARG, "n=%d is negative", n);
+    if (n == 0) return ok();
+    if (!th || !W_eff) return fail(WL_ERR_INVALID_ARG, "th or W_eff is NULL");
+    // Every argument is checked before anything is launched.
+    for (int32_t j = 0; j < n; ++j) {
+        char name[32];
+        snprintf(name, sizeof name, "theta %d", j);
+        wl_status st = check_theta(th[j], name);
+        if (st != WL_OK) return st;
+        if (th[j]->dtype != th[0]->dtype)
+            return fail(WL_ERR_INVALID_ARG, "thetas 0 and %d differ in dtype", j);
+        if (!W_eff[j]) return fail(WL_ERR_INVALID_ARG, "W_eff %d is NULL", j);
+        if (!aligned(W_eff[j], 16)) return fail(WL_ERR_INVALID_ARG, "W_eff %d is not 16-byte aligned", j);
+    }
+    for (int32_t j = 0; j < n; ++j) {
+        const Range out{W_eff[j], (size_t)th[j]->d_out * th[j]->d_in * elem_bytes(th[j])};
+        for (int32_t i = 0; i < n; ++i) {
+            Range in[4];
+            theta_ranges(th[i], in);
+            for (int q = 0; q < 4; ++q)
+                if (overlaps(out, in[q])) return fail(WL_ERR_INVALID_ARG, "W_eff %d overlaps an input of theta %d", j, i);
+            if (i != j && overlaps(out, {W_eff[i], (size_t)th[i]->d_out * th[i]->d_in * elem_bytes(th[i])}))
+                return fail(WL_ERR_INVALID_ARG, "W_eff %d and %d overlap", j, i);
+        }
+    }
+    const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (th[0]->dtype == WL_DTYPE_F32) {
+        // The fp32 variant has no batched kernel: one launch per projection.
+        for (int32_t j = 0; j < n; ++j) {
+            const wl_status st = wl_materialize_weff(th[j], W_eff[j], hip_stream);
+            if (st != WL_OK) return st;
+        }
+        return ok();
+    }
+    for (int32_t j0 = 0; j0 < n; j0 += wl::kWeffBatchMax) {
+        wl::WeffBatch bt{};
+        int tiles = 0;
+        for (int32_t j = j0; j < n && j < j0 + wl::kWeffBatchMax; ++j) {
+            wl::Weff &w = bt.w[bt.n];
+            w.W0 = static_cast<const uint16_t *>(th[j]->W0);
+            w.s = th[j]->s;
+            w.U = static_cast<const uint16_t *>(th[j]->U);
+            w.V = static_cast<const uint16_t *>(th[j]->V);
+            w.W_eff = static_cast<uint16_t *>(W_eff[j]);
+            w.d_in = th[j]->d_in;
+            w.d_out = th[j]->d_out;
+            w.r = th[j]->r;
+            tiles += wl::weff_tiles(w.d_in, w.d_out);
+            bt.tiles_end[bt.n++] = tiles;
+        }
+        const hipError_t e = wl::launch_weff_batch(bt, stream);
+        if (e != hipSuccess) return fail(WL_ERR_HIP, "materialize launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
 wl_status wl_bundle_size(const wl_theta *const *th, int32_t n_th, size_t *bundle_bytes, size_t *dense_bytes) {
     if (!th || n_th < 1) return fail(WL_ERR_INVALID_ARG, "no thetas");
     if (!bundle_bytes || !dense_bytes) return fail(WL_ERR_INVALID_ARG, "bundle_bytes or dense_bytes is NULL");

@@ -314,6 +314,16 @@ struct Weff {
     int d_in, d_out, r;
 };
 hipError_t launch_weff(const Weff &w, hipStream_t stream);
+// Up to kWeffBatchMax projections in one launch; tiles_end[p] = tiles of
+// entries 0..p (weff_tiles of each), n >= 1 entries.
+constexpr int kWeffBatchMax = 8;
+struct WeffBatch {
+    Weff w[kWeffBatchMax];
+    int tiles_end[kWeffBatchMax];
+    int n;
+};
+int weff_tiles(int d_in, int d_out);
+hipError_t launch_weff_batch(const WeffBatch &bt, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Relative Frobenius error of bf16 R against bf16 W (n elements each): fp64

@@ -22,7 +22,7 @@ import torch
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwl.so")
 
 OP_LINEAR, OP_QKV, OP_MLP = 0, 1, 2
-ABI_VERSION = 5
+ABI_VERSION = 6
 # The first SYNC_BYTES of a projection workspace are the library's sync area:
 # cleared by wl_workspace_init (new_workspace does it) before first use, then
 # written only by the library's calls.
@@ -71,6 +71,8 @@ def _load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.wl_qkv_fused.argtypes = [P, P, P, vp, vp, i32, vp, sz, vp]
     lib.wl_mlp_fused.argtypes = [P, P, P, vp, vp, i32, vp, sz, vp]
     lib.wl_materialize_weff.argtypes = [P, vp, vp]
+    lib.wl_materialize_weff_batch.argtypes = [ctypes.POINTER(P), ctypes.POINTER(vp), i32, vp]
+    lib.wl_materialize_weff_batch.restype = ctypes.c_int
     for name in ("wl_linear", "wl_linear_static", "wl_qkv_fused", "wl_mlp_fused", "wl_materialize_weff"):
         getattr(lib, name).restype = ctypes.c_int
     lib.wl_set_regime.argtypes = [i32]
@@ -261,6 +263,21 @@ def wl_materialize_weff(th: dict, W_eff: torch.Tensor | None = None):
         W_eff = torch.empty(int(th["d_out"]), int(th["d_in"]), dtype=th["W0"].dtype, device=dev)
     _check(lib.wl_materialize_weff(ctypes.byref(st), _ptr(W_eff), _stream(dev)))
     return W_eff
+
+
+def wl_materialize_weff_batch(thetas: list, W_effs: list | None = None) -> list:
+    """wl_materialize_weff for every theta in one launch per eight; returns the
+    W_eff tensors (allocated when W_effs is None)."""
+    if not thetas:
+        return []
+    dev = thetas[0]["W0"].device
+    if W_effs is None:
+        W_effs = [torch.empty(int(t["d_out"]), int(t["d_in"]), dtype=t["W0"].dtype, device=dev) for t in thetas]
+    structs = [make_theta(t) for t in thetas]
+    arr = (ctypes.POINTER(Theta) * len(structs))(*[ctypes.pointer(st) for st in structs])
+    outs = (ctypes.c_void_p * len(W_effs))(*[_ptr(w) for w in W_effs])
+    _check(lib.wl_materialize_weff_batch(arr, outs, len(structs), _stream(dev)))
+    return W_effs
 
 
 def bundle_size(thetas: list) -> tuple:

@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol(wl):
 
 
 def test_abi_version_and_status_strings(wl):
-    assert wl.abi_version() == 5
+    assert wl.abi_version() == 6
     assert wl.lib.wl_status_str(0) == b"ok"
     assert wl.lib.wl_status_str(4) == b"workspace too small"
     assert wl.lib.wl_status_str(99) == b"unknown status"
@@ -190,6 +190,31 @@ def test_weff_checks(wl):
     assert wl.lib.wl_materialize_weff(ctypes.byref(theta(r=99)), D, None) == 2
 
 
+def weff_batch(wl, ths, outs):
+    P = ctypes.POINTER(wl.Theta)
+    arr = (P * len(ths))(*[ctypes.pointer(t) for t in ths])
+    ptrs = (ctypes.c_void_p * len(outs))(*outs)
+    return wl.lib.wl_materialize_weff_batch(arr, ptrs, len(ths), None)
+
+
+def test_weff_batch_checks(wl):
+    # Every case fails validation (or is the n = 0 no-op) before any launch.
+    assert wl.lib.wl_materialize_weff_batch(None, None, 0, None) == 0
+    assert wl.lib.wl_materialize_weff_batch(None, None, -1, None) == 1
+    assert wl.lib.wl_materialize_weff_batch(None, None, 2, None) == 1
+    t0, t1 = theta(), theta(W0=A + 0x100000, U=B + 0x100000, V=C + 0x100000)
+    assert weff_batch(wl, [t0, theta(d_in=60)], [D, D + 0x100000]) == 1      # a bad second theta
+    assert weff_batch(wl, [t0, theta(r=99)], [D, D + 0x100000]) == 2
+    assert weff_batch(wl, [t0, t1], [D, None]) == 1
+    assert weff_batch(wl, [t0, t1], [D, D + 0x100002]) == 1                   # misaligned
+    assert weff_batch(wl, [t0, t1], [D, A + 0x100000]) == 1                   # on theta 1's W0
+    assert weff_batch(wl, [t0, t1], [B + 0x100000, D]) == 1                   # output 0 on theta 1's U
+    assert weff_batch(wl, [t0, t1], [D, D + 0x800]) == 1                      # the outputs overlap
+    assert b"overlap" in wl.lib.wl_last_error()
+    t1.dtype = 1
+    assert weff_batch(wl, [t0, t1], [D, D + 0x100000]) == 1                   # two dtypes
+
+
 def test_regime_switch(wl):
     prev = wl.set_regime(2)
     try:
@@ -223,7 +248,7 @@ def test_workspace_starts_with_the_sync_area(wl):
     text = open(HEADER).read()
     assert re.search(r"#define WL_SYNC_BYTES 9764864\b", text)
     assert re.search(rf"#define WL_STATIC_SCRATCH_BYTES {wl.STATIC_SCRATCH_BYTES}\b", text)
-    assert re.search(r"#define WL_ABI_VERSION 5\b", text)
+    assert re.search(r"#define WL_ABI_VERSION 6\b", text)
 
 
 def test_workspace_init_checks(wl):

@@ -257,6 +257,25 @@ def test_weff_matches_oracle(wl, orc, d_in, d_out, r):
     assert rel <= 2e-3
 
 
+def test_weff_batch_equals_single_calls(wl, orc):
+    """wl_materialize_weff_batch: the seven projections of a Gemma-3-1B-shaped
+    layer plus ragged shapes, r = 0 with s = None, odd ranks and rank 64 (ten
+    thetas: two launches), bit for bit the one-projection results, and one of
+    them against the oracle."""
+    g = gen(4100)
+    sh = inputs.family_shapes(inputs.GEMMA3_1B)
+    ths = [inputs.theta(g, *sh[f], 32) for f in ("q", "k", "v", "o", "gate", "up", "down")]
+    ths += [inputs.theta(g, 264, 136, 17), no_s(inputs.theta(g, 136, 129, 0)), inputs.theta(g, 8, 1, 64)]
+    dths = [dev(th) for th in ths]
+    outs = wl.wl_materialize_weff_batch(dths)
+    torch.cuda.synchronize()
+    for j, (dth, w) in enumerate(zip(dths, outs)):
+        single = wl.wl_materialize_weff(dth)
+        assert torch.equal(w.view(torch.int16), single.view(torch.int16)), f"theta {j}"
+    w_ref, bound = orc.weff(ths[7])
+    check(outs[7], w_ref, bound, "weff batch 136x264 r=17")
+
+
 def test_weff_passthrough_and_integers(wl, orc):
     g = gen(41)
     th = inputs.theta(g, 264, 136, 0)
