@@ -25,7 +25,11 @@ extern "C" {
  *      (the MLP as a gate/up launch and a down launch);
  *   4  forces the few-token path (split matrix-core products and an epilogue
  *      launch) wherever it applies (T <= 64, d_in <= 8192);
- *   5  as 1, but the MLP as a gate/up launch and a down launch.
+ *   5  as 1, but the MLP as a gate/up launch and a down launch;
+ *   6  as 2, with V^T x always computed by a launch of its own before the GEMM
+ *      and the rank term in the GEMM's epilogue (by default a GEMM whose input
+ *      axis is split computes V^T x in its own launch and adds the rank term in
+ *      its reduction).
  * Where a forced regime does not apply the matrix-core GEMM runs. Returns the
  * previous value, or -1 (and changes nothing) for any other argument. */
 int32_t wl_set_regime(int32_t regime);

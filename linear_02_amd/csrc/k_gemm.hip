@@ -36,8 +36,7 @@
 // accuracy. Results are rounded once to bf16. Pair mode (the MLP's gate/up)
 // keeps two accumulator sets over the same x tile and writes
 // bf16(gelu_tanh(g) * u).
-#include "wl_device.h"
-#include "wl_kernels.h"
+#include "wl_vtxmm.h"
 
 namespace wl {
 
@@ -86,11 +85,15 @@ __device__ __forceinline__ void barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int WM, int WN, int TM, int TN, int BK, int P, int D, int NV>
+// PV > 0: the launch also carries g.n_prod V^T x units (32-wide rank blocks
+// PV), workgroups after the tiles, which the tiles do not read (the split
+// reduction adds the rank term after this launch).
+template <int WM, int WN, int TM, int TN, int BK, int P, int D, int NV, int PV = 0>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(Gemm g) {
     using C = Cfg<WM, WN, TM, TN, BK, P, D, NV>;
     constexpr int BM = C::BM, BN = C::BN, KP = C::KP, NT = C::kThreads;
-    __shared__ u32x4 lds[C::LDS_PIECES];
+    constexpr int kVtxPieces = PV > 0 ? vtx_unit_lds_bytes<WM * WN, PV>() / 16 : 0;
+    __shared__ u32x4 lds[C::LDS_PIECES > kVtxPieces ? C::LDS_PIECES : kVtxPieces];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
@@ -103,6 +106,14 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
         for (int c = 0; c < g.n_ch; ++c) n_nt += (g.ch[c].d_out + BN - 1) / BN;
     const int n_mt = (g.T + BM - 1) / BM;
     const int tiles = n_nt * n_mt, total = tiles * g.ksplit;
+    if constexpr (PV > 0) {
+        if ((int)blockIdx.x >= total) {
+            const int q = blockIdx.x - total, n_tb = (g.T + 31) / 32;
+            vtxmm_unit<WM * WN, PV, 0>(g.job, q % n_tb, (q / n_tb) % g.job.S, q / (n_tb * g.job.S),
+                                       reinterpret_cast<unsigned char *>(lds));
+            return;
+        }
+    }
     int tile;
     {
         const int per = (total + 7) / 8, x = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -505,7 +516,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
     }
 }
 
-template <int WM, int WN, int TM, int TN, int BK, int D, int P, int NV>
+template <int WM, int WN, int TM, int TN, int BK, int D, int P, int NV, int PV = 0>
 hipError_t launch_cfg(const Gemm &g, hipStream_t stream) {
     using C = Cfg<WM, WN, TM, TN, BK, P, D, NV>;
     int n_nt = 0;
@@ -513,8 +524,9 @@ hipError_t launch_cfg(const Gemm &g, hipStream_t stream) {
         n_nt = (g.ch[0].d_out + C::BN - 1) / C::BN;
     else
         for (int c = 0; c < g.n_ch; ++c) n_nt += (g.ch[c].d_out + C::BN - 1) / C::BN;
-    const int total = n_nt * ((g.T + C::BM - 1) / C::BM) * g.ksplit;
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BK, P, D, NV>), dim3(total), dim3(C::kThreads), 0, stream, g);
+    const int total = n_nt * ((g.T + C::BM - 1) / C::BM) * g.ksplit + (PV > 0 ? g.n_prod : 0);
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, BK, P, D, NV, PV>), dim3(total), dim3(C::kThreads), 0, stream,
+                       g);
     return hipGetLastError();
 }
 
@@ -542,6 +554,74 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *part, in
                 dst[e] = f_bf16(a);
             }
         }
+    }
+}
+
+// The same with the rank term (0 < r <= 32) formed here, from the complete V^T x:
+//   y[t][col0 + o] = bf16( sum over splits q, in order, of part[q][t][o]
+//                          + sum over k, in increasing order, of U[o][k] vtx[t][k] )
+// in fp32, S (2 to kRedMaxSplit) splits. Thread per output o (its U row held in
+// registers), kRedTok tokens per workgroup: the workgroup's V^T x rows go to
+// LDS once, every load is issued before any is used (addresses clamped into
+// the tensors, masks applied afterwards, so no branch stands between them), and
+// partials and outputs are read and written in runs across the lanes.
+constexpr int kRedTok = 16;
+constexpr int kRedMaxSplit = kRedMaxSplits;
+static_assert(kRedTok * 32 % 256 == 0, "the V^T x rows of a workgroup fill whole passes of its 256 threads");
+template <int S>
+__global__ __launch_bounds__(256) void split_reduce_rank_kernel(const float *part, int T, int d_out, uint16_t *y,
+                                                                int ldy, int col0, const uint16_t *U,
+                                                                const float *vtx, int r) {
+    __shared__ __attribute__((aligned(16))) float vl[kRedTok][32];
+    const int tid = threadIdx.x;
+    const int o = blockIdx.x * 256 + tid;
+    const int t0 = blockIdx.y * kRedTok;
+    const int oc = min(o, d_out - 1);
+    const size_t ss = (size_t)T * d_out;
+    float pv[kRedTok][S];
+#pragma unroll
+    for (int j = 0; j < kRedTok; ++j) {
+        const float *src = part + (size_t)min(t0 + j, T - 1) * d_out + oc;
+#pragma unroll
+        for (int q = 0; q < S; ++q) pv[j][q] = ldg(src + (size_t)q * ss);
+    }
+    float u[32];
+    const uint16_t *ur = U + (size_t)oc * r;
+    if ((r & 7) == 0) {
+#pragma unroll
+        for (int k0 = 0; k0 < 32; k0 += 8) {
+            const u32x4 w = ldg(reinterpret_cast<const u32x4 *>(ur + min(k0, r - 8)));
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                u[k0 + 2 * e] = k0 < r ? bf16_f(ww[e] & 0xFFFFu) : 0.f;
+                u[k0 + 2 * e + 1] = k0 < r ? bf16_f(ww[e] >> 16) : 0.f;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            const float v = bf16_f(ldg(ur + min(k, r - 1)));
+            u[k] = k < r ? v : 0.f;
+        }
+    }
+    // V^T x rows of the workgroup's tokens (zero past T or r).
+#pragma unroll
+    for (int m = 0; m < kRedTok * 32 / 256; ++m) {
+        const int e = tid + 256 * m, j = e / 32, k = e % 32;
+        const float v = ldg(vtx + (size_t)min(t0 + j, T - 1) * r + min(k, r - 1));
+        vl[j][k] = (t0 + j < T && k < r) ? v : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRedTok; ++j) {
+        float a = pv[j][0];
+#pragma unroll
+        for (int q = 1; q < S; ++q) a += pv[j][q];
+        float rank = 0.f;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) rank = __builtin_fmaf(u[k], vl[j][k], rank);
+        if (o < d_out && t0 + j < T) y[(size_t)(t0 + j) * ldy + col0 + o] = f_bf16(a + rank);
     }
 }
 
@@ -634,8 +714,28 @@ hipError_t launch_gemm(const Gemm &g_in, hipStream_t stream) {
     for (int c = 0; c < (g.pair ? 1 : g.n_ch); ++c) rows += g.ch[c].d_out;
     g.col_fast = g.T > rows * (g.pair ? 2 : 1);   // x ([T][d_in]) larger than the W0 rows it meets
     if (g.ksplit > 1) {
-        const hipError_t e = launch_nv<WL_GEMM_TILE_SPLIT, 1>(g, stream);
+        // With g.n_prod > 0 the tiles leave out the rank term: the launch's extra
+        // workgroups compute V^T x (one split), and the reduction adds U V^T x.
+        // (ranks up to 32: with a second rank block the units' code would cost the
+        // tiles registers).
+        const bool in_reduce = g.n_prod > 0 && g.ch[0].r > 0 && g.ch[0].r <= 32 && g.ksplit <= kRedMaxSplit;
+        const hipError_t e = in_reduce ? launch_cfg<WL_GEMM_TILE_SPLIT, 1, 0, 1>(g, stream)
+                                       : launch_nv<WL_GEMM_TILE_SPLIT, 1>(g, stream);
         if (e != hipSuccess) return e;
+        if (in_reduce) {
+            const dim3 grid((g.ch[0].d_out + 255) / 256, (g.T + kRedTok - 1) / kRedTok);
+            const Child &c = g.ch[0];
+            if (g.ksplit == 2)
+                hipLaunchKernelGGL(split_reduce_rank_kernel<2>, grid, dim3(256), 0, stream, g.part, g.T, c.d_out,
+                                   g.y, g.ldy, c.col0, c.U, c.vtx, c.r);
+            else if (g.ksplit == 3)
+                hipLaunchKernelGGL(split_reduce_rank_kernel<3>, grid, dim3(256), 0, stream, g.part, g.T, c.d_out,
+                                   g.y, g.ldy, c.col0, c.U, c.vtx, c.r);
+            else
+                hipLaunchKernelGGL(split_reduce_rank_kernel<4>, grid, dim3(256), 0, stream, g.part, g.T, c.d_out,
+                                   g.y, g.ldy, c.col0, c.U, c.vtx, c.r);
+            return hipGetLastError();
+        }
         const int64_t n = (int64_t)g.T * ((g.ch[0].d_out + 3) / 4);
         const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
         hipLaunchKernelGGL(split_reduce_kernel, dim3(blocks), dim3(256), 0, stream, g.part, g.ksplit, g.T,

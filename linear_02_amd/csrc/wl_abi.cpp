@@ -127,7 +127,8 @@ Kind choose(int T, int d_in, int sum_r) {
         case 1:
         case 3:
         case 5: return tt ? kKindGemv : kKindGemm;
-        case 2: return kKindGemm;
+        case 2:
+        case 6: return kKindGemm;
         case 4: return sk ? kKindSkinny : kKindGemm;
         default: break;
     }
@@ -385,16 +386,23 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
     } else {
         wl::Gemm g{};
         for (int c = 0; c < n_ch; ++c) g.ch[c] = ch[c];
+        const wl::GemmSplit sp = wl::gemm_split_plan(T, d_in, rows, n_ch, pair);
+        // A split input axis (one child, r <= 32, at most 4 splits) adds the rank term in its
+        // reduction: V^T x (one split) then comes from extra workgroups of the
+        // GEMM launch itself, whose tiles do not read it. Regime 6 keeps the
+        // launch of its own.
+        const bool in_reduce = sp.ksplit > 1 && sp.ksplit <= wl::kRedMaxSplits && sum_r > 0 && sum_r <= 32 &&
+                               g_regime.load(std::memory_order_relaxed) != 6;
         if (sum_r > 0) {
-            // V^T x split partials on the matrix cores, added in order by the GEMM epilogue.
+            // V^T x split partials on the matrix cores, added in order by their consumer.
             wl::VtxMM mm{};
             mm.x = static_cast<const uint16_t *>(x);
             mm.d_in = d_in;
             mm.T = T;
             int max_r = 0;
             for (int c = 0; c < n_ch; ++c) max_r = ch[c].r > max_r ? ch[c].r : max_r;
-            mm.S = wl::vtxmm_splits(d_in, max_r);
             const int nkb = (d_in + 63) / 64;
+            mm.S = in_reduce ? 1 : wl::vtxmm_splits(d_in, max_r);
             mm.kb_per_split = (nkb + mm.S - 1) / mm.S;
             mm.S = (nkb + mm.kb_per_split - 1) / mm.kb_per_split;
             size_t moff = L.mm_vtx;
@@ -409,8 +417,13 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
                 mm.r[mm.n] = ch[c].r;
                 ++mm.n;
             }
-            e = wl::launch_vtxmm(mm, stream);
-            if (e != hipSuccess) return fail(WL_ERR_HIP, "V^T x launch failed: %s", hipGetErrorString(e));
+            if (in_reduce) {
+                g.job = mm;
+                g.n_prod = (T + 31) / 32 * mm.S * mm.n;
+            } else {
+                e = wl::launch_vtxmm(mm, stream);
+                if (e != hipSuccess) return fail(WL_ERR_HIP, "V^T x launch failed: %s", hipGetErrorString(e));
+            }
         }
         g.n_ch = n_ch;
         g.pair = pair;
@@ -419,7 +432,6 @@ wl_status run_proj(const wl::Child *ch, int n_ch, bool pair, int d_in, int T, co
         g.T = T;
         g.x = static_cast<const uint16_t *>(x);
         g.y = static_cast<uint16_t *>(y);
-        const wl::GemmSplit sp = wl::gemm_split_plan(T, d_in, rows, n_ch, pair);
         g.ksplit = sp.ksplit;
         g.kb_per_split = sp.kb_per_split;
         g.part = reinterpret_cast<float *>(ws + L.mm_part);
@@ -543,7 +555,7 @@ const char *wl_status_str(wl_status st) {
 const char *wl_last_error(void) { return g_error.c_str(); }
 
 int32_t wl_set_regime(int32_t regime) {
-    if (regime < 0 || regime > 5) return -1;
+    if (regime < 0 || regime > 6) return -1;
     return g_regime.exchange(regime);
 }
 

@@ -255,7 +255,14 @@ struct Gemm {
     int ksplit;
     int kb_per_split;
     float *part;
+    // Split path only (1 < ksplit <= kRedMaxSplits, one child with 0 < r <= 32): n_prod > 0 moves the
+    // rank term out of the tiles into the reduction; the launch then also runs
+    // n_prod V^T x units of job (one split: job.S = 1, token block fastest),
+    // workgroups after the tiles, writing the child's vtx.
+    VtxMM job;
+    int n_prod;
 };
+constexpr int kRedMaxSplits = 4;   // splits of the input axis the rank-term reduction takes
 struct GemmSplit {
     int ksplit, kb_per_split;
 };

@@ -312,11 +312,12 @@ REGIME_AUTO, REGIME_GEMV, REGIME_MFMA, REGIME_GEMV_TWO_LAUNCH, REGIME_SKINNY, RE
 def set_regime(regime: int) -> int:
     """0 auto, 1 decode kernels (the MLP in one launch where it applies), 2
     matrix-core GEMM, 3 decode GEMV always after a separate V^T x launch, 4
-    few-token split path, 5 as 1 with the MLP as two launches; returns the
-    previous setting (wl_testing.h)."""
+    few-token split path, 5 as 1 with the MLP as two launches, 6 as 2 with
+    V^T x always in a launch of its own and the rank term in the GEMM epilogue;
+    returns the previous setting (wl_testing.h)."""
     prev = int(lib.wl_set_regime(regime))
     if prev < 0:
-        raise ValueError(f"regime {regime} is not one of 0 to 5")
+        raise ValueError(f"regime {regime} is not one of 0 to 6")
     return prev
 
 

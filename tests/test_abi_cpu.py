@@ -219,9 +219,10 @@ def test_regime_switch(wl):
     prev = wl.set_regime(2)
     try:
         assert wl.set_regime(5) == 2
-        assert wl.set_regime(1) == 5
+        assert wl.set_regime(6) == 5
+        assert wl.set_regime(1) == 6
         with pytest.raises(ValueError):
-            wl.set_regime(6)
+            wl.set_regime(7)
     finally:
         wl.set_regime(prev)
 

@@ -35,9 +35,9 @@ def wl():
     return mod
 
 
-@pytest.fixture(params=["gemv", "mfma", "gemv2", "skinny", "mlp2"])
+@pytest.fixture(params=["gemv", "mfma", "gemv2", "skinny", "mlp2", "mfma_sep"])
 def regime(request, wl):
-    prev = wl.set_regime({"gemv": 1, "mfma": 2, "gemv2": 3, "skinny": 4, "mlp2": 5}[request.param])
+    prev = wl.set_regime({"gemv": 1, "mfma": 2, "gemv2": 3, "skinny": 4, "mlp2": 5, "mfma_sep": 6}[request.param])
     yield request.param
     wl.set_regime(prev)
 
@@ -78,6 +78,9 @@ LINEAR_CASES = [
     (136, 129, 17, 12),       # ragged rows and input axis
     (3080, 136, 8, 70),       # matrix cores: input axis split in two, partial last step
     (3080, 131, 8, 70),       # the same with an odd output count (scalar reduction)
+    (3080, 136, 5, 70),       # split input axis, odd rank: the reduction's scalar U path
+    (6912, 256, 32, 1024),    # input axis in 4 splits, the rank term in the reduction
+    (16384, 128, 16, 512),    # 10 splits: the rank term stays in the GEMM epilogue
 ]
 
 
