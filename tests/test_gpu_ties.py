@@ -121,7 +121,7 @@ def expect_ties(orc, y_ref: np.ndarray, what: str) -> np.ndarray:
     return bf16_of_bits(rne_bits(orc, y_ref))
 
 
-REGIMES = [0, 1, 2, 3, 4, 5]
+REGIMES = [0, 1, 2, 3, 4, 5, 6]
 
 
 @pytest.mark.parametrize("T", [1, 3, 32])
@@ -141,6 +141,25 @@ def test_linear_rounds_ties_to_even(wl, orc, regime, T):
     finally:
         wl.set_regime(prev)
     check_exact(y, want, f"linear ties regime {regime} T={T}")
+
+
+@pytest.mark.parametrize("regime", [2, 6])
+def test_split_projection_rounds_ties_to_even(wl, orc, regime):
+    """A projection whose input axis is split (6912 inputs, 256 outputs, T = 1024:
+    four splits): the rank term added in the reduction (regime 2) or in split
+    0's epilogue (regime 6), one rounding either way."""
+    T = 1024
+    th = tie_theta(6912, 256)
+    x = tie_x(T, 6912)
+    y_ref, _ = orc.linear(th, x)
+    want = expect_ties(orc, y_ref, "split linear")
+    prev = wl.set_regime(regime)
+    try:
+        y = wl.wl_linear(wl.theta_to(th, DEV), x.to(DEV))
+        torch.cuda.synchronize()
+    finally:
+        wl.set_regime(prev)
+    check_exact(y, want, f"split linear ties regime {regime}")
 
 
 @pytest.mark.parametrize("T", [1, 4, 32])
