@@ -149,7 +149,7 @@ def _regime_sources(tokens: int, dtype: str = "bf16") -> tuple:
         return ("k_gemv.hip", "k_vtx.hip", "wl_vtx_slice.h", "wl_handoff.h")
     if tokens <= 64:
         return ("k_skinny.hip",)
-    return ("k_gemm.hip", "k_vtxmm.hip")
+    return ("k_gemm.hip", "k_vtxmm.hip", "wl_vtxmm.h")
 
 
 def source_digest(tokens: int, dtype: str = "bf16") -> str:
