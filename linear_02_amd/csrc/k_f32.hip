@@ -358,31 +358,70 @@ __global__ __launch_bounds__(256) void f32_gemm_kernel(F32Proj g) {
 }
 
 // ---- W_eff[o][i] = s[o] W0[o][i] + sum_k U[o][k] V[i][k], fp32 ---------------------
-// Workgroup: 256 consecutive columns i (one per thread, V[i][:] in registers) x 64
-// rows o (U rows and s in LDS).
+// Workgroup: 256 consecutive columns i (one per thread, V[i][:] in registers) x
+// kWeffRows rows o (U rows and s in LDS). Every W0 load of the workgroup is
+// issued before any product, and the products run rank step outer, row inner:
+// kWeffRows independent sums per thread instead of one dependent chain per row
+// (64 rows per workgroup, row after row, took 241 µs for a layer's seven
+// projections, the small ones bound by a single wave's chain).
+constexpr int kWeffRows = 32;
 template <int RB>
-__global__ __launch_bounds__(256) void f32_weff_kernel(WeffF32 w) {
-    __shared__ float Us[64][kMaxRank + 1];
-    __shared__ float ss[64];
-    const int tid = threadIdx.x, i = blockIdx.x * 256 + tid, o0 = blockIdx.y * 64;
-    const int r = w.r, rows = min(64, w.d_out - o0);
-    for (int e = tid; e < 64 * RB; e += 256) {
-        const int row = e / RB, k = e % RB;
-        Us[row][k] = (row < rows && k < r) ? w.U[(size_t)(o0 + row) * r + k] : 0.f;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f32_weff_kernel(WeffF32 w) {
+    __shared__ __attribute__((aligned(16))) float Us[kMaxRank][kWeffRows];   // [k][row]
+    __shared__ float ss[kWeffRows];
+    const int tid = threadIdx.x, i = blockIdx.x * 256 + tid, o0 = blockIdx.y * kWeffRows;
+    const int r = w.r, rows = min(kWeffRows, w.d_out - o0);
+    constexpr int RB1 = RB > 0 ? RB : 1;   // (no iteration when RB = 0)
+    for (int e = tid; e < kWeffRows * RB; e += 256) {
+        const int row = e / RB1, k = e % RB1;
+        Us[k][row] = (row < rows && k < r) ? w.U[(size_t)(o0 + row) * r + k] : 0.f;
     }
-    if (tid < 64) ss[tid] = (tid < rows && w.s) ? w.s[o0 + tid] : 1.0f;
+    if (tid < kWeffRows) ss[tid] = (tid < rows && w.s) ? w.s[o0 + tid] : 1.0f;
+    const int ic = min(i, w.d_in - 1);
+    float w0[kWeffRows];
+#pragma unroll
+    for (int j = 0; j < kWeffRows; ++j)
+        w0[j] = __builtin_nontemporal_load(w.W0 + (size_t)(o0 + min(j, rows - 1)) * w.d_in + ic);
+    float v[RB1];
+    v[0] = 0.f;
+    if (RB == 0) {
+        // no rank term: V is not read (it may be null)
+    } else if ((r & 3) == 0) {
+        // V[i][:] as 16-byte pieces (rows 16-byte aligned), masked past r
+#pragma unroll
+        for (int k = 0; k < RB1; k += 4) {
+            const f32x4 p4 = *reinterpret_cast<const f32x4 *>(w.V + (size_t)ic * r + min(k, r - 4));
+            v[k] = k < r ? p4.x : 0.f;
+            if (k + 1 < RB1) v[k + 1] = k < r ? p4.y : 0.f;
+            if (k + 2 < RB1) v[k + 2] = k < r ? p4.z : 0.f;
+            if (k + 3 < RB1) v[k + 3] = k < r ? p4.w : 0.f;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < RB1; ++k) v[k] = k < r ? w.V[(size_t)ic * r + min(k, r - 1)] : 0.f;
+    }
     __syncthreads();
-    if (i >= w.d_in) return;
-    float v[RB > 0 ? RB : 1];
+    float d[kWeffRows];
 #pragma unroll
-    for (int k = 0; k < RB; ++k) v[k] = k < r ? w.V[(size_t)i * r + k] : 0.f;
-    for (int row = 0; row < rows; ++row) {
-        const size_t idx = (size_t)(o0 + row) * w.d_in + i;
-        float d = 0.f;
+    for (int j = 0; j < kWeffRows; ++j) d[j] = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < RB; ++k) {
+        float uk[kWeffRows];
 #pragma unroll
-        for (int k = 0; k < RB; ++k) d = fmaf(Us[row][k], v[k], d);
-        w.W_eff[idx] = fmaf(ss[row], w.W0[idx], d);
+        for (int q = 0; q < kWeffRows / 4; ++q) {
+            const f32x4 u4 = *reinterpret_cast<const f32x4 *>(&Us[k][4 * q]);
+            uk[4 * q] = u4.x;
+            uk[4 * q + 1] = u4.y;
+            uk[4 * q + 2] = u4.z;
+            uk[4 * q + 3] = u4.w;
+        }
+#pragma unroll
+        for (int j = 0; j < kWeffRows; ++j) d[j] = fmaf(uk[j], v[k], d[j]);
     }
+    if (i >= w.d_in) return;
+#pragma unroll
+    for (int j = 0; j < kWeffRows; ++j)
+        if (j < rows) __builtin_nontemporal_store(fmaf(ss[j], w0[j], d[j]), w.W_eff + (size_t)(o0 + j) * w.d_in + i);
 }
 
 }  // namespace
@@ -445,7 +484,7 @@ hipError_t launch_f32_gemm(const F32Proj &g, hipStream_t stream) {
 }
 
 hipError_t launch_weff_f32(const WeffF32 &w, hipStream_t stream) {
-    const dim3 grid((w.d_in + 255) / 256, (w.d_out + 63) / 64), block(256);
+    const dim3 grid((w.d_in + 255) / 256, (w.d_out + kWeffRows - 1) / kWeffRows), block(256);
     if (w.r == 0) hipLaunchKernelGGL(f32_weff_kernel<0>, grid, block, 0, stream, w);
     else if (w.r <= 8) hipLaunchKernelGGL(f32_weff_kernel<8>, grid, block, 0, stream, w);
     else if (w.r <= 16) hipLaunchKernelGGL(f32_weff_kernel<16>, grid, block, 0, stream, w);
