@@ -212,11 +212,6 @@ __global__ __launch_bounds__(256) void f32_gemm_kernel(F32Proj g) {
     const int wm = wave & 1, wn = wave >> 1;
     const int fr = lane & 31, fh = lane >> 5;
 
-    int n_nt = 0;
-    if (P == 2)
-        n_nt = (g.ch[0].d_out + BN - 1) / BN;
-    else
-        for (int c = 0; c < g.n_ch; ++c) n_nt += (g.ch[c].d_out + BN - 1) / BN;
     const int n_mt = (g.T + kBM - 1) / kBM;
     const int mt = blockIdx.x % n_mt, nt = blockIdx.x / n_mt;
     int cidx = 0, n0 = nt * BN;
