@@ -55,6 +55,7 @@ constexpr int kUB = 9;                    // 16-byte pieces per lane per gate/up
 template <int TT>
 constexpr int kSB = TT == 1 ? 4 : 2;      // gate/up row steps (4 rows each) per batch
 constexpr int kEarlyWords = 16;           // tagged V^T x words per thread read ahead
+constexpr int kRedPitch = 36;             // row of the slice-sum reduction in LDS (32 lanes, padded: no bank conflicts, 16-byte rows)
 
 // 16-byte load through the global address space, not kept in the caches
 // (each W0 element is used once per launch).
@@ -111,7 +112,7 @@ struct Lds {
     alignas(16) uint16_t h[TT][kW];                     // bf16 h of the slice
     float vj[TT][kMaxRank];                             // sum over the slice of V_d[i][k] h[t][i]
     float vjp[kThreads];                                // its row-group sums
-    float red[32][kMlpGroup];                           // reduction of the partial outputs
+    alignas(16) float red[kMlpGroup][kRedPitch];        // reduction of the partial outputs, [output][slice lane]
     uint32_t tag;
     int miss, need;
 };
@@ -391,19 +392,34 @@ __device__ __forceinline__ void form_vj(const MlpDec &a, const Part &pt, Lds<TT>
     if (tid < G * n) {
         const int g = tid / n, item = tid % n, t = item / rd, k = item % rd;
         float acc = 0.f;
-#pragma unroll 8
-        for (int u = 0; u < R; ++u) {
-            const int i = g * R + u, ic = min(i, pt.wj - 1);
-            // a product of two bf16 values is exact in fp32
-            const float v = bf16_f(lds_ld(V + ic * rd + k)) * bf16_f(lds_ld(&s.h[t][ic]));
-            acc += i < pt.wj ? v : 0.f;
+        // R is a multiple of 8: eight rows' reads issued together, then their
+        // products added in row order.
+        for (int u0 = 0; u0 < R; u0 += 8) {
+            uint16_t vv[8], hh[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int ic = min(g * R + u0 + u, pt.wj - 1);
+                vv[u] = lds_ld(V + ic * rd + k);
+                hh[u] = lds_ld(&s.h[t][ic]);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                // a product of two bf16 values is exact in fp32
+                const float v = bf16_f(vv[u]) * bf16_f(hh[u]);
+                acc += g * R + u0 + u < pt.wj ? v : 0.f;
+            }
         }
         s.vjp[tid] = acc;
     }
     __syncthreads();
     if (tid < n) {
-        float acc = s.vjp[tid];
-        for (int g = 1; g < G; ++g) acc += s.vjp[g * n + tid];
+        // the G <= 8 group sums read together, added in group order
+        float gv[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) gv[g] = lds_ld(&s.vjp[min(g, G - 1) * n + tid]);
+        float acc = gv[0];
+#pragma unroll
+        for (int g = 1; g < 8; ++g) acc = g < G ? acc + gv[g] : acc;
         s.vj[tid / rd][tid % rd] = acc;
     }
     __syncthreads();
@@ -424,10 +440,21 @@ struct DownLane {
     __device__ __forceinline__ int row(int o0, int pass) const { return o0 + pass * (kWaves * kRW) + q * kRW + ro; }
 };
 
+// The down operands (W0, U and s of down) each span less than 4 GiB (the plan
+// bounds d_out by the rows the parts hold and the intermediate axis by the
+// slices), so their offsets are formed in 32 bits and added to the uniform base.
+static_assert((unsigned long long)kMlpDownPasses * kWaves * kRW * 8 * kMlpMaxSlices * kW * 2 < (1ull << 32),
+              "down W0 offsets fit 32 bits");
+template <class T, class B>
+__device__ __forceinline__ const T *at_byte(const B *base, uint32_t bytes) {
+    return reinterpret_cast<const T *>(reinterpret_cast<const unsigned char *>(base) + bytes);
+}
+
 // The lane's piece of down row o (row and piece clamped into the tensor).
 __device__ __forceinline__ u32x4 load_down_piece(const MlpDec &a, const Part &pt, int o) {
     const DownLane dl;
-    return ld_stream(a.W0d + (size_t)min(o, a.D - 1) * a.F + pt.i0 + 8 * min(dl.c, pt.wj / 8 - 1));
+    const uint32_t e = (uint32_t)min(o, a.D - 1) * (uint32_t)a.F + (uint32_t)(pt.i0 + 8 * min(dl.c, pt.wj / 8 - 1));
+    return ld_stream(at_byte<uint16_t>(a.W0d, 2u * e));
 }
 
 // The lane's rank slots e = 0..7: k = 8c + e when rd is a multiple of 8, else
@@ -515,25 +542,35 @@ struct DownRows {
 };
 __device__ __forceinline__ void load_down_w0(const MlpDec &a, const Part &pt, int o0, DownRows &b) {
     const DownLane dl;
+    // load_down_piece for the rows of every pass, the clamped row offsets formed
+    // as in load_down_us
+    const uint32_t ob = (uint32_t)dl.row(o0, 0), last = (uint32_t)(a.D - 1), step = kWaves * kRW, F = (uint32_t)a.F;
+    const uint32_t col = (uint32_t)(pt.i0 + 8 * min(dl.c, pt.wj / 8 - 1));
 #pragma unroll
-    for (int m = 0; m < kPB; ++m) b.wd[m] = load_down_piece(a, pt, dl.row(o0, m));
+    for (int m = 0; m < kPB; ++m) b.wd[m] = ld_stream(at_byte<uint16_t>(a.W0d, 2u * (min((ob + m * step) * F, last * F) + col)));
 }
 // One wave-uniform branch each for the U layout and for s, outside the row
 // loops, so that every load of a loop is issued before any is waited for.
 __device__ __forceinline__ void load_down_us(const MlpDec &a, int o0, DownRows &b) {
     const DownLane dl;
     const int rd = a.rd;
+    // Row of pass m: min(o_0 + m kWaves kRW, D - 1), whose offsets are the
+    // clamped multiples min((o_0 + m kWaves kRW) rd, (D - 1) rd): one product per
+    // lane, then additions.
+    const uint32_t ob = (uint32_t)dl.row(o0, 0), last = (uint32_t)(a.D - 1), step = kWaves * kRW;
     if (rd > 0 && rd % 8 == 0) {
+        const uint32_t piece = 8u * (uint32_t)min(dl.c, rd / 8 - 1);
 #pragma unroll
         for (int m = 0; m < kPB; ++m) {
-            const int o = min(dl.row(o0, m), a.D - 1);
-            b.u[m] = ldg(reinterpret_cast<const u32x4 *>(a.Ud + (size_t)o * rd) + min(dl.c, rd / 8 - 1));
+            const uint32_t e = min((ob + m * step) * (uint32_t)rd, last * (uint32_t)rd) + piece;
+            b.u[m] = ldg(at_byte<u32x4>(a.Ud, 2u * e));
         }
     } else if (rd > 0) {
+        const uint32_t k = (uint32_t)min(dl.c, rd - 1);
 #pragma unroll
         for (int m = 0; m < kPB; ++m) {
-            const int o = min(dl.row(o0, m), a.D - 1);
-            b.u[m] = u32x4{(uint32_t)ldg(a.Ud + (size_t)o * rd + min(dl.c, rd - 1)), 0u, 0u, 0u};
+            const uint32_t e = min((ob + m * step) * (uint32_t)rd, last * (uint32_t)rd) + k;
+            b.u[m] = u32x4{(uint32_t)ldg(at_byte<uint16_t>(a.Ud, 2u * e)), 0u, 0u, 0u};
         }
     } else {
 #pragma unroll
@@ -541,7 +578,7 @@ __device__ __forceinline__ void load_down_us(const MlpDec &a, int o0, DownRows &
     }
     if (a.sd) {
 #pragma unroll
-        for (int m = 0; m < kPB; ++m) b.so[m] = ldg(a.sd + min(dl.row(o0, m), a.D - 1));
+        for (int m = 0; m < kPB; ++m) b.so[m] = ldg(at_byte<float>(a.sd, 4u * min(ob + m * step, last)));
     } else {
 #pragma unroll
         for (int m = 0; m < kPB; ++m) b.so[m] = 1.f;
@@ -829,12 +866,22 @@ __global__ __launch_bounds__(kThreads) void mlp_dec_kernel(MlpDec a) {
                 }
                 reduce_poll<TT>(a, q, t, tag32, kSpinLimit, sum);
             }
-            s.red[js][oo] = sum;
+            s.red[oo][js] = sum;
             __syncthreads();
             if (tid < kMlpGroup) {
                 const int o = q * kMlpGroup + tid;
+                // All 32 values read first (vector reads), then added in order.
+                f32x4 rv[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) rv[m] = lds_ld(reinterpret_cast<const f32x4 *>(&s.red[tid][4 * m]));
                 float y = 0.f;
-                for (int jj = 0; jj < 32; ++jj) y += s.red[jj][tid];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    y += rv[m].x;
+                    y += rv[m].y;
+                    y += rv[m].z;
+                    y += rv[m].w;
+                }
                 if (o < a.D) a.y[(size_t)(g.t0 + t) * a.D + o] = f_bf16(y);
             }
             __syncthreads();
