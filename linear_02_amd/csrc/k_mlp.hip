@@ -457,10 +457,16 @@ __device__ __forceinline__ u32x4 load_down_piece(const MlpDec &a, const Part &pt
     return ld_stream(at_byte<uint16_t>(a.W0d, 2u * e));
 }
 
-// The lane's rank slots e = 0..7: k = 8c + e when rd is a multiple of 8, else
-// (rd < 8) slot 0 is k = c. Slots without an entry below rd hold zero, in U
-// and in vj alike, so every lane runs the same eight products.
+// The lane's rank slots e = 0..SL-1. SL = 4 (rd a multiple of 4, at most 32):
+// k = 4c + e. SL = 8: k = 8c + e when rd is a multiple of 8, else (rd < 8) slot
+// 0 is k = c. Slots without an entry below rd hold zero, in U and in vj alike,
+// so every lane runs the same SL products.
+template <int SL>
 __device__ __forceinline__ bool rank_slot(int rd, int c, int e, int &k) {
+    if (SL == 4) {
+        k = 4 * c + e;
+        return k < rd;
+    }
     if (rd % 8 == 0) {
         k = 8 * c + e;
         return k < rd;
@@ -468,39 +474,48 @@ __device__ __forceinline__ bool rank_slot(int rd, int c, int e, int &k) {
     k = c;
     return e == 0 && c < rd;
 }
+// Slots per lane for a down rank rd: four where the row's ranks fit four per
+// lane (half the products and U bytes of eight), else eight.
+__host__ __device__ constexpr int rank_slots(int rd) { return rd % 4 == 0 && rd <= 4 * kL ? 4 : 8; }
 
-// U_d[o][k] for the lane's rank slots (rd > 0): piece c of the row when rd is
-// a multiple of 8, else entry c in the low half of the first word; the piece
+// U_d[o][k] for the lane's rank slots (rd > 0): with SL = 4 the 8-byte piece
+// c of the row (in the low half); with SL = 8 the 16-byte piece c when rd is
+// a multiple of 8, else entry c in the low half of the first word. The piece
 // or entry is clamped into the row, so slots past rd hold copies that
 // down_row masks out (the mask is applied where the value is used, so that no
 // load has to have arrived when the next is issued).
+template <int SL>
 __device__ __forceinline__ u32x4 load_u_piece(const MlpDec &a, int c, int o) {
     const int rd = a.rd;
     const uint16_t *row = a.Ud + (size_t)min(o, a.D - 1) * rd;
+    if (SL == 4) {
+        const u32x2 v = ldg(reinterpret_cast<const u32x2 *>(row) + min(c, rd / 4 - 1));
+        return u32x4{v.x, v.y, 0u, 0u};
+    }
     if (rd % 8 == 0) return ldg(reinterpret_cast<const u32x4 *>(row) + min(c, rd / 8 - 1));
     return u32x4{(uint32_t)ldg(row + min(c, rd - 1)), 0u, 0u, 0u};
 }
 
 // What every down row of the lane uses: its 16-byte piece of h and its vj
 // slots, per token.
-template <int TT>
+template <int TT, int SL>
 struct DownIn {
     u32x4 h[TT];
-    float v[TT][8];
+    float v[TT][SL];
     bool uok;   // the lane has rank slots below rd
 };
-template <int TT>
-__device__ __forceinline__ void load_down_in(const MlpDec &a, const Lds<TT> &s, DownIn<TT> &d) {
+template <int TT, int SL>
+__device__ __forceinline__ void load_down_in(const MlpDec &a, const Lds<TT> &s, DownIn<TT, SL> &d) {
     const DownLane dl;
     int k0;
-    d.uok = rank_slot(a.rd, dl.c, 0, k0);
+    d.uok = rank_slot<SL>(a.rd, dl.c, 0, k0);
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
         d.h[t] = lds_ld(reinterpret_cast<const u32x4 *>(s.h[t]) + dl.c);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < SL; ++e) {
             int k;
-            const bool ok = rank_slot(a.rd, dl.c, e, k);
+            const bool ok = rank_slot<SL>(a.rd, dl.c, e, k);
             const float v = lds_ld(&s.vj[t][min(k, kMaxRank - 1)]);
             d.v[t][e] = ok ? v : 0.f;
         }
@@ -510,20 +525,20 @@ __device__ __forceinline__ void load_down_in(const MlpDec &a, const Lds<TT> &s, 
 // p_j[t][o] of one down row, on every lane of the row's kL-lane group: the sum
 // over the group's lanes of s[o] * (W0 h over the lane's 8 inputs) + (U vj over
 // the lane's rank slots).
-template <int TT>
-__device__ __forceinline__ void down_row(const Part &pt, u32x4 wd, u32x4 u, float so, const DownIn<TT> &d,
+template <int TT, int SL>
+__device__ __forceinline__ void down_row(const Part &pt, u32x4 wd, u32x4 u, float so, const DownIn<TT, SL> &d,
                                          float (&p)[TT]) {
     const DownLane dl;
     const bool in = 8 * dl.c < pt.wj;
-    const u32x4 z{0u, 0u, 0u, 0u};
-    u = d.uok ? u : z;
-    const float uk[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
-                         bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+    const uint32_t uw[4] = {d.uok ? u.x : 0u, d.uok ? u.y : 0u, d.uok ? u.z : 0u, d.uok ? u.w : 0u};
+    float uk[SL];
+#pragma unroll
+    for (int e = 0; e < SL; ++e) uk[e] = e & 1 ? bf16_hi(uw[e >> 1]) : bf16_lo(uw[e >> 1]);
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
         float rt = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rt += uk[e] * d.v[t][e];
+        for (int e = 0; e < SL; ++e) rt += uk[e] * d.v[t][e];
         float m = dot8(wd, d.h[t], 0.f);
         m = in ? m : 0.f;   // a select, not a branch (a lane past a ragged slice's end)
         p[t] = group_sum_lanes<kL>(so * m + rt);
@@ -551,6 +566,7 @@ __device__ __forceinline__ void load_down_w0(const MlpDec &a, const Part &pt, in
 }
 // One wave-uniform branch each for the U layout and for s, outside the row
 // loops, so that every load of a loop is issued before any is waited for.
+template <int SL>
 __device__ __forceinline__ void load_down_us(const MlpDec &a, int o0, DownRows &b) {
     const DownLane dl;
     const int rd = a.rd;
@@ -558,7 +574,15 @@ __device__ __forceinline__ void load_down_us(const MlpDec &a, int o0, DownRows &
     // clamped multiples min((o_0 + m kWaves kRW) rd, (D - 1) rd): one product per
     // lane, then additions.
     const uint32_t ob = (uint32_t)dl.row(o0, 0), last = (uint32_t)(a.D - 1), step = kWaves * kRW;
-    if (rd > 0 && rd % 8 == 0) {
+    if (SL == 4 && rd > 0) {
+        const uint32_t piece = 4u * (uint32_t)min(dl.c, rd / 4 - 1);
+#pragma unroll
+        for (int m = 0; m < kPB; ++m) {
+            const uint32_t e = min((ob + m * step) * (uint32_t)rd, last * (uint32_t)rd) + piece;
+            const u32x2 v = ldg(at_byte<u32x2>(a.Ud, 2u * e));
+            b.u[m] = u32x4{v.x, v.y, 0u, 0u};
+        }
+    } else if (rd > 0 && rd % 8 == 0) {
         const uint32_t piece = 8u * (uint32_t)min(dl.c, rd / 8 - 1);
 #pragma unroll
         for (int m = 0; m < kPB; ++m) {
@@ -586,9 +610,9 @@ __device__ __forceinline__ void load_down_us(const MlpDec &a, int o0, DownRows &
 }
 
 // The part's down rows [o0, o1) of slice j as tagged words.
-template <int TT>
+template <int TT, int SL>
 __device__ __forceinline__ void down_part_rows(const MlpDec &a, const Part &pt, int o0, int o1, const DownRows &b,
-                                               const DownIn<TT> &d, unsigned long long tag) {
+                                               const DownIn<TT, SL> &d, unsigned long long tag) {
     static_assert(kRW == kMlpGroup, "a wave's rows of one pass are one output group");
     const DownLane dl;
     const int tn = min(TT, a.gu.T - a.gu.t0);
@@ -601,7 +625,7 @@ __device__ __forceinline__ void down_part_rows(const MlpDec &a, const Part &pt, 
     // chains interleave; then the stores.
     float p[kPB][TT];
 #pragma unroll
-    for (int m = 0; m < kPB; ++m) down_row<TT>(pt, b.wd[m], b.u[m], b.so[m], d, p[m]);
+    for (int m = 0; m < kPB; ++m) down_row<TT, SL>(pt, b.wd[m], b.u[m], b.so[m], d, p[m]);
 #pragma unroll
     for (int m = 0; m < kPB; ++m) {
         const int o = dl.row(o0, m);
@@ -618,7 +642,7 @@ __device__ __forceinline__ void down_part_rows(const MlpDec &a, const Part &pt, 
 // p_j for the rows of output group q only (a reducer computing a slice whose
 // words did not come): wave 0, rows 8q .. 8q + 7 (one pass of kRW = 8 rows),
 // the same per-row arithmetic.
-template <int TT>
+template <int TT, int SL>
 __device__ __forceinline__ void down_group_rows(const MlpDec &a, const Part &pt, int q, const Lds<TT> &s,
                                                 unsigned long long tag) {
     static_assert(kRW == kMlpGroup, "one pass of a wave covers one output group");
@@ -627,12 +651,12 @@ __device__ __forceinline__ void down_group_rows(const MlpDec &a, const Part &pt,
     if (dl.q != 0) return;
     const int o = q * kMlpGroup + dl.ro;
     const u32x4 wd = load_down_piece(a, pt, o);
-    const u32x4 u = a.rd > 0 ? load_u_piece(a, dl.c, o) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 u = a.rd > 0 ? load_u_piece<SL>(a, dl.c, o) : u32x4{0u, 0u, 0u, 0u};
     const float so = a.sd ? ldg(a.sd + min(o, a.D - 1)) : 1.f;
-    DownIn<TT> d;
-    load_down_in<TT>(a, s, d);
+    DownIn<TT, SL> d;
+    load_down_in<TT, SL>(a, s, d);
     float p[TT];
-    down_row<TT>(pt, wd, u, so, d, p);
+    down_row<TT, SL>(pt, wd, u, so, d, p);
     if (dl.c == 0 && o < a.D)
         for (int t = 0; t < tn; ++t)
             __hip_atomic_store(part_word(a, q, pt.j, t, TT, o % kMlpGroup), tag | __float_as_uint(p[t]),
@@ -752,7 +776,7 @@ __device__ void slice_h_here(const MlpDec &a, int j, Lds<TT> &s) {
     __syncthreads();
 }
 
-template <int TT, bool ONE>
+template <int TT, bool ONE, int SL>
 __global__ __launch_bounds__(kThreads) void mlp_dec_kernel(MlpDec a) {
     __shared__ Lds<TT> s;
     const GemvF &g = a.gu;
@@ -801,7 +825,7 @@ __global__ __launch_bounds__(kThreads) void mlp_dec_kernel(MlpDec a) {
     __syncthreads();
     finish_gateup_vtx<TT>(a, s, early, ev);
     wait_vm<0>();   // the slice's small operands (direct-to-LDS), issued with the last batch
-    load_down_us(a, o0, dr);   // L2 reads, in flight while h is formed and exchanged
+    load_down_us<SL>(a, o0, dr);   // L2 reads, in flight while h is formed and exchanged
     put_scale<TT>(sv, s);
     __syncthreads();
     form_h<TT>(a, pt, s);
@@ -830,9 +854,9 @@ __global__ __launch_bounds__(kThreads) void mlp_dec_kernel(MlpDec a) {
         __syncthreads();
     }
     if (a.rd > 0) form_vj<TT>(a, pt, s);
-    DownIn<TT> din;
-    load_down_in<TT>(a, s, din);
-    down_part_rows<TT>(a, pt, o0, o1, dr, din, tag);
+    DownIn<TT, SL> din;
+    load_down_in<TT, SL>(a, s, din);
+    down_part_rows<TT, SL>(a, pt, o0, o1, dr, din, tag);
 
     // ---- sums over slices for this workgroup's output groups ----
     const int retries = g.spin_limit - 1;
@@ -861,7 +885,7 @@ __global__ __launch_bounds__(kThreads) void mlp_dec_kernel(MlpDec a) {
                     if (!need) continue;
                     slice_h_here<TT>(a, jj, s);
                     if (a.rd > 0) form_vj<TT>(a, make_part(a, jj, 0), s);
-                    down_group_rows<TT>(a, make_part(a, jj, 0), q, s, tag);
+                    down_group_rows<TT, SL>(a, make_part(a, jj, 0), q, s, tag);
                     __syncthreads();
                 }
                 reduce_poll<TT>(a, q, t, tag32, kSpinLimit, sum);
@@ -925,6 +949,20 @@ MlpPlan mlp_dec_plan(int d_model, int F, int d_out, int r_gate, int r_up, int r_
     return p;
 }
 
+namespace {
+template <int SL>
+void launch_tt(const MlpDec &b, int tt, bool one, int grid, hipStream_t stream) {
+    switch (tt * 2 + one) {
+        case 8: hipLaunchKernelGGL((mlp_dec_kernel<4, false, SL>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+        case 9: hipLaunchKernelGGL((mlp_dec_kernel<4, true, SL>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+        case 4: hipLaunchKernelGGL((mlp_dec_kernel<2, false, SL>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+        case 5: hipLaunchKernelGGL((mlp_dec_kernel<2, true, SL>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+        case 3: hipLaunchKernelGGL((mlp_dec_kernel<1, true, SL>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+        default: hipLaunchKernelGGL((mlp_dec_kernel<1, false, SL>), dim3(grid), dim3(kThreads), 0, stream, b); break;
+    }
+}
+}  // namespace
+
 hipError_t launch_mlp_dec(const MlpDec &a, const MlpPlan &p, hipStream_t stream) {
     MlpDec b = a;
     b.gu.S = p.S;
@@ -939,14 +977,10 @@ hipError_t launch_mlp_dec(const MlpDec &a, const MlpPlan &p, hipStream_t stream)
     b.NG = p.NG;
     const int grid = p.n_prod + p.NS * p.P;
     const bool one = (kW / p.P) / 8 <= (p.tt == 1 ? kSB<1> : kSB<2>);   // one batch of gate/up row steps per part
-    switch (p.tt * 2 + one) {
-        case 8: hipLaunchKernelGGL((mlp_dec_kernel<4, false>), dim3(grid), dim3(kThreads), 0, stream, b); break;
-        case 9: hipLaunchKernelGGL((mlp_dec_kernel<4, true>), dim3(grid), dim3(kThreads), 0, stream, b); break;
-        case 4: hipLaunchKernelGGL((mlp_dec_kernel<2, false>), dim3(grid), dim3(kThreads), 0, stream, b); break;
-        case 5: hipLaunchKernelGGL((mlp_dec_kernel<2, true>), dim3(grid), dim3(kThreads), 0, stream, b); break;
-        case 3: hipLaunchKernelGGL((mlp_dec_kernel<1, true>), dim3(grid), dim3(kThreads), 0, stream, b); break;
-        default: hipLaunchKernelGGL((mlp_dec_kernel<1, false>), dim3(grid), dim3(kThreads), 0, stream, b); break;
-    }
+    if (rank_slots(a.rd) == 4)
+        launch_tt<4>(b, p.tt, one, grid, stream);
+    else
+        launch_tt<8>(b, p.tt, one, grid, stream);
     return hipGetLastError();
 }
 
