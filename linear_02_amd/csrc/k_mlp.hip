@@ -392,8 +392,8 @@ __device__ __forceinline__ void form_vj(const MlpDec &a, const Part &pt, Lds<TT>
     if (tid < G * n) {
         const int g = tid / n, item = tid % n, t = item / rd, k = item % rd;
         float acc = 0.f;
-        // R is a multiple of 8: eight rows' reads issued together, then their
-        // products added in row order.
+        // R is a multiple of 8: eight rows' reads, then their products added
+        // in row order.
         for (int u0 = 0; u0 < R; u0 += 8) {
             uint16_t vv[8], hh[8];
 #pragma unroll
